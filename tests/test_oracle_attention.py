@@ -1,0 +1,292 @@
+"""Pins of the oracle's forward and backward.
+
+* textbook reductions: one group is plain causal attention (torch SDPA, fp64, CPU);
+* folded == unfolded: every suffix's rows equal causal attention over
+  [prefix | suffix_i], prefix rows equal in every copy, prefix dK/dV = sum over copies;
+* closed forms: Q = 0 gives LSE = ln(#visible) and O = mean of the visible V rows;
+* gradients: torch.autograd on an independent masked-softmax formulation, and
+  central finite differences.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import attention as oa
+from oracle.mask import meta_from_layout
+from shared_prefix_block_amd import workloads as wl
+from tests import unfolded as uf
+
+
+def _t64(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.float64))
+
+
+def _rand(T, hq, hkv, d, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(T, hq, d, generator=g, dtype=torch.float64)
+    k = torch.randn(T, hkv, d, generator=g, dtype=torch.float64)
+    v = torch.randn(T, hkv, d, generator=g, dtype=torch.float64)
+    do = torch.randn(T, hq, d, generator=g, dtype=torch.float64)
+    return q, k, v, do
+
+
+def _sdpa_causal(q, k, v, scale=None):
+    """[n, H, d] causal attention via torch SDPA in fp64 (GQA via enable_gqa)."""
+    o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
+                                       v.transpose(0, 1)[None], is_causal=True, scale=scale,
+                                       enable_gqa=q.shape[1] != k.shape[1])
+    return o[0].transpose(0, 1)
+
+
+def _lse_causal(q, k, scale):
+    rep = q.shape[1] // k.shape[1]
+    kk = k.repeat_interleave(rep, dim=1)
+    s = torch.einsum("qhd,khd->hqk", q, kk) * scale
+    n = q.shape[0]
+    s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), -math.inf)
+    return torch.logsumexp(s, dim=-1)
+
+
+@pytest.mark.parametrize("specs,hq,hkv", [
+    ([(37, [])], 2, 2),
+    ([(20, [17])], 4, 2),
+    ([(0, [29])], 2, 1),
+])
+def test_single_sequence_is_causal_sdpa(specs, hq, hkv):
+    lay = wl.tokens_layout(specs)
+    meta = meta_from_layout(lay)
+    q, k, v, _ = _rand(lay.T, hq, hkv, 16, 1)
+    o, lse = oa.forward(meta, q, k, v)
+    ref = _sdpa_causal(q, k, v)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, _lse_causal(q, k, 0.25).numpy(), rtol=0, atol=1e-12)
+
+
+def test_prefix_free_groups_are_block_diagonal_causal():
+    specs = [(0, [5, 7, 3]), (6, []), (4, [])]
+    lay = wl.tokens_layout(specs)
+    meta = meta_from_layout(lay)
+    q, k, v, _ = _rand(lay.T, 2, 2, 8, 2)
+    o, _ = oa.forward(meta, q, k, v)
+    bounds = [0, 5, 12, 15, 21, 25]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        ref = _sdpa_causal(q[a:b], k[a:b], v[a:b])
+        np.testing.assert_allclose(o[a:b], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def _folded_vs_unfolded(lay, seqs, owner, hq, hkv, d, seed):
+    """Forward and backward of the folded layout against causal SDPA per unfolded seq.
+
+    ``owner[t]`` is the unfolded sequence that receives token t's dO (every other copy
+    of t gets dO = 0), so folded dQ of t equals that copy's dQ and folded dK/dV of t
+    equal the sum over all copies."""
+    meta = meta_from_layout(lay)
+    q, k, v, do = _rand(lay.T, hq, hkv, d, seed)
+    o, lse, dq, dk, dv = oa.backward(meta, q, k, v, do)
+    o_f, lse_f = oa.forward(meta, q, k, v)
+    np.testing.assert_allclose(o_f, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_f, lse, rtol=0, atol=1e-13)
+    sc = 1 / math.sqrt(d)
+    dk_sum = torch.zeros_like(k)
+    dv_sum = torch.zeros_like(v)
+    seen = np.zeros(lay.T, bool)
+    for si, s in enumerate(seqs):
+        s_t = torch.as_tensor(s, dtype=torch.long)
+        qs = q[s_t].clone().requires_grad_(True)
+        ks = k[s_t].clone().requires_grad_(True)
+        vs = v[s_t].clone().requires_grad_(True)
+        os_ = _sdpa_causal(qs, ks, vs)
+        np.testing.assert_allclose(o[s], os_.detach().numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, s], _lse_causal(q[s_t], k[s_t], sc).numpy(),
+                                   rtol=0, atol=1e-12)
+        mine = torch.as_tensor(owner[s] == si)
+        dos = torch.where(mine[:, None, None], do[s_t], torch.zeros_like(do[s_t]))
+        os_.backward(dos)
+        qg = qs.grad.numpy()
+        np.testing.assert_allclose(dq[s][mine.numpy()], qg[mine.numpy()], rtol=0, atol=1e-11)
+        dk_sum.index_add_(0, s_t, ks.grad)
+        dv_sum.index_add_(0, s_t, vs.grad)
+        seen[s] = True
+    np.testing.assert_allclose(dk, dk_sum.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, dv_sum.numpy(), rtol=0, atol=1e-11)
+    pad = ~seen
+    assert np.all(o[pad] == 0) and np.all(np.isneginf(lse[:, pad]))
+    assert np.all(dq[pad] == 0) and np.all(dk[pad] == 0) and np.all(dv[pad] == 0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_folded_equals_unfolded_groups(seed):
+    rng = np.random.default_rng(seed)
+    specs = wl.random_group_specs(rng, max_groups=3, max_p=12, max_g=4, max_r=10)
+    lay = wl.tokens_layout(specs, pad_multiple=8)
+    if lay.T_real == 0:
+        return
+    seqs, _ = uf.group_sequences(specs)
+    owner = np.full(lay.T, -1)
+    for si in range(len(seqs) - 1, -1, -1):
+        owner[seqs[si]] = si  # the first sequence that holds a token owns its dO
+    hq, hkv = [(2, 2), (4, 2), (3, 1)][seed % 3]
+    _folded_vs_unfolded(lay, seqs, owner, hq, hkv, 8, seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_folded_equals_unfolded_trees(seed):
+    rng = np.random.default_rng(100 + seed)
+    nl, paths = wl.random_tree(rng, max_nodes=7, max_len=9)
+    lay = wl.tree_layout(nl, paths, extra_pad=3)
+    if lay.T_real == 0:
+        return
+    seqs = uf.tree_sequences(nl, paths)
+    owner = np.full(lay.T, -1)
+    for si in range(len(seqs) - 1, -1, -1):
+        owner[seqs[si]] = si
+    _folded_vs_unfolded(lay, seqs, owner, 4, 2, 8, seed)
+
+
+def test_folded_equals_unfolded_config1():
+    cfg = wl.CONFIGS[1]
+    lay = wl.layout_for(cfg)
+    seqs, _ = uf.group_sequences(lay.specs)
+    owner = np.full(lay.T, -1)
+    for si in range(len(seqs) - 1, -1, -1):
+        owner[seqs[si]] = si
+    _folded_vs_unfolded(lay, seqs, owner, cfg.hq, cfg.hkv, cfg.d, 11)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_zero_query_closed_form(seed):
+    """Q = 0: every visible score is 0, so LSE = ln(#visible) and O = mean visible V."""
+    rng = np.random.default_rng(200 + seed)
+    specs = wl.random_group_specs(rng, max_groups=3, max_p=20, max_g=4, max_r=20)
+    lay = wl.tokens_layout(specs, pad_multiple=16)
+    meta = meta_from_layout(lay)
+    _, k, v, _ = _rand(lay.T, 4, 2, 8, seed)
+    q = torch.zeros(lay.T, 4, 8, dtype=torch.float64)
+    o, lse = oa.forward(meta, q, k, v)
+    n = uf.n_visible_groups(specs, lay.T)
+    real = np.arange(lay.T) < lay.T_real
+    with np.errstate(divide="ignore"):
+        want_lse = np.where(real, np.log(np.maximum(n, 1)), -np.inf)
+    for h in range(4):
+        np.testing.assert_allclose(lse[h], want_lse, rtol=0, atol=1e-13)
+    seqs, _ = uf.group_sequences(specs)
+    vv = v.numpy()
+    for s in seqs:
+        csum = np.cumsum(vv[s], axis=0) / np.arange(1, len(s) + 1)[:, None, None]
+        for h in range(4):
+            np.testing.assert_allclose(o[s, h], csum[:, h // 2], rtol=0, atol=1e-13)
+
+
+def test_constant_values_give_constant_output():
+    lay = wl.layout_for(wl.CONFIGS[1])
+    meta = meta_from_layout(lay)
+    q, k, _, _ = _rand(lay.T, 2, 2, 64, 5)
+    c = torch.linspace(-1, 1, 64, dtype=torch.float64)
+    v = c.expand(lay.T, 2, 64).clone()
+    o, _ = oa.forward(meta, q, k, v)
+    np.testing.assert_allclose(o, np.broadcast_to(c.numpy(), o.shape), rtol=0, atol=1e-13)
+
+
+def _torch_masked_attention(q, k, v, vis, scale):
+    """Independent formulation: masked_fill + softmax in torch, -inf rows -> 0."""
+    rep = q.shape[1] // k.shape[1]
+    kk = k.repeat_interleave(rep, dim=1)
+    vv = v.repeat_interleave(rep, dim=1)
+    s = torch.einsum("qhd,khd->hqk", q, kk) * scale
+    m = torch.as_tensor(vis)[None]
+    s = s.masked_fill(~m, -math.inf)
+    has = m.any(-1, keepdim=True)
+    p = torch.softmax(torch.where(has, s, torch.zeros_like(s)), dim=-1) * has
+    return torch.einsum("hqk,khd->qhd", p, vv)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_backward_matches_autograd(seed):
+    rng = np.random.default_rng(300 + seed)
+    if seed % 2:
+        nl, paths = wl.random_tree(rng, max_nodes=6, max_len=8)
+        lay = wl.tree_layout(nl, paths, extra_pad=2)
+        seqs = uf.tree_sequences(nl, paths)
+    else:
+        specs = wl.random_group_specs(rng, max_groups=2, max_p=10, max_g=3, max_r=8)
+        lay = wl.tokens_layout(specs, pad_multiple=8)
+        seqs, _ = uf.group_sequences(specs)
+    if lay.T_real == 0:
+        return
+    vis = uf.visibility_from_sequences(lay.T, seqs)
+    meta = meta_from_layout(lay)
+    q, k, v, do = _rand(lay.T, 4, 2, 8, seed)
+    sc = 0.3
+    qq, kk, vv = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out = _torch_masked_attention(qq, kk, vv, vis, sc)
+    out.backward(do)
+    o, lse, dq, dk, dv = oa.backward(meta, q, k, v, do, scale=sc)
+    np.testing.assert_allclose(o, out.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq, qq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, kk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, vv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_finite_differences():
+    specs = [(3, [2, 3]), (2, [2])]
+    lay = wl.tokens_layout(specs, pad_multiple=4)
+    meta = meta_from_layout(lay)
+    q, k, v, do = _rand(lay.T, 2, 1, 4, 9)
+    q, k, v, do = q.numpy(), k.numpy(), v.numpy(), do.numpy()
+    _, _, dq, dk, dv = oa.backward(meta, q, k, v, do)
+
+    def loss(qx, kx, vx):
+        o, _ = oa.forward(meta, qx, kx, vx)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(**{a + "x": b for a, b in args_p.items()})
+                        - loss(**{a + "x": b for a, b in args_m.items()})) / (2 * h)
+        err = np.abs(num - g).max() / max(1.0, np.abs(g).max())
+        assert err < 1e-6, (name, err)
+
+
+def test_sampled_paths_agree_with_full():
+    specs = [(9, [5, 6, 4]), (7, [3, 8])]
+    lay = wl.tokens_layout(specs, pad_multiple=16)
+    meta = meta_from_layout(lay)
+    q, k, v, do = _rand(lay.T, 4, 2, 8, 21)
+    o, lse, dq, dk, dv = oa.backward(meta, q, k, v, do)
+    rows = np.array([0, 3, 9, 15, 20, 31, 40, 47])
+    o_r, lse_r, dq_r = oa.grad_rows(meta, q, k, v, do, rows)
+    np.testing.assert_allclose(o_r, o[rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_r, lse[:, rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dq_r, dq[rows], rtol=0, atol=1e-13)
+    o_f, lse_f = oa.forward(meta, q, k, v, rows=rows)
+    np.testing.assert_allclose(o_f, o[rows], rtol=0, atol=1e-13)
+    cols = np.array([1, 8, 12, 24, 26, 40, 47])
+    dk_c, dv_c = oa.grad_cols(meta, q, k, v, do, cols)
+    np.testing.assert_allclose(dk_c, dk[cols], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv_c, dv[cols], rtol=0, atol=1e-13)
+
+
+def test_gradient_sum_identities():
+    """Rows of P sum to 1, so sum_kv dV = sum_q dO over non-empty rows; and
+    sum_kv dS = 0 per row, so sum_kv dK = 0 (per kv head, over the group)."""
+    lay = wl.tokens_layout([(11, [6, 9, 2]), (4, [7])], pad_multiple=16)
+    meta = meta_from_layout(lay)
+    q, k, v, do = _rand(lay.T, 4, 2, 8, 33)
+    _, _, _, dk, dv = oa.backward(meta, q, k, v, do)
+    real = np.arange(lay.T) < lay.T_real
+    dos = do.numpy()[real]
+    for hk in range(2):
+        np.testing.assert_allclose(dv[:, hk].sum(0), dos[:, 2 * hk:2 * hk + 2].sum((0, 1)),
+                                   rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dk[:, hk].sum(0), 0, rtol=0, atol=1e-11)
