@@ -1,0 +1,188 @@
+/*
+ * psa.h - shared-prefix (prefix-tree) block-sparse attention on MI355X (gfx950).
+ *
+ * C ABI of libpsa.so.  Plain pointers and sizes only.  Every call returns a
+ * psa_status; a failing call writes nothing the caller owns and launches nothing,
+ * and psa_last_error() gives a detail string for the calling thread.  No exception
+ * or abort crosses this boundary.
+ *
+ * What is computed (sources are web pages; each is named by its title):
+ *
+ *  - The mask.  unsloth "prefix_grouper_kernel.py", function _make_mask_mod and its
+ *    docstring: q may attend to kv iff both are in the same group, kv <= q, and
+ *    either kv is a prompt (prefix) token or q is a completion (suffix) token of the
+ *    same completion as kv.  Prompt rows are therefore causal, and every completion
+ *    row sees its whole prompt.  Pad tokens (negative group id) see nothing and are
+ *    seen by nothing (same page, the comment above _pad_len).
+ *  - The prefix tree.  Automodel PR #2564, "Changelog": the tree is carried as
+ *    node_lengths and sample_paths; a token sees every token of its node's strict
+ *    ancestors and the tokens of its own node at or before itself.
+ *  - The attention.  unsloth "prefix_grouper_kernel.py", flex_shared_prefix_attention:
+ *    Q/K/V are [T, heads, head_dim] (the page's [1, T, H, D] without the batch),
+ *    K/V carry the KV-head count (GQA), the softmax scale defaults to 1/sqrt(head_dim).
+ *    q head h reads kv head h / (hq / hkv).
+ *  - The block sparsity.  Same page, module docstring: tiles that the mask empties
+ *    are never computed.  A tile map classifies every (q-tile, kv-tile) pair as
+ *    empty (0), partial (1) or full (2); kernels apply the per-element mask only on
+ *    partial tiles.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q, o, dq, dout : [T, hq, d]      k, v, dk, dv : [T, hkv, d]
+ *   lse            : [hq, T] float32, natural log; -inf on rows that see no key.
+ * Element type: PSA_FP32 -> float, PSA_BF16 -> bfloat16 (raw 16-bit storage).
+ * Outputs are overwritten in full, pad rows included (O = 0, LSE = -inf, grads 0).
+ */
+#ifndef PSA_H
+#define PSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PSA_ABI_VERSION 1
+
+typedef enum {
+  PSA_OK = 0,
+  PSA_ERR_NULL = 1,         /* a required pointer is NULL                              */
+  PSA_ERR_SHAPE = 2,        /* T, head counts or tile sizes out of range; hq % hkv != 0 */
+  PSA_ERR_LAYOUT = 3,       /* metadata not in the packed layout the library accepts    */
+  PSA_ERR_DTYPE = 4,        /* unknown psa_dtype                                        */
+  PSA_ERR_UNSUPPORTED = 5,  /* head_dim / dtype combination not compiled                */
+  PSA_ERR_MAP_MISMATCH = 6, /* map built for another T, tile shape or device            */
+  PSA_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than psa_bwd_workspace_size    */
+  PSA_ERR_HIP = 8,          /* a HIP runtime call failed (text in psa_last_error)       */
+  PSA_ERR_ALLOC = 9,        /* a device or host allocation failed                       */
+  PSA_ERR_VALUE = 10        /* a scalar argument is invalid (e.g. non-finite scale)     */
+} psa_status;
+
+typedef enum { PSA_FP32 = 0, PSA_BF16 = 1 } psa_dtype;
+typedef enum { PSA_PASS_FWD = 0, PSA_PASS_BWD = 1 } psa_pass;
+
+/* Opaque, library-owned, immutable after it is built. */
+typedef struct psa_tile_map psa_tile_map;
+
+typedef struct {
+  int64_t T;           /* tokens, pads included                                  */
+  int32_t block_m;     /* q rows per tile                                         */
+  int32_t block_n;     /* kv columns per tile                                     */
+  int64_t n_qtiles;    /* ceil(T / block_m)                                       */
+  int64_t n_ktiles;    /* ceil(T / block_n)                                       */
+  int64_t nnz;         /* non-empty tiles                                         */
+  int64_t n_full;      /* tiles whose every pair is kept                          */
+  int64_t n_partial;   /* non-empty tiles that are not full                       */
+} psa_tile_map_info;
+
+/* Library ABI version (PSA_ABI_VERSION of the build). */
+int32_t psa_abi_version(void);
+/* Static text for a status code. */
+const char* psa_status_string(psa_status s);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* psa_last_error(void);
+
+/*
+ * Tile shape (block_m, block_n) that psa_fwd (pass PSA_PASS_FWD) or psa_bwd
+ * (PSA_PASS_BWD) needs its map built with, for this dtype and head_dim.
+ * Errors: PSA_ERR_NULL, PSA_ERR_DTYPE, PSA_ERR_UNSUPPORTED.
+ */
+psa_status psa_tile_shape(psa_pass pass, psa_dtype dtype, int32_t d, int32_t* block_m,
+                          int32_t* block_n);
+
+/*
+ * Build a tile map from per-token labels (device pointers, T entries each):
+ *   group[t]     >= 0 group id, < 0 pad token;
+ *   suffix[t]    completion id (ignored on prompt and pad tokens);
+ *   is_prefix[t] 1 on prompt tokens, 0 on completion tokens (ignored on pads).
+ * Accepted layout (reading of unsloth "prefix_grouper_kernel.py",
+ * build_seg_info_multigroup, which always packs this way): each group is one
+ * contiguous run; group ids increase from run to run; a group's prompt tokens come
+ * before its completion tokens; each completion is one contiguous run and completion
+ * ids increase within a group; pads may sit between groups or at either end.
+ * Anything else returns PSA_ERR_LAYOUT (never a silently different mask).
+ * 1 <= block_m, block_n <= 1024.  T may be 0 (an empty map).
+ * Work is enqueued on `stream` (a hipStream_t, NULL = default); the call waits once
+ * on that stream to size the sparse lists.  The map may be used on `stream` at once;
+ * on another stream, after synchronising with `stream`.
+ * Ownership: *out belongs to the caller until psa_tile_map_destroy.
+ * Errors: PSA_ERR_NULL, PSA_ERR_SHAPE, PSA_ERR_LAYOUT, PSA_ERR_HIP, PSA_ERR_ALLOC.
+ */
+psa_status psa_build_tile_map_tokens(int64_t T, const int32_t* group, const int32_t* suffix,
+                                     const uint8_t* is_prefix, int32_t block_m,
+                                     int32_t block_n, void* stream, psa_tile_map** out);
+
+/*
+ * Build a tile map from a prefix tree (host pointers):
+ *   node_lengths[n_nodes]  tokens of each node; node n owns the n-th contiguous run;
+ *   path_ptr[n_paths + 1], path_nodes[path_ptr[n_paths]]  sample path s lists node
+ *   indices root -> leaf in path_nodes[path_ptr[s] .. path_ptr[s+1]).
+ * Accepted layout (reading of Automodel PR #2564, whose fold already emits
+ * [prompt | c_0 | c_1 ...]): every node lies on a path; a node has one parent across
+ * all paths; nodes are in depth-first pre-order (a parent precedes its children and
+ * each subtree is one contiguous run of nodes).  Several roots pack several trees.
+ * Zero-length nodes are allowed.  T >= sum(node_lengths); tokens past the sum are pads.
+ * Same stream, ownership and error rules as psa_build_tile_map_tokens.
+ */
+psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
+                                   int64_t n_paths, const int32_t* path_ptr,
+                                   const int32_t* path_nodes, int64_t T, int32_t block_m,
+                                   int32_t block_n, void* stream, psa_tile_map** out);
+
+/* Sizes of a built map.  Errors: PSA_ERR_NULL. */
+psa_status psa_tile_map_info_get(const psa_tile_map* map, psa_tile_map_info* out);
+
+/*
+ * Copy a map to host buffers (NULL arguments are skipped); waits for the map's
+ * build stream.  Sizes: end[T] (int32: key t is visible to rows q with
+ * t <= q < end[t]), kinds[n_qtiles * n_ktiles] (row-major, 0/1/2), row_ptr[n_qtiles+1],
+ * col[nnz], kind[nnz] (CSR: per q-tile its kv-tiles ascending), col_ptr[n_ktiles+1],
+ * row[nnz], kind_csc[nnz] (CSC: per kv-tile its q-tiles ascending).
+ * Errors: PSA_ERR_NULL, PSA_ERR_HIP.
+ */
+psa_status psa_tile_map_export(const psa_tile_map* map, int32_t* end, uint8_t* kinds,
+                               int32_t* row_ptr, int32_t* col, uint8_t* kind,
+                               int32_t* col_ptr, int32_t* row, uint8_t* kind_csc);
+
+/* Free a map (NULL is a no-op).  Work that uses it must have completed. */
+void psa_tile_map_destroy(psa_tile_map* map);
+
+/*
+ * Forward: O = softmax(scale * Q K^T masked) V per q head, and LSE.
+ * Device pointers: q, k, v (inputs), o, lse (outputs, fully overwritten).
+ * scale <= 0 selects 1/sqrt(d).  T must equal the map's T; the map's tile shape must
+ * be psa_tile_shape(PSA_PASS_FWD, dtype, d).  Asynchronous on `stream`.
+ * Errors: PSA_ERR_NULL, PSA_ERR_SHAPE, PSA_ERR_DTYPE, PSA_ERR_UNSUPPORTED,
+ * PSA_ERR_MAP_MISMATCH, PSA_ERR_VALUE, PSA_ERR_HIP.
+ */
+psa_status psa_fwd(const psa_tile_map* map, psa_dtype dtype, int64_t T, int32_t hq,
+                   int32_t hkv, int32_t d, float scale, const void* q, const void* k,
+                   const void* v, void* o, float* lse, void* stream);
+
+/* Bytes of device workspace psa_bwd needs for these sizes.  Errors as psa_fwd. */
+psa_status psa_bwd_workspace_size(const psa_tile_map* map, psa_dtype dtype, int64_t T,
+                                  int32_t hq, int32_t hkv, int32_t d, size_t* bytes);
+
+/*
+ * Backward (FlashAttention-2 style): dQ, dK, dV of sum(dO * O) given the forward's
+ * O and LSE.  dK and dV sum over the q heads that share a kv head.  Device pointers:
+ * q, k, v, o, lse, dout (inputs, element type `dtype`), dq, dk, dv (outputs, element
+ * type `grad_dtype`, fully overwritten), workspace (caller-owned scratch of at least
+ * psa_bwd_workspace_size bytes, contents undefined on entry and exit).
+ * grad_dtype is PSA_FP32 (the fp32 accumulators as they are; with bf16 inputs this is
+ * the form that meets the bf16 parity bar for any gradient magnitude) or `dtype`.
+ * The map's tile shape must be psa_tile_shape(PSA_PASS_BWD, ...).  Asynchronous on
+ * `stream`.  Errors: as psa_fwd, plus PSA_ERR_WORKSPACE; PSA_ERR_DTYPE for a
+ * grad_dtype that is neither PSA_FP32 nor `dtype`.
+ */
+psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype, int64_t T,
+                   int32_t hq, int32_t hkv, int32_t d, float scale, const void* q,
+                   const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSA_H */

@@ -37,11 +37,11 @@ def tile_counts(meta, block_m: int, block_n: int, block_rows: int = 1024) -> np.
         tj_u = tj[cstart]
         for r0 in range(0, len(comp), block_rows):
             blk = comp[r0:r0 + block_rows]
-            m = meta.mask(blk, comp).astype(np.int64)
+            m = meta.mask(blk, comp).astype(np.int32)
             per_col_tile = np.add.reduceat(m, cstart, axis=1)
             ti = blk // block_m
             rstart = np.concatenate([[0], np.flatnonzero(np.diff(ti)) + 1])
-            per_tile = np.add.reduceat(per_col_tile, rstart, axis=0)
+            per_tile = np.add.reduceat(per_col_tile.astype(np.int64), rstart, axis=0)
             counts[np.ix_(ti[rstart], tj_u)] += per_tile
     return counts
 

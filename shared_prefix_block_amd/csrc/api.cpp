@@ -1,0 +1,477 @@
+// C ABI of libpsa.so: argument validation, tile-map lifetime, kernel dispatch.
+//
+// Every validation runs before the first launch of a call, so a failing call writes
+// nothing the caller owns.  The map builder is the one call that waits on its
+// stream (once), to size the sparse lists.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "psa.h"
+#include "psa_internal.h"
+
+namespace {
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxT = (int64_t{1} << 31) - 4096;
+constexpr int64_t kMaxTiles = int64_t{1} << 32;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Carver {  // carves one allocation into 256-byte aligned pieces
+  size_t off = 0;
+  template <typename T>
+  size_t take(size_t count) {
+    size_t at = off;
+    off = align_up(off + count * sizeof(T), 256);
+    return at;
+  }
+};
+
+psa_status check_tiles(int64_t T, int32_t bm, int32_t bn) {
+  if (T < 0 || T > kMaxT) return psa_set_error(PSA_ERR_SHAPE, "T out of range [0, 2^31-4096]");
+  if (bm < 1 || bm > 1024 || bn < 1 || bn > 1024)
+    return psa_set_error(PSA_ERR_SHAPE, "block_m and block_n must lie in [1, 1024]");
+  int64_t nq = (T + bm - 1) / bm, nk = (T + bn - 1) / bn;
+  if (nq * nk > kMaxTiles) return psa_set_error(PSA_ERR_SHAPE, "too many tiles (T / block too large)");
+  return PSA_OK;
+}
+
+void free_map(psa_tile_map* m) {
+  if (!m) return;
+  if (m->buf1) (void)hipFree(m->buf1);
+  if (m->buf2) (void)hipFree(m->buf2);
+  delete m;
+}
+
+// Descending-length order of CSR rows / CSC columns (stable: ties keep index order).
+void length_order(const std::vector<int32_t>& ptr, int64_t n, int32_t* out) {
+  std::vector<int32_t> idx(n);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+    return (ptr[a + 1] - ptr[a]) > (ptr[b + 1] - ptr[b]);
+  });
+  std::copy(idx.begin(), idx.end(), out);
+}
+
+// Phase 1 allocation + classification; the per-token `end` array must be filled by
+// the caller's launch between alloc_phase1 and finish_build.
+psa_status alloc_phase1(psa_tile_map* m, size_t* info_off, size_t* scratch_off,
+                        size_t* flag_off) {
+  Carver c;
+  size_t o_end = c.take<int32_t>(std::max<int64_t>(m->T, 1));
+  size_t o_kinds = c.take<uint8_t>(std::max<int64_t>(m->nq * m->nk, 1));
+  size_t o_rp = c.take<int32_t>(m->nq + 1);
+  size_t o_cp = c.take<int32_t>(m->nk + 1);
+  size_t o_kmin = c.take<int32_t>(std::max<int64_t>(m->nk, 1));
+  size_t o_kmax = c.take<int32_t>(std::max<int64_t>(m->nk, 1));
+  size_t o_info = c.take<int64_t>(8);
+  size_t o_flag = c.take<int32_t>(4);
+  if (hipMalloc(&m->buf1, c.off) != hipSuccess) {
+    m->buf1 = nullptr;
+    return psa_set_error(PSA_ERR_ALLOC, "device allocation of the tile map failed");
+  }
+  char* b = static_cast<char*>(m->buf1);
+  m->end = reinterpret_cast<int32_t*>(b + o_end);
+  m->kinds = reinterpret_cast<uint8_t*>(b + o_kinds);
+  m->row_ptr = reinterpret_cast<int32_t*>(b + o_rp);
+  m->col_ptr = reinterpret_cast<int32_t*>(b + o_cp);
+  *scratch_off = o_kmin;
+  (void)o_kmax;
+  *info_off = o_info;
+  *flag_off = o_flag;
+  return PSA_OK;
+}
+
+psa_status finish_build(psa_tile_map* m, size_t info_off, size_t scratch_off, size_t flag_off,
+                        bool check_flag, psa_tile_map** out) {
+  char* b = static_cast<char*>(m->buf1);
+  int32_t* kmin = reinterpret_cast<int32_t*>(b + scratch_off);
+  int32_t* kmax = kmin + align_up(std::max<int64_t>(m->nk, 1) * 4, 256) / 4;
+  int64_t* info = reinterpret_cast<int64_t*>(b + info_off);
+  int32_t* flag = reinterpret_cast<int32_t*>(b + flag_off);
+  hipError_t e = launch_classify(m->T, m->bm, m->bn, m->nq, m->nk, m->end, m->kinds,
+                                 m->row_ptr, m->col_ptr, kmin, kmax, info, m->stream);
+  if (e != hipSuccess) return psa_hip_error(e, "tile classification launch");
+
+  // one wait: info, flag and both pointer arrays come back together
+  std::vector<int64_t> info_h(8, 0);
+  int32_t flag_h[4] = {0, 0, 0, 0};
+  std::vector<int32_t> rp_h(m->nq + 1), cp_h(m->nk + 1);
+  if ((e = hipMemcpyAsync(info_h.data(), info, 8 * sizeof(int64_t), hipMemcpyDeviceToHost,
+                          m->stream)) != hipSuccess ||
+      (e = hipMemcpyAsync(flag_h, flag, sizeof(flag_h), hipMemcpyDeviceToHost, m->stream)) !=
+          hipSuccess ||
+      (e = hipMemcpyAsync(rp_h.data(), m->row_ptr, rp_h.size() * 4, hipMemcpyDeviceToHost,
+                          m->stream)) != hipSuccess ||
+      (e = hipMemcpyAsync(cp_h.data(), m->col_ptr, cp_h.size() * 4, hipMemcpyDeviceToHost,
+                          m->stream)) != hipSuccess ||
+      (e = hipStreamSynchronize(m->stream)) != hipSuccess)
+    return psa_hip_error(e, "tile map readback");
+  if (check_flag && flag_h[0] != 0) {
+    static const char* why[] = {
+        "",
+        "group ids decrease along the sequence (groups must be contiguous, ascending runs)",
+        "a group is split by pad tokens",
+        "a prompt token follows a completion token of the same group",
+        "completion ids decrease within a group (completions must be contiguous runs)"};
+    int code = flag_h[0] >= 1 && flag_h[0] <= 4 ? flag_h[0] : 0;
+    return psa_set_error(PSA_ERR_LAYOUT, std::string("token layout rejected at position ") +
+                                             std::to_string(flag_h[1] - 1) + ": " + why[code]);
+  }
+  m->nnz = info_h[0];
+  m->n_full = info_h[1];
+  m->n_partial = info_h[2];
+
+  Carver c;
+  size_t o_col = c.take<int32_t>(std::max<int64_t>(m->nnz, 1));
+  size_t o_kind = c.take<uint8_t>(std::max<int64_t>(m->nnz, 1));
+  size_t o_row = c.take<int32_t>(std::max<int64_t>(m->nnz, 1));
+  size_t o_kc = c.take<uint8_t>(std::max<int64_t>(m->nnz, 1));
+  size_t o_qo = c.take<int32_t>(std::max<int64_t>(m->nq, 1));
+  size_t o_ko = c.take<int32_t>(std::max<int64_t>(m->nk, 1));
+  if ((e = hipMalloc(&m->buf2, c.off)) != hipSuccess) {
+    m->buf2 = nullptr;
+    return psa_set_error(PSA_ERR_ALLOC, "device allocation of the tile lists failed");
+  }
+  char* b2 = static_cast<char*>(m->buf2);
+  m->col = reinterpret_cast<int32_t*>(b2 + o_col);
+  m->kind = reinterpret_cast<uint8_t*>(b2 + o_kind);
+  m->row = reinterpret_cast<int32_t*>(b2 + o_row);
+  m->kind_csc = reinterpret_cast<uint8_t*>(b2 + o_kc);
+  m->qorder = reinterpret_cast<int32_t*>(b2 + o_qo);
+  m->korder = reinterpret_cast<int32_t*>(b2 + o_ko);
+
+  if (m->nnz > 0) {
+    e = launch_fill_lists(m->nq, m->nk, m->kinds, m->row_ptr, m->col_ptr, m->col, m->kind,
+                          m->row, m->kind_csc, m->stream);
+    if (e != hipSuccess) return psa_hip_error(e, "tile list launch");
+  }
+  m->host_orders.resize(m->nq + m->nk);
+  length_order(rp_h, m->nq, m->host_orders.data());
+  length_order(cp_h, m->nk, m->host_orders.data() + m->nq);
+  if (m->nq > 0) {
+    if ((e = hipMemcpyAsync(m->qorder, m->host_orders.data(), m->nq * 4, hipMemcpyHostToDevice,
+                            m->stream)) != hipSuccess ||
+        (e = hipMemcpyAsync(m->korder, m->host_orders.data() + m->nq, m->nk * 4,
+                            hipMemcpyHostToDevice, m->stream)) != hipSuccess)
+      return psa_hip_error(e, "tile order upload");
+  }
+  *out = m;
+  return PSA_OK;
+}
+
+psa_status check_attn_args(const psa_tile_map* map, psa_dtype dtype, int64_t T, int32_t hq,
+                           int32_t hkv, int32_t d, float scale, psa_pass pass) {
+  if (!map) return psa_set_error(PSA_ERR_NULL, "map is NULL");
+  if (dtype != PSA_FP32 && dtype != PSA_BF16) return psa_set_error(PSA_ERR_DTYPE, "unknown dtype");
+  if (T < 0 || T > kMaxT) return psa_set_error(PSA_ERR_SHAPE, "T out of range");
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return psa_set_error(PSA_ERR_SHAPE, "need hq >= 1, hkv >= 1 and hq % hkv == 0");
+  if (T * int64_t{hq} * d > (int64_t{1} << 40))
+    return psa_set_error(PSA_ERR_SHAPE, "tensor too large");
+  bool ok = pass == PSA_PASS_FWD ? fwd_supported(dtype, d) : bwd_supported(dtype, d);
+  if (!ok) return psa_set_error(PSA_ERR_UNSUPPORTED, "head_dim " + std::to_string(d) +
+                                                          " is not compiled for this dtype");
+  if (!std::isfinite(scale)) return psa_set_error(PSA_ERR_VALUE, "scale is not finite");
+  if (T != map->T)
+    return psa_set_error(PSA_ERR_MAP_MISMATCH, "T = " + std::to_string(T) +
+                                                   " but the map was built for T = " +
+                                                   std::to_string(map->T));
+  if (map->bm != kTileM || map->bn != kTileN)
+    return psa_set_error(PSA_ERR_MAP_MISMATCH,
+                         "map tile shape " + std::to_string(map->bm) + "x" +
+                             std::to_string(map->bn) + " is not the kernel tile shape " +
+                             std::to_string(kTileM) + "x" + std::to_string(kTileN));
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != map->device)
+    return psa_set_error(PSA_ERR_MAP_MISMATCH, "map was built on another device");
+  return PSA_OK;
+}
+
+}  // namespace
+
+psa_status psa_set_error(psa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+psa_status psa_hip_error(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return PSA_ERR_HIP;
+}
+
+extern "C" {
+
+int32_t psa_abi_version(void) { return PSA_ABI_VERSION; }
+
+const char* psa_status_string(psa_status s) {
+  switch (s) {
+    case PSA_OK: return "ok";
+    case PSA_ERR_NULL: return "null pointer";
+    case PSA_ERR_SHAPE: return "shape out of range";
+    case PSA_ERR_LAYOUT: return "metadata layout not accepted";
+    case PSA_ERR_DTYPE: return "unknown dtype";
+    case PSA_ERR_UNSUPPORTED: return "unsupported head_dim / dtype";
+    case PSA_ERR_MAP_MISMATCH: return "tile map does not match the call";
+    case PSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PSA_ERR_HIP: return "HIP runtime error";
+    case PSA_ERR_ALLOC: return "allocation failed";
+    case PSA_ERR_VALUE: return "invalid scalar argument";
+  }
+  return "unknown status";
+}
+
+const char* psa_last_error(void) { return g_last_error.c_str(); }
+
+psa_status psa_tile_shape(psa_pass pass, psa_dtype dtype, int32_t d, int32_t* block_m,
+                          int32_t* block_n) {
+  if (!block_m || !block_n) return psa_set_error(PSA_ERR_NULL, "output pointer is NULL");
+  if (dtype != PSA_FP32 && dtype != PSA_BF16) return psa_set_error(PSA_ERR_DTYPE, "unknown dtype");
+  bool ok = pass == PSA_PASS_FWD ? fwd_supported(dtype, d)
+                                 : pass == PSA_PASS_BWD ? bwd_supported(dtype, d) : false;
+  if (!ok) return psa_set_error(PSA_ERR_UNSUPPORTED, "no kernel for this pass / dtype / head_dim");
+  *block_m = kTileM;
+  *block_n = kTileN;
+  return PSA_OK;
+}
+
+psa_status psa_build_tile_map_tokens(int64_t T, const int32_t* group, const int32_t* suffix,
+                                     const uint8_t* is_prefix, int32_t block_m,
+                                     int32_t block_n, void* stream, psa_tile_map** out) {
+  if (!out) return psa_set_error(PSA_ERR_NULL, "out is NULL");
+  psa_status st = check_tiles(T, block_m, block_n);
+  if (st != PSA_OK) return st;
+  if (T > 0 && (!group || !suffix || !is_prefix))
+    return psa_set_error(PSA_ERR_NULL, "label pointer is NULL");
+  psa_tile_map* m = new (std::nothrow) psa_tile_map();
+  if (!m) return psa_set_error(PSA_ERR_ALLOC, "host allocation failed");
+  m->T = T;
+  m->bm = block_m;
+  m->bn = block_n;
+  m->nq = (T + block_m - 1) / block_m;
+  m->nk = (T + block_n - 1) / block_n;
+  m->stream = static_cast<hipStream_t>(stream);
+  hipError_t e = hipGetDevice(&m->device);
+  if (e != hipSuccess) {
+    free_map(m);
+    return psa_hip_error(e, "hipGetDevice");
+  }
+  size_t info_off, scratch_off, flag_off;
+  if ((st = alloc_phase1(m, &info_off, &scratch_off, &flag_off)) != PSA_OK) {
+    free_map(m);
+    return st;
+  }
+  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(m->buf1) + flag_off);
+  e = launch_tokens_end(T, group, suffix, is_prefix, m->end, flag, m->stream);
+  if (e != hipSuccess) {
+    free_map(m);
+    return psa_hip_error(e, "label scan launch");
+  }
+  st = finish_build(m, info_off, scratch_off, flag_off, true, out);
+  if (st != PSA_OK) free_map(m);
+  return st;
+}
+
+psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
+                                   int64_t n_paths, const int32_t* path_ptr,
+                                   const int32_t* path_nodes, int64_t T, int32_t block_m,
+                                   int32_t block_n, void* stream, psa_tile_map** out) {
+  if (!out) return psa_set_error(PSA_ERR_NULL, "out is NULL");
+  psa_status st = check_tiles(T, block_m, block_n);
+  if (st != PSA_OK) return st;
+  if (n_nodes < 0 || n_paths < 0) return psa_set_error(PSA_ERR_SHAPE, "negative count");
+  if (n_nodes > 0 && (!node_lengths || !path_ptr || (!path_nodes && n_paths > 0)))
+    return psa_set_error(PSA_ERR_NULL, "tree pointer is NULL");
+  if (n_nodes > 0 && n_paths == 0)
+    return psa_set_error(PSA_ERR_LAYOUT, "nodes given but no sample path");
+
+  // --- host validation: parents, depth-first pre-order, subtree extents ---
+  std::vector<int64_t> parent(n_nodes, -2);
+  std::vector<int64_t> start(n_nodes + 1, 0);
+  for (int64_t n = 0; n < n_nodes; ++n) {
+    if (node_lengths[n] < 0) return psa_set_error(PSA_ERR_LAYOUT, "negative node length");
+    start[n + 1] = start[n] + node_lengths[n];
+  }
+  if (start[n_nodes] > T)
+    return psa_set_error(PSA_ERR_SHAPE, "T is shorter than sum(node_lengths)");
+  if (n_paths > 0 && path_ptr[0] != 0) return psa_set_error(PSA_ERR_LAYOUT, "path_ptr[0] != 0");
+  for (int64_t s = 0; s < n_paths; ++s) {
+    int64_t a = path_ptr[s], b = path_ptr[s + 1];
+    if (b <= a) return psa_set_error(PSA_ERR_LAYOUT, "empty or decreasing sample path");
+    int64_t prev = -1;
+    for (int64_t k = a; k < b; ++k) {
+      int64_t node = path_nodes[k];
+      if (node < 0 || node >= n_nodes)
+        return psa_set_error(PSA_ERR_LAYOUT, "path node index out of range");
+      if (parent[node] == -2)
+        parent[node] = prev;
+      else if (parent[node] != prev)
+        return psa_set_error(PSA_ERR_LAYOUT,
+                             "node " + std::to_string(node) + " has two different parents");
+      prev = node;
+    }
+  }
+  std::vector<int64_t> stack;
+  for (int64_t n = 0; n < n_nodes; ++n) {
+    if (parent[n] == -2)
+      return psa_set_error(PSA_ERR_LAYOUT, "node " + std::to_string(n) + " lies on no path");
+    if (parent[n] == -1) {
+      stack.clear();
+    } else {
+      while (!stack.empty() && stack.back() != parent[n]) stack.pop_back();
+      if (stack.empty())
+        return psa_set_error(PSA_ERR_LAYOUT, "nodes are not in depth-first pre-order (node " +
+                                                 std::to_string(n) + ")");
+    }
+    stack.push_back(n);
+  }
+  std::vector<int64_t> sub_end(n_nodes);
+  for (int64_t n = 0; n < n_nodes; ++n) sub_end[n] = n + 1;
+  for (int64_t n = n_nodes - 1; n >= 0; --n)
+    if (parent[n] >= 0) sub_end[parent[n]] = std::max(sub_end[parent[n]], sub_end[n]);
+  std::vector<int64_t> table(2 * std::max<int64_t>(n_nodes, 1), 0);
+  for (int64_t n = 0; n < n_nodes; ++n) {
+    table[n] = start[n];
+    table[n_nodes + n] = start[sub_end[n]];
+  }
+
+  psa_tile_map* m = new (std::nothrow) psa_tile_map();
+  if (!m) return psa_set_error(PSA_ERR_ALLOC, "host allocation failed");
+  m->T = T;
+  m->bm = block_m;
+  m->bn = block_n;
+  m->nq = (T + block_m - 1) / block_m;
+  m->nk = (T + block_n - 1) / block_n;
+  m->stream = static_cast<hipStream_t>(stream);
+  hipError_t e = hipGetDevice(&m->device);
+  if (e != hipSuccess) {
+    free_map(m);
+    return psa_hip_error(e, "hipGetDevice");
+  }
+  size_t info_off, scratch_off, flag_off;
+  if ((st = alloc_phase1(m, &info_off, &scratch_off, &flag_off)) != PSA_OK) {
+    free_map(m);
+    return st;
+  }
+  void* d_table = nullptr;
+  if (n_nodes > 0) {
+    if ((e = hipMalloc(&d_table, table.size() * sizeof(int64_t))) != hipSuccess) {
+      free_map(m);
+      return psa_set_error(PSA_ERR_ALLOC, "device allocation of the node table failed");
+    }
+    if ((e = hipMemcpyAsync(d_table, table.data(), table.size() * sizeof(int64_t),
+                            hipMemcpyHostToDevice, m->stream)) != hipSuccess) {
+      (void)hipFree(d_table);
+      free_map(m);
+      return psa_hip_error(e, "node table upload");
+    }
+  }
+  const int64_t* dt = static_cast<const int64_t*>(d_table);
+  e = launch_tree_end(T, n_nodes, dt, dt ? dt + n_nodes : nullptr, start[n_nodes], m->end,
+                      m->stream);
+  if (e != hipSuccess) {
+    if (d_table) (void)hipFree(d_table);
+    free_map(m);
+    return psa_hip_error(e, "tree expansion launch");
+  }
+  st = finish_build(m, info_off, scratch_off, flag_off, false, out);
+  if (d_table) (void)hipFree(d_table);  // finish_build waited on the stream
+  if (st != PSA_OK) free_map(m);
+  return st;
+}
+
+psa_status psa_tile_map_info_get(const psa_tile_map* map, psa_tile_map_info* out) {
+  if (!map || !out) return psa_set_error(PSA_ERR_NULL, "map or out is NULL");
+  out->T = map->T;
+  out->block_m = map->bm;
+  out->block_n = map->bn;
+  out->n_qtiles = map->nq;
+  out->n_ktiles = map->nk;
+  out->nnz = map->nnz;
+  out->n_full = map->n_full;
+  out->n_partial = map->n_partial;
+  return PSA_OK;
+}
+
+psa_status psa_tile_map_export(const psa_tile_map* map, int32_t* end, uint8_t* kinds,
+                               int32_t* row_ptr, int32_t* col, uint8_t* kind,
+                               int32_t* col_ptr, int32_t* row, uint8_t* kind_csc) {
+  if (!map) return psa_set_error(PSA_ERR_NULL, "map is NULL");
+  hipError_t e = hipStreamSynchronize(map->stream);
+  if (e != hipSuccess) return psa_hip_error(e, "hipStreamSynchronize");
+  struct Item {
+    void* dst;
+    const void* src;
+    size_t bytes;
+  } items[] = {
+      {end, map->end, size_t(map->T) * 4},
+      {kinds, map->kinds, size_t(map->nq * map->nk)},
+      {row_ptr, map->row_ptr, size_t(map->nq + 1) * 4},
+      {col, map->col, size_t(map->nnz) * 4},
+      {kind, map->kind, size_t(map->nnz)},
+      {col_ptr, map->col_ptr, size_t(map->nk + 1) * 4},
+      {row, map->row, size_t(map->nnz) * 4},
+      {kind_csc, map->kind_csc, size_t(map->nnz)},
+  };
+  for (const Item& it : items) {
+    if (!it.dst || it.bytes == 0) continue;
+    if ((e = hipMemcpy(it.dst, it.src, it.bytes, hipMemcpyDeviceToHost)) != hipSuccess)
+      return psa_hip_error(e, "tile map export");
+  }
+  return PSA_OK;
+}
+
+void psa_tile_map_destroy(psa_tile_map* map) { free_map(map); }
+
+psa_status psa_fwd(const psa_tile_map* map, psa_dtype dtype, int64_t T, int32_t hq,
+                   int32_t hkv, int32_t d, float scale, const void* q, const void* k,
+                   const void* v, void* o, float* lse, void* stream) {
+  psa_status st = check_attn_args(map, dtype, T, hq, hkv, d, scale, PSA_PASS_FWD);
+  if (st != PSA_OK) return st;
+  if (T == 0) return PSA_OK;
+  if (!q || !k || !v || !o || !lse) return psa_set_error(PSA_ERR_NULL, "tensor pointer is NULL");
+  AttnShape s{T, hq, hkv, d, scale > 0.f ? scale : 1.0f / std::sqrt(float(d))};
+  hipError_t e = launch_fwd(*map, dtype, s, q, k, v, o, lse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return psa_hip_error(e, "forward launch");
+  return PSA_OK;
+}
+
+psa_status psa_bwd_workspace_size(const psa_tile_map* map, psa_dtype dtype, int64_t T,
+                                  int32_t hq, int32_t hkv, int32_t d, size_t* bytes) {
+  if (!bytes) return psa_set_error(PSA_ERR_NULL, "bytes is NULL");
+  psa_status st = check_attn_args(map, dtype, T, hq, hkv, d, 1.0f, PSA_PASS_BWD);
+  if (st != PSA_OK) return st;
+  *bytes = bwd_workspace_bytes(AttnShape{T, hq, hkv, d, 1.0f});
+  return PSA_OK;
+}
+
+psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype, int64_t T,
+                   int32_t hq, int32_t hkv, int32_t d, float scale, const void* q,
+                   const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  psa_status st = check_attn_args(map, dtype, T, hq, hkv, d, scale, PSA_PASS_BWD);
+  if (st != PSA_OK) return st;
+  if (grad_dtype != PSA_FP32 && grad_dtype != dtype)
+    return psa_set_error(PSA_ERR_DTYPE, "grad_dtype must be PSA_FP32 or the input dtype");
+  if (T == 0) return PSA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return psa_set_error(PSA_ERR_NULL, "tensor pointer is NULL");
+  AttnShape s{T, hq, hkv, d, scale > 0.f ? scale : 1.0f / std::sqrt(float(d))};
+  size_t need = bwd_workspace_bytes(s);
+  if (!workspace || workspace_bytes < need)
+    return psa_set_error(PSA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  hipError_t e = launch_bwd(*map, dtype, grad_dtype, s, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return psa_hip_error(e, "backward launch");
+  return PSA_OK;
+}
+
+}  // extern "C"

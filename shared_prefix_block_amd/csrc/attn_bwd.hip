@@ -1,0 +1,477 @@
+// Backward kernels (FlashAttention-2 style gradients of the block-sparse forward).
+//
+//   bwd_pre : Dl[h, q] = sum_d dO[q, h, d] * O[q, h, d];  L2[h, q] = LSE * log2(e)
+//             (+inf on rows that saw no key, so their probabilities come out 0).
+//   dkdv    : one work-group per (kv-tile of 128 keys, kv head).  K and V stay in
+//             registers; the CSC list of the kv-tile's non-empty q-tiles is walked for
+//             every q head of the GQA group, so dK and dV are summed over the group
+//             inside the work-group (no atomics, no repeated K/V).  Per q sub-step:
+//             S = Q K^T and dP = dO V^T (Q, dO from LDS), P = exp2(S c - L2), masked on
+//             partial tiles, dS = P (dP - Dl), dV^T += dO^T P, dK^T += Q^T dS.
+//   dq      : one work-group per (q-tile, q head), walking the CSR list like the
+//             forward: S^T = K Q^T and dP^T = V dO^T (Q, dO in registers), the same
+//             P and dS, dQ^T += K^T dS^T.  Recomputing P here costs two extra
+//             products but keeps dQ free of atomics and deterministic.
+// dK and dQ are scaled by the softmax scale on the way out.
+//
+// Source of the gradient formulas: the analytic softmax-attention backward
+// (FlashAttention-2); the mask, layout and GQA conventions are the forward's
+// (unsloth "prefix_grouper_kernel.py", _make_mask_mod, flex_shared_prefix_attention).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "attn_common.h"
+#include "psa_internal.h"
+
+namespace psa {
+namespace {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* Dl;  // [hq, T]
+  float* L2;  // [hq, T]
+  const int32_t* end;
+  const int32_t* row_ptr;
+  const int32_t* col;
+  const uint8_t* kind;
+  const int32_t* col_ptr;
+  const int32_t* row;
+  const uint8_t* kind_csc;
+  const int32_t* qorder;
+  const int32_t* korder;
+  int64_t T;
+  int32_t hq, hkv;
+  float c;      // scale * log2(e)
+  float scale;  // softmax scale
+  int64_t n_work;
+  int32_t chunk;
+};
+
+// ---------------------------------------------------------------------------
+// bwd_pre: 16 lanes per (row, head); 16 rows per 256-thread block.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  const int64_t rid = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);  // = q * hq + h
+  const int sub = threadIdx.x & 15;
+  const int64_t n = p.T * p.hq;
+  const bool valid = rid < n;
+  const T* O = static_cast<const T*>(p.o);
+  const T* dO = static_cast<const T*>(p.dout);
+  float acc = 0.f;
+  if (valid) {
+    const T* op = O + rid * D;
+    const T* gp = dO + rid * D;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const int d = sub + 16 * i;
+      acc += to_f32(op[d]) * to_f32(gp[d]);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (valid && sub == 0) {
+    const int64_t q = rid / p.hq;
+    const int h = int(rid % p.hq);
+    p.Dl[int64_t(h) * p.T + q] = acc;
+    const float lse = p.lse[int64_t(h) * p.T + q];
+    p.L2[int64_t(h) * p.T + q] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dkdv
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DkdvCfg {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BK = 32 * NW;  // keys per work-group
+  static_assert(BK == kTileN, "kv-tile must match the map");
+  static constexpr int EB = int(sizeof(T));
+  static constexpr int BMS = (D * EB > 256) ? 32 : 64;  // q rows per sub-step
+  static constexpr int NS = D + 16 / EB;                // row-major tile stride
+  static constexpr int TS = BMS + 16 / EB;              // transposed tile stride
+  static constexpr int N_ELEMS = BMS * NS;
+  static constexpr int T_ELEMS = D * TS;
+  static constexpr int LDS_BYTES = 2 * (N_ELEMS + T_ELEMS) * EB + 2 * BMS * 4;
+};
+
+template <typename T, typename G, int D>
+__global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
+  using C = DkdvCfg<T, D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  T* Qs = reinterpret_cast<T*>(smem);
+  T* Qt = Qs + C::N_ELEMS;
+  T* Gs = Qt + C::T_ELEMS;  // dO row-major
+  T* Gt = Gs + C::N_ELEMS;  // dO transposed
+  float* Ls = reinterpret_cast<float*>(Gt + C::T_ELEMS);
+  float* Dsh = Ls + C::BMS;
+
+  const int64_t w_id = xcd_remap(blockIdx.x, p.chunk);
+  if (w_id >= p.n_work) return;
+  const int64_t ntok = p.T;
+  const int hq = p.hq, hkv = p.hkv, rep = hq / hkv;
+  const int hk = int(w_id % hkv);
+  const int kt = p.korder[w_id / hkv];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t kvrow = int64_t(kt) * C::BK + 32 * wave + l32;
+  const bool kvvalid = kvrow < ntok;
+  const int kvrow_i = int(kvrow);
+  const int32_t end_kv = kvvalid ? p.end[kvrow] : kvrow_i;
+
+  const T* Kg = static_cast<const T*>(p.k);
+  const T* Vg = static_cast<const T*>(p.v);
+  const T* Qg = static_cast<const T*>(p.q);
+  const T* Gg = static_cast<const T*>(p.dout);
+
+  Frag<T> kf[D / 16], vf[D / 16];
+  {
+    const int64_t off = (kvrow * hkv + hk) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kf[s] = kvvalid ? frag_load(Kg + off + 16 * s) : frag_zero<T>();
+      vf[s] = kvvalid ? frag_load(Vg + off + 16 * s) : frag_zero<T>();
+    }
+  }
+  f32x16 adk[D / 32], adv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    adk[db] = zero16();
+    adv[db] = zero16();
+  }
+  const float c = p.c;
+  const int64_t ldq = int64_t(hq) * D;
+
+  const int e0 = p.col_ptr[kt], e1 = p.col_ptr[kt + 1];
+  for (int e = e0; e < e1; ++e) {
+    const int i = p.row[e];
+    const bool partial = p.kind_csc[e] == 1;
+    for (int r = 0; r < rep; ++r) {
+      const int h = hk * rep + r;
+      for (int sub = 0; sub < kTileM / C::BMS; ++sub) {
+        const int64_t q0 = int64_t(i) * kTileM + sub * C::BMS;
+        if (q0 >= ntok) break;
+        const int nvalid = ntok - q0 < C::BMS ? int(ntok - q0) : C::BMS;
+        const int q0i = int(q0);
+        __syncthreads();
+        const T* qp = Qg + q0 * ldq + int64_t(h) * D;
+        const T* gp = Gg + q0 * ldq + int64_t(h) * D;
+        stage_rows<T, C::BMS, D, C::NS, C::NT>(Qs, qp, ldq, nvalid);
+        stage_rows_t<T, C::BMS, D, C::TS, C::NT>(Qt, qp, ldq, nvalid);
+        stage_rows<T, C::BMS, D, C::NS, C::NT>(Gs, gp, ldq, nvalid);
+        stage_rows_t<T, C::BMS, D, C::TS, C::NT>(Gt, gp, ldq, nvalid);
+        if (threadIdx.x < C::BMS) {
+          const int rr = threadIdx.x;
+          const bool ok = rr < nvalid;
+          Ls[rr] = ok ? p.L2[int64_t(h) * ntok + q0 + rr] : INFINITY;
+          Dsh[rr] = ok ? p.Dl[int64_t(h) * ntok + q0 + rr] : 0.f;
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int qb = 0; qb < C::BMS / 32; ++qb) {
+          f32x16 sacc = zero16(), pacc = zero16();
+          const T* qr = Qs + (32 * qb + l32) * C::NS + 8 * half;
+          const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
+#pragma unroll
+          for (int s = 0; s < D / 16; ++s) {
+            mma(sacc, frag_load(qr + 16 * s), kf[s]);
+            mma(pacc, frag_load(gr + 16 * s), vf[s]);
+          }
+          float pv[16], ds[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int ql = 32 * qb + g * 8 + half * 4;
+            const f32x4 l2 = *reinterpret_cast<const f32x4*>(Ls + ql);
+            const f32x4 dl = *reinterpret_cast<const f32x4*>(Dsh + ql);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int ii = 4 * g + u;
+              float pr = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2[u]));
+              if (partial) pr = visible(kvrow_i, q0i + ql + u, end_kv) ? pr : 0.f;
+              pv[ii] = pr;
+              ds[ii] = pr * (pacc[ii] - dl[u]);
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            Frag<T> pf, pl, sf, sl;
+            frag_split<T>(pv + 8 * t, pf, pl);
+            frag_split<T>(ds + 8 * t, sf, sl);
+            const int col0 = 32 * qb + 16 * t + 8 * half;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+              const Frag<T> ga = frag_load(Gt + (32 * db + l32) * C::TS + col0);
+              const Frag<T> qa = frag_load(Qt + (32 * db + l32) * C::TS + col0);
+              mma(adv[db], ga, pf);
+              mma(adk[db], qa, sf);
+              if constexpr (NeedsSplit<T>::value) {
+                mma(adv[db], ga, pl);
+                mma(adk[db], qa, sl);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  if (kvvalid) {
+    G* dkp = static_cast<G*>(p.dk) + (kvrow * hkv + hk) * D;
+    G* dvp = static_cast<G*>(p.dv) + (kvrow * hkv + hk) * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + g * 8 + half * 4;
+        vec4_store(dkp + d, vec4_from(adk[db][4 * g] * sc, adk[db][4 * g + 1] * sc,
+                                      adk[db][4 * g + 2] * sc, adk[db][4 * g + 3] * sc,
+                                      static_cast<G*>(nullptr)));
+        vec4_store(dvp + d, vec4_from(adv[db][4 * g], adv[db][4 * g + 1], adv[db][4 * g + 2],
+                                      adv[db][4 * g + 3], static_cast<G*>(nullptr)));
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DqCfg {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = 32 * NW;
+  static_assert(BM == kTileM, "q-tile must match the map");
+  static constexpr int EB = int(sizeof(T));
+  static constexpr int BN = (D * EB > 256) ? 32 : 64;  // keys per sub-step
+  static constexpr int NS = D + 16 / EB;
+  static constexpr int TS = BN + 16 / EB;
+  static constexpr int N_ELEMS = BN * NS;
+  static constexpr int T_ELEMS = D * TS;
+  static constexpr int LDS_BYTES = (2 * N_ELEMS + T_ELEMS) * EB + BN * 4;
+};
+
+template <typename T, typename G, int D>
+__global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
+  using C = DqCfg<T, D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Vs = Ks + C::N_ELEMS;
+  T* Kt = Vs + C::N_ELEMS;
+  int32_t* Es = reinterpret_cast<int32_t*>(Kt + C::T_ELEMS);
+
+  const int64_t w_id = xcd_remap(blockIdx.x, p.chunk);
+  if (w_id >= p.n_work) return;
+  const int64_t ntok = p.T;
+  const int hq = p.hq, hkv = p.hkv, rep = hq / hkv;
+  const int h = int(w_id % hq);
+  const int qt = p.qorder[w_id / hq];
+  const int hk = h / rep;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t qrow = int64_t(qt) * C::BM + 32 * wave + l32;
+  const bool qvalid = qrow < ntok;
+  const int qrow_i = int(qrow);
+
+  const T* Qg = static_cast<const T*>(p.q);
+  const T* Gg = static_cast<const T*>(p.dout);
+  const T* Kg = static_cast<const T*>(p.k);
+  const T* Vg = static_cast<const T*>(p.v);
+
+  Frag<T> qf[D / 16], gf[D / 16];
+  {
+    const int64_t off = (qrow * hq + h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qf[s] = qvalid ? frag_load(Qg + off + 16 * s) : frag_zero<T>();
+      gf[s] = qvalid ? frag_load(Gg + off + 16 * s) : frag_zero<T>();
+    }
+  }
+  const float l2 = qvalid ? p.L2[int64_t(h) * ntok + qrow] : INFINITY;
+  const float dl = qvalid ? p.Dl[int64_t(h) * ntok + qrow] : 0.f;
+  f32x16 adq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) adq[db] = zero16();
+  const float c = p.c;
+  const int64_t ldk = int64_t(hkv) * D;
+
+  const int e0 = p.row_ptr[qt], e1 = p.row_ptr[qt + 1];
+  for (int e = e0; e < e1; ++e) {
+    const int j = p.col[e];
+    const bool partial = p.kind[e] == 1;
+    for (int sub = 0; sub < kTileN / C::BN; ++sub) {
+      const int64_t kv0 = int64_t(j) * kTileN + sub * C::BN;
+      if (kv0 >= ntok) break;
+      const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
+      const int kv0i = int(kv0);
+      __syncthreads();
+      const T* kp = Kg + kv0 * ldk + int64_t(hk) * D;
+      const T* vp = Vg + kv0 * ldk + int64_t(hk) * D;
+      stage_rows<T, C::BN, D, C::NS, C::NT>(Ks, kp, ldk, nvalid);
+      stage_rows<T, C::BN, D, C::NS, C::NT>(Vs, vp, ldk, nvalid);
+      stage_rows_t<T, C::BN, D, C::TS, C::NT>(Kt, kp, ldk, nvalid);
+      if (partial && threadIdx.x < C::BN) {
+        const int r = threadIdx.x;
+        Es[r] = r < nvalid ? p.end[kv0 + r] : int32_t(kv0 + r);
+      }
+      __syncthreads();
+
+      f32x16 ds[C::BN / 32];
+#pragma unroll
+      for (int kb = 0; kb < C::BN / 32; ++kb) {
+        f32x16 sacc = zero16(), pacc = zero16();
+        const T* kr = Ks + (32 * kb + l32) * C::NS + 8 * half;
+        const T* vr = Vs + (32 * kb + l32) * C::NS + 8 * half;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          mma(sacc, frag_load(kr + 16 * s), qf[s]);
+          mma(pacc, frag_load(vr + 16 * s), gf[s]);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2));
+          if (partial) {
+            const int kvl = 32 * kb + acc_row(ii, half);
+            pr = visible(kv0i + kvl, qrow_i, Es[kvl]) ? pr : 0.f;
+          }
+          ds[kb][ii] = pr * (pacc[ii] - dl);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < C::BN / 16; ++t) {
+        float sv[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sv[jj] = ds[t >> 1][(t & 1) * 8 + jj];
+        Frag<T> sf, sl;
+        frag_split<T>(sv, sf, sl);
+        const T* kr = Kt + l32 * C::TS + 16 * t + 8 * half;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const Frag<T> ka = frag_load(kr + 32 * db * C::TS);
+          mma(adq[db], ka, sf);
+          if constexpr (NeedsSplit<T>::value) mma(adq[db], ka, sl);
+        }
+      }
+    }
+  }
+
+  if (qvalid) {
+    G* dqp = static_cast<G*>(p.dq) + (qrow * hq + h) * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + g * 8 + half * 4;
+        vec4_store(dqp + d, vec4_from(adq[db][4 * g] * sc, adq[db][4 * g + 1] * sc,
+                                      adq[db][4 * g + 2] * sc, adq[db][4 * g + 3] * sc,
+                                      static_cast<G*>(nullptr)));
+      }
+  }
+}
+
+size_t ws_align(size_t x) { return (x + 255) / 256 * 256; }
+
+template <typename T, typename G, int D>
+hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void* q,
+                        const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                        hipStream_t stream) {
+  BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  const size_t plane = ws_align(size_t(s.T) * s.hq * sizeof(float));
+  p.Dl = static_cast<float*>(workspace);
+  p.L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + plane);
+  p.end = map.end;
+  p.row_ptr = map.row_ptr;
+  p.col = map.col;
+  p.kind = map.kind;
+  p.col_ptr = map.col_ptr;
+  p.row = map.row;
+  p.kind_csc = map.kind_csc;
+  p.qorder = map.qorder;
+  p.korder = map.korder;
+  p.T = s.T;
+  p.hq = s.hq;
+  p.hkv = s.hkv;
+  p.scale = s.scale;
+  p.c = s.scale * kLog2e;
+  const int rep = s.hq / s.hkv;
+
+  const int64_t rows = s.T * s.hq;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(unsigned((rows + 15) / 16)), dim3(256), 0,
+                     stream, p);
+
+  p.n_work = map.nk * s.hkv;
+  p.chunk = 2;
+  int64_t per = 8 * int64_t(p.chunk);
+  int64_t grid = (p.n_work + per - 1) / per * per;
+  hipLaunchKernelGGL((dkdv_kernel<T, G, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+
+  p.n_work = map.nq * s.hq;
+  p.chunk = rep * 2;
+  per = 8 * int64_t(p.chunk);
+  grid = (p.n_work + per - 1) / per * per;
+  hipLaunchKernelGGL((dq_kernel<T, G, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace psa
+
+bool bwd_supported(psa_dtype dt, int32_t d) { return fwd_supported(dt, d); }
+
+size_t bwd_workspace_bytes(const AttnShape& s) {
+  return 2 * psa::ws_align(size_t(s.T) * s.hq * sizeof(float));
+}
+
+hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype gdt, const AttnShape& s,
+                      const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, hipStream_t stream) {
+  using psa::bf16_t;
+#define PSA_BWD(T, G, D) \
+  return psa::launch_bwd_t<T, G, D>(map, s, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream)
+  if (dt == PSA_BF16 && gdt == PSA_FP32) {
+    switch (s.d) {
+      case 64: PSA_BWD(bf16_t, float, 64);
+      case 128: PSA_BWD(bf16_t, float, 128);
+      case 256: PSA_BWD(bf16_t, float, 256);
+    }
+  } else if (dt == PSA_BF16 && gdt == PSA_BF16) {
+    switch (s.d) {
+      case 64: PSA_BWD(bf16_t, bf16_t, 64);
+      case 128: PSA_BWD(bf16_t, bf16_t, 128);
+      case 256: PSA_BWD(bf16_t, bf16_t, 256);
+    }
+  } else if (dt == PSA_FP32 && gdt == PSA_FP32) {
+    switch (s.d) {
+      case 64: PSA_BWD(float, float, 64);
+      case 128: PSA_BWD(float, float, 128);
+    }
+  }
+#undef PSA_BWD
+  return hipErrorInvalidValue;
+}

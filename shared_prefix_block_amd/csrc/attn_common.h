@@ -1,0 +1,305 @@
+// Building blocks shared by the forward and backward attention kernels (gfx950).
+//
+// Matrix work uses the CDNA 32x32 MFMA shapes: v_mfma_f32_32x32x16_bf16 for bf16
+// inputs and v_mfma_f32_32x32x2_f32 for fp32 inputs, both accumulating in fp32.
+// A "fragment" is the 8 consecutive reduction-index values one lane feeds to a
+// 32x32 product over 16 reduction indices: lane l (row or column l % 32, half
+// h = l / 32) holds reduction indices 8h .. 8h+7.  For bf16 that is one MFMA; for
+// fp32 it is 8 MFMAs of 2 reduction indices each (lane half h supplies index j of
+// its 8 in MFMA j), which sums the same 16 products in another order.
+//
+// Accumulator layout of a 32x32 block (the same for both MFMAs): lane l holds
+// column l % 32 and rows (i / 4) * 8 + (l / 32) * 4 + (i % 4) for i = 0 .. 15.
+//
+// Scores are formed with the key index as the row (S^T = K Q^T), so each lane owns
+// one query column and the row-wise softmax needs only in-lane work plus one
+// exchange between lane halves.  The probabilities then feed the second product
+// straight from registers as its B operand; the reduction index (keys) of that
+// operand follows the accumulator's row order, so the tiles used as the A operand
+// are stored transposed in LDS with rows permuted to match: within every 16 rows,
+// groups of 4 rows (g = 0..3) sit at slots 0, 2, 1, 3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace psa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16_t {  // raw bfloat16 storage
+  uint16_t bits;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// fragments
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Frag;
+template <>
+struct Frag<bf16_t> {
+  u32x4 v;
+};
+template <>
+struct Frag<float> {
+  f32x4 lo, hi;
+};
+
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_zero();
+template <>
+__device__ __forceinline__ Frag<bf16_t> frag_zero<bf16_t>() {
+  Frag<bf16_t> f;
+  f.v = u32x4{0u, 0u, 0u, 0u};
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> frag_zero<float>() {
+  Frag<float> f;
+  f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+  f.hi = f.lo;
+  return f;
+}
+
+// 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32).
+__device__ __forceinline__ Frag<bf16_t> frag_load(const bf16_t* p) {
+  Frag<bf16_t> f;
+  f.v = *reinterpret_cast<const u32x4*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag<float> frag_load(const float* p) {
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);  // round to nearest even
+  return uint32_t(__builtin_bit_cast(uint16_t, x)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
+}
+
+// Fragment from 8 fp32 values (probabilities or score gradients).
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from(const float* x);
+template <>
+__device__ __forceinline__ Frag<bf16_t> frag_from<bf16_t>(const float* x) {
+  Frag<bf16_t> f;
+  f.v = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+              pack_bf16x2(x[6], x[7])};
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> frag_from<float>(const float* x) {
+  Frag<float> f;
+  f.lo = f32x4{x[0], x[1], x[2], x[3]};
+  f.hi = f32x4{x[4], x[5], x[6], x[7]};
+  return f;
+}
+
+// Split of 8 fp32 values into hi = bf16(x) and lo = bf16(x - hi): a product with
+// hi + lo (two MFMAs, exact bf16 x bf16 products, fp32 sums) keeps about 16 significant
+// bits of x instead of 8.  The backward uses it for P and dS, whose bf16 rounding
+// would otherwise dominate the error of dQ, dK and dV.  fp32 fragments need no split.
+template <typename T>
+struct NeedsSplit {
+  static constexpr bool value = false;
+};
+template <>
+struct NeedsSplit<bf16_t> {
+  static constexpr bool value = true;
+};
+
+__device__ __forceinline__ float bf16_round(float x) {
+  return __builtin_bit_cast(float, uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)))
+                                       << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ void frag_split(const float* x, Frag<T>& hi, Frag<T>& lo) {
+  hi = frag_from<T>(x);
+  if constexpr (NeedsSplit<T>::value) {
+    float r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = x[j] - bf16_round(x[j]);
+    lo = frag_from<T>(r);
+  } else {
+    lo = hi;  // unused
+  }
+}
+
+__device__ __forceinline__ void mma(f32x16& c, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                              __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const Frag<float>& a, const Frag<float>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[0], b.lo[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[1], b.lo[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[2], b.lo[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[3], b.lo[3], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[0], b.hi[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[1], b.hi[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[2], b.hi[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[3], b.hi[3], c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// The mask in interval form: key kv is visible to row q iff kv <= q < end[kv].
+// Evaluated as one select (no short-circuit branch) so it stays a v_cndmask.
+__device__ __forceinline__ bool visible(int kv, int q, int end_kv) {
+  return (kv <= q) & (q < end_kv);
+}
+
+// Row (within a 32x32 accumulator block) of element i for lane half h.
+__device__ __forceinline__ int acc_row(int i, int half) { return (i >> 2) * 8 + half * 4 + (i & 3); }
+
+// Position of row r inside a transposed, row-permuted tile (see the file comment).
+__device__ __forceinline__ int perm_pos(int r) {
+  const int g = (r >> 2) & 3;
+  return (r & ~15) + (((g & 1) << 1) | (g >> 1)) * 4 + (r & 3);
+}
+
+// ---------------------------------------------------------------------------
+// 4-element vectors for stores and the transposing stage
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Vec4;
+template <>
+struct Vec4<bf16_t> {
+  u32x2 v;
+};
+template <>
+struct Vec4<float> {
+  f32x4 v;
+};
+
+__device__ __forceinline__ Vec4<bf16_t> vec4_load(const bf16_t* p) {
+  Vec4<bf16_t> r;
+  r.v = *reinterpret_cast<const u32x2*>(p);
+  return r;
+}
+__device__ __forceinline__ Vec4<float> vec4_load(const float* p) {
+  Vec4<float> r;
+  r.v = *reinterpret_cast<const f32x4*>(p);
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ Vec4<T> vec4_zero();
+template <>
+__device__ __forceinline__ Vec4<bf16_t> vec4_zero<bf16_t>() {
+  Vec4<bf16_t> r;
+  r.v = u32x2{0u, 0u};
+  return r;
+}
+template <>
+__device__ __forceinline__ Vec4<float> vec4_zero<float>() {
+  Vec4<float> r;
+  r.v = f32x4{0.f, 0.f, 0.f, 0.f};
+  return r;
+}
+__device__ __forceinline__ void vec4_store(bf16_t* p, const Vec4<bf16_t>& x) {
+  *reinterpret_cast<u32x2*>(p) = x.v;
+}
+__device__ __forceinline__ void vec4_store(float* p, const Vec4<float>& x) {
+  *reinterpret_cast<f32x4*>(p) = x.v;
+}
+__device__ __forceinline__ Vec4<bf16_t> vec4_from(float a, float b, float c, float d,
+                                                  bf16_t*) {
+  Vec4<bf16_t> r;
+  r.v = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  return r;
+}
+__device__ __forceinline__ Vec4<float> vec4_from(float a, float b, float c, float d, float*) {
+  Vec4<float> r;
+  r.v = f32x4{a, b, c, d};
+  return r;
+}
+
+// 4x4 transpose: in r[k] = row k (4 columns); out c[j] = column j (4 rows).
+__device__ __forceinline__ void transpose4(const Vec4<bf16_t>* r, Vec4<bf16_t>* c) {
+  // element (k, j) is 16-bit half (j & 1) of word (j >> 1) of r[k]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int w = j >> 1, sh = (j & 1) * 16;
+    uint32_t e0 = (r[0].v[w] >> sh) & 0xffffu, e1 = (r[1].v[w] >> sh) & 0xffffu;
+    uint32_t e2 = (r[2].v[w] >> sh) & 0xffffu, e3 = (r[3].v[w] >> sh) & 0xffffu;
+    c[j].v = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+  }
+}
+__device__ __forceinline__ void transpose4(const Vec4<float>* r, Vec4<float>* c) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j].v = f32x4{r[0].v[j], r[1].v[j], r[2].v[j], r[3].v[j]};
+}
+
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __builtin_bit_cast(float, uint32_t(x.bits) << 16);
+}
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// ---------------------------------------------------------------------------
+// Global -> LDS staging of one tile of `R` rows x `D` columns of a [T, heads, D]
+// tensor (row stride `ld` elements); rows at or past `nvalid` are zero-filled.
+// ---------------------------------------------------------------------------
+// Row-major copy: dst[r * S + c].
+template <typename T, int R, int D, int S, int NT>
+__device__ __forceinline__ void stage_rows(T* dst, const T* src, int64_t ld, int nvalid) {
+  constexpr int E = 16 / int(sizeof(T));  // elements per 16-byte chunk
+  constexpr int CPR = D / E;              // chunks per row
+  constexpr int CHUNKS = R * CPR;
+  static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
+#pragma unroll
+  for (int it = 0; it < CHUNKS / NT; ++it) {
+    const int c = it * NT + int(threadIdx.x);
+    const int r = c / CPR, cc = (c % CPR) * E;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (r < nvalid) val = *reinterpret_cast<const u32x4*>(src + int64_t(r) * ld + cc);
+    *reinterpret_cast<u32x4*>(dst + r * S + cc) = val;
+  }
+}
+
+// Transposed, row-permuted copy: dst[c * S + perm_pos(r)].  Each thread moves 4x4
+// blocks: 4 row loads (consecutive threads read consecutive columns of a row), an
+// in-register transpose, 4 stores of 4 permuted-row values each.
+template <typename T, int R, int D, int S, int NT>
+__device__ __forceinline__ void stage_rows_t(T* dst, const T* src, int64_t ld, int nvalid) {
+  constexpr int CG = D / 4;  // column groups
+  constexpr int BLOCKS = (R / 4) * CG;
+  static_assert(BLOCKS % NT == 0, "tile must split evenly over the threads");
+#pragma unroll
+  for (int it = 0; it < BLOCKS / NT; ++it) {
+    const int b = it * NT + int(threadIdx.x);
+    const int r0 = (b / CG) * 4, c0 = (b % CG) * 4;
+    Vec4<T> rows[4], cols[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      rows[k] = (r0 + k < nvalid) ? vec4_load(src + int64_t(r0 + k) * ld + c0) : vec4_zero<T>();
+    transpose4(rows, cols);
+    const int pos = perm_pos(r0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vec4_store(dst + (c0 + j) * S + pos, cols[j]);
+  }
+}
+
+// blockIdx -> work item so that runs of `chunk` consecutive items land on one XCD
+// (work-groups are dealt to the 8 XCDs round-robin).  `grid` is a multiple of 8*chunk.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t chunk) {
+  const int64_t xcd = bid & 7, slot = bid >> 3;
+  return ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
+}
+
+}  // namespace psa

@@ -1,0 +1,90 @@
+// Internal declarations shared by the C ABI (api.cpp) and the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "psa.h"
+
+// The tile map: per-token interval ends plus the full/partial/empty classification
+// of every (q-tile, kv-tile) pair, as a dense kinds matrix and as CSR / CSC lists.
+struct psa_tile_map {
+  int64_t T = 0;
+  int32_t bm = 0, bn = 0;
+  int64_t nq = 0, nk = 0;
+  int64_t nnz = 0, n_full = 0, n_partial = 0;
+  int device = 0;
+  hipStream_t stream = nullptr;  // build stream (export waits on it)
+
+  // phase-1 allocation (sized before the sync)
+  void* buf1 = nullptr;
+  int32_t* end = nullptr;      // [T]      key t visible to rows q in [t, end[t])
+  uint8_t* kinds = nullptr;    // [nq*nk]  0 empty, 1 partial, 2 full (row-major)
+  int32_t* row_ptr = nullptr;  // [nq+1]
+  int32_t* col_ptr = nullptr;  // [nk+1]
+  // phase-2 allocation (sized after the sync)
+  void* buf2 = nullptr;
+  int32_t* col = nullptr;       // [nnz] CSR kv-tile index
+  uint8_t* kind = nullptr;      // [nnz] CSR kind
+  int32_t* row = nullptr;       // [nnz] CSC q-tile index
+  uint8_t* kind_csc = nullptr;  // [nnz] CSC kind
+  int32_t* qorder = nullptr;    // [nq]  q-tiles by descending CSR row length
+  int32_t* korder = nullptr;    // [nk]  kv-tiles by descending CSC column length
+  std::vector<int32_t> host_orders;  // staging of qorder/korder (lives with the map)
+};
+
+// Error helpers (api.cpp)
+psa_status psa_set_error(psa_status s, const std::string& msg);
+psa_status psa_hip_error(hipError_t e, const char* what);
+
+// ---------------------------------------------------------------------------
+// tilemap.hip
+// ---------------------------------------------------------------------------
+// Per-token interval ends from labels; flag[0] receives a nonzero layout-error code
+// (the first offending position + 1 in flag[1]).
+hipError_t launch_tokens_end(int64_t T, const int32_t* group, const int32_t* suffix,
+                             const uint8_t* is_prefix, int32_t* end, int32_t* flag,
+                             hipStream_t stream);
+// Per-token interval ends from a per-node table (node token start, node subtree end).
+hipError_t launch_tree_end(int64_t T, int64_t n_nodes, const int64_t* node_start,
+                           const int64_t* node_subtree_end, int64_t t_real, int32_t* end,
+                           hipStream_t stream);
+// Classification + counts + pointer scans.  info (device, 8 x int64) receives
+// nnz, n_full, n_partial.
+hipError_t launch_classify(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk,
+                           const int32_t* end, uint8_t* kinds, int32_t* row_ptr,
+                           int32_t* col_ptr, int32_t* ktile_min_end, int32_t* ktile_max_end,
+                           int64_t* info, hipStream_t stream);
+hipError_t launch_fill_lists(int64_t nq, int64_t nk, const uint8_t* kinds,
+                             const int32_t* row_ptr, const int32_t* col_ptr, int32_t* col,
+                             uint8_t* kind, int32_t* row, uint8_t* kind_csc,
+                             hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// attention kernels
+// ---------------------------------------------------------------------------
+struct AttnShape {
+  int64_t T;
+  int32_t hq, hkv, d;
+  float scale;  // resolved softmax scale
+};
+
+// Kernel tile shapes (the map's block_m, block_n must equal these).
+constexpr int32_t kTileM = 128;
+constexpr int32_t kTileN = 128;
+
+bool fwd_supported(psa_dtype dt, int32_t d);
+bool bwd_supported(psa_dtype dt, int32_t d);
+
+hipError_t launch_fwd(const psa_tile_map& map, psa_dtype dt, const AttnShape& s,
+                      const void* q, const void* k, const void* v, void* o, float* lse,
+                      hipStream_t stream);
+
+size_t bwd_workspace_bytes(const AttnShape& s);
+hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype grad_dt, const AttnShape& s,
+                      const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, hipStream_t stream);

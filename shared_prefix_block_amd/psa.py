@@ -1,0 +1,312 @@
+"""ctypes binding of libpsa.so (shared-prefix block-sparse attention, gfx950).
+
+Argument marshalling only: tensors are passed as device pointers plus the current
+HIP stream, and every step of the computation runs in the library's HIP kernels.
+If libpsa.so is missing the first call raises; there is no fallback path.
+
+    m = psa.build_tile_map_tokens(group, suffix, is_prefix)          # device int32/uint8
+    o, lse = psa.fwd(m, q, k, v)                                      # [T,hq,d], [hq,T]
+    dq, dk, dv = psa.bwd(m, q, k, v, o, lse, do)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+import numpy as np
+import torch  # loaded first so that its HIP runtime is the one libpsa.so binds to
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpsa.so")
+_lib = None
+_lock = threading.Lock()
+
+PSA_FP32, PSA_BF16 = 0, 1
+PASS_FWD, PASS_BWD = 0, 1
+STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_LAYOUT",
+          4: "PSA_ERR_DTYPE", 5: "PSA_ERR_UNSUPPORTED", 6: "PSA_ERR_MAP_MISMATCH",
+          7: "PSA_ERR_WORKSPACE", 8: "PSA_ERR_HIP", 9: "PSA_ERR_ALLOC", 10: "PSA_ERR_VALUE"}
+
+EXPORTS = ["psa_abi_version", "psa_status_string", "psa_last_error", "psa_tile_shape",
+           "psa_build_tile_map_tokens", "psa_build_tile_map_tree", "psa_tile_map_info_get",
+           "psa_tile_map_export", "psa_tile_map_destroy", "psa_fwd", "psa_bwd_workspace_size",
+           "psa_bwd"]
+
+
+class PsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+class TileMapInfo(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("n_qtiles", ctypes.c_int64), ("n_ktiles", ctypes.c_int64),
+                ("nnz", ctypes.c_int64), ("n_full", ctypes.c_int64),
+                ("n_partial", ctypes.c_int64)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Open libpsa.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(or python -m shared_prefix_block_amd.build)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                              ctypes.c_size_t)
+        PP = ctypes.POINTER(ctypes.c_void_p)
+        sig = {
+            "psa_abi_version": (I32, []),
+            "psa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "psa_last_error": (ctypes.c_char_p, []),
+            "psa_tile_shape": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, I32,
+                                              ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+            "psa_build_tile_map_tokens": (ctypes.c_int, [I64, P, P, P, I32, I32, P, PP]),
+            "psa_build_tile_map_tree": (ctypes.c_int, [I64, P, I64, P, P, I64, I32, I32, P, PP]),
+            "psa_tile_map_info_get": (ctypes.c_int, [P, ctypes.POINTER(TileMapInfo)]),
+            "psa_tile_map_export": (ctypes.c_int, [P, P, P, P, P, P, P, P, P]),
+            "psa_tile_map_destroy": (None, [P]),
+            "psa_fwd": (ctypes.c_int, [P, ctypes.c_int, I64, I32, I32, I32, F, P, P, P, P, P, P]),
+            "psa_bwd_workspace_size": (ctypes.c_int, [P, ctypes.c_int, I64, I32, I32, I32,
+                                                      ctypes.POINTER(SZ)]),
+            "psa_bwd": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, I64, I32, I32, I32, F, P, P,
+                                       P, P, P, P, P, P, P, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        detail = _lib.psa_last_error().decode(errors="replace")
+        raise PsaError(status, detail)
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return PSA_FP32
+    if dt == torch.bfloat16:
+        return PSA_BF16
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def tile_shape(pass_: int, dtype: torch.dtype, d: int):
+    lib = load()
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.psa_tile_shape(pass_, _dtype_code(dtype), d, ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+class TileMap:
+    """Owning handle of a psa_tile_map (destroyed when collected or on close())."""
+
+    def __init__(self, handle: int, device: torch.device, keepalive=None):
+        self._h = ctypes.c_void_p(handle)
+        self.device = device
+        self._keep = keepalive
+        info = TileMapInfo()
+        _check(load().psa_tile_map_info_get(self._h, ctypes.byref(info)))
+        self.info = {f: getattr(info, f) for f, _ in TileMapInfo._fields_}
+        self.T = info.T
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise RuntimeError("tile map already destroyed")
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            torch.cuda.synchronize(self.device)
+            load().psa_tile_map_destroy(self._h)
+            self._h = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            if self._h and _lib is not None:
+                torch.cuda.synchronize(self.device)
+                _lib.psa_tile_map_destroy(self._h)
+                self._h = ctypes.c_void_p(0)
+        except Exception:
+            pass
+
+    def export(self) -> dict:
+        """end, kinds [nq, nk], CSR and CSC as numpy arrays."""
+        i = self.info
+        T, nq, nk, nnz = i["T"], i["n_qtiles"], i["n_ktiles"], i["nnz"]
+        out = {"end": np.zeros(T, np.int32), "kinds": np.zeros(nq * nk, np.uint8),
+               "row_ptr": np.zeros(nq + 1, np.int32), "col": np.zeros(nnz, np.int32),
+               "kind": np.zeros(nnz, np.uint8), "col_ptr": np.zeros(nk + 1, np.int32),
+               "row": np.zeros(nnz, np.int32), "kind_csc": np.zeros(nnz, np.uint8)}
+        args = [ctypes.c_void_p(a.ctypes.data) if a.size else ctypes.c_void_p(0)
+                for a in out.values()]
+        _check(load().psa_tile_map_export(self.handle, *args))
+        out["kinds"] = out["kinds"].reshape(nq, nk)
+        return out
+
+
+def build_tile_map_tokens(group: torch.Tensor, suffix: torch.Tensor, is_prefix: torch.Tensor,
+                          block_m: Optional[int] = None, block_n: Optional[int] = None,
+                          dtype: torch.dtype = torch.bfloat16, d: int = 128) -> TileMap:
+    """Tile map from per-token labels (device tensors: int32, int32, uint8)."""
+    lib = load()
+    if block_m is None or block_n is None:
+        block_m, block_n = tile_shape(PASS_FWD, dtype, d)
+    for t, dt in ((group, torch.int32), (suffix, torch.int32), (is_prefix, torch.uint8)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise TypeError("labels must be contiguous device tensors (int32, int32, uint8)")
+    T = group.numel()
+    if suffix.numel() != T or is_prefix.numel() != T:
+        raise ValueError("label tensors differ in length")
+    dev = group.device
+    out = ctypes.c_void_p()
+    with torch.cuda.device(dev):
+        _check(lib.psa_build_tile_map_tokens(T, _ptr(group), _ptr(suffix), _ptr(is_prefix),
+                                             block_m, block_n, _stream(dev), ctypes.byref(out)))
+    return TileMap(out.value, dev)
+
+
+def build_tile_map_tree(node_lengths: Sequence[int], sample_paths: Sequence[Sequence[int]],
+                        T: Optional[int] = None, device=None, block_m: Optional[int] = None,
+                        block_n: Optional[int] = None, dtype: torch.dtype = torch.bfloat16,
+                        d: int = 128) -> TileMap:
+    """Tile map from a prefix tree given on the host."""
+    lib = load()
+    if block_m is None or block_n is None:
+        block_m, block_n = tile_shape(PASS_FWD, dtype, d)
+    dev = torch.device(device) if device is not None else torch.device("cuda",
+                                                                       torch.cuda.current_device())
+    nl = np.ascontiguousarray(np.asarray(node_lengths, dtype=np.int32))
+    ptr = np.zeros(len(sample_paths) + 1, np.int32)
+    for s, p in enumerate(sample_paths):
+        ptr[s + 1] = ptr[s] + len(p)
+    nodes = np.ascontiguousarray(np.asarray([n for p in sample_paths for n in p], dtype=np.int32))
+    if T is None:
+        T = int(nl.sum())
+    out = ctypes.c_void_p()
+
+    def addr(a):
+        return ctypes.c_void_p(a.ctypes.data if a.size else 0)
+
+    with torch.cuda.device(dev):
+        _check(lib.psa_build_tile_map_tree(len(nl), addr(nl), len(sample_paths), addr(ptr),
+                                           addr(nodes), int(T), block_m, block_n, _stream(dev),
+                                           ctypes.byref(out)))
+    return TileMap(out.value, dev)
+
+
+def _check_qkv(q, k, v):
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [T, heads, d]")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v must share a dtype")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError("shape mismatch between q and k/v")
+
+
+def fwd(m: TileMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None):
+    """O [T, hq, d] (q's dtype) and LSE [hq, T] float32."""
+    lib = load()
+    _check_qkv(q, k, v)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty(hq, T, device=q.device, dtype=torch.float32) if lse is None else lse
+    with torch.cuda.device(q.device):
+        _check(lib.psa_fwd(m.handle, _dtype_code(q.dtype), T, hq, hkv, d,
+                           0.0 if scale is None else float(scale), _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(o), _ptr(lse_t), _stream(q.device)))
+    return o, lse_t
+
+
+def bwd_workspace_size(m: TileMap, q: torch.Tensor, k: torch.Tensor) -> int:
+    lib = load()
+    T, hq, d = q.shape
+    n = ctypes.c_size_t()
+    _check(lib.psa_bwd_workspace_size(m.handle, _dtype_code(q.dtype), T, hq, k.shape[1], d,
+                                      ctypes.byref(n)))
+    return n.value
+
+
+def bwd(m: TileMap, q, k, v, o, lse, do, scale: Optional[float] = None,
+        workspace: Optional[torch.Tensor] = None, grad_dtype: torch.dtype = torch.float32):
+    """dQ, dK, dV in ``grad_dtype`` (float32, the default, or q's dtype)."""
+    lib = load()
+    _check_qkv(q, k, v)
+    for t in (o, do):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("o and do must match q")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [hq, T]")
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    need = bwd_workspace_size(m, q, k)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.psa_bwd(m.handle, _dtype_code(q.dtype), _dtype_code(grad_dtype), T, hq, hkv, d,
+                           0.0 if scale is None else float(scale), _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(q.device)))
+    return dq, dk, dv
+
+
+class PrefixAttention(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in libpsa's kernels."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, tile_map, scale=None):
+        o, lse = fwd(tile_map, q.contiguous(), k.contiguous(), v.contiguous(), scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.tile_map = tile_map
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(ctx.tile_map, q, k, v, o, lse, do.to(q.dtype).contiguous(), ctx.scale)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
+
+
+def layout_tile_map(layout, device, dtype: torch.dtype = torch.bfloat16, d: int = 128,
+                    block_m: Optional[int] = None, block_n: Optional[int] = None) -> TileMap:
+    """Tile map of a workloads.Layout (token labels are copied to the device)."""
+    if layout.kind == "tokens":
+        g = torch.as_tensor(layout.group, dtype=torch.int32).to(device)
+        s = torch.as_tensor(layout.suffix, dtype=torch.int32).to(device)
+        p = torch.as_tensor(layout.is_prefix, dtype=torch.uint8).to(device)
+        return build_tile_map_tokens(g, s, p, block_m, block_n, dtype, d)
+    return build_tile_map_tree(layout.node_lengths, layout.sample_paths, layout.T, device,
+                               block_m, block_n, dtype, d)

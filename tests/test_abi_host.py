@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute call).
+
+The library must load, export every function psa.h declares, and reject bad
+arguments before touching the GPU.  Tree layouts are validated on the host, so the
+layout rules of the tree builder are tested here too.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from shared_prefix_block_amd import psa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(psa.lib_path()):
+        pytest.skip("libpsa.so not built")
+    return psa.load()
+
+
+def test_header_declares_binding_exports():
+    assert _declared() == sorted(psa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.psa_abi_version() == 1
+    for code, name in psa.STATUS.items():
+        s = lib.psa_status_string(code).decode()
+        assert s and s != "unknown status", name
+    assert lib.psa_status_string(99).decode() == "unknown status"
+
+
+def test_tile_shape(lib):
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.psa_tile_shape(0, 1, 128, ctypes.byref(bm), ctypes.byref(bn)) == 0
+    assert (bm.value, bn.value) == (128, 128)
+    assert lib.psa_tile_shape(1, 0, 64, ctypes.byref(bm), ctypes.byref(bn)) == 0
+    assert lib.psa_tile_shape(0, 1, 96, ctypes.byref(bm), ctypes.byref(bn)) == 5
+    assert lib.psa_tile_shape(0, 0, 256, ctypes.byref(bm), ctypes.byref(bn)) == 5
+    assert lib.psa_tile_shape(0, 7, 128, ctypes.byref(bm), ctypes.byref(bn)) == 4
+    assert lib.psa_tile_shape(0, 1, 128, None, ctypes.byref(bn)) == 1
+
+
+def _tree(lib, nl, paths, T=None, bm=128, bn=128):
+    import numpy as np
+    nl_a = np.asarray(nl, np.int32)
+    ptr = np.zeros(len(paths) + 1, np.int32)
+    for i, p in enumerate(paths):
+        ptr[i + 1] = ptr[i] + len(p)
+    nodes = np.asarray([n for p in paths for n in p] or [0], np.int32)
+    out = ctypes.c_void_p()
+    T = int(nl_a.sum()) if T is None else T
+    st = lib.psa_build_tile_map_tree(len(nl), ctypes.c_void_p(nl_a.ctypes.data), len(paths),
+                                     ctypes.c_void_p(ptr.ctypes.data),
+                                     ctypes.c_void_p(nodes.ctypes.data), T, bm, bn, None,
+                                     ctypes.byref(out))
+    return st, lib.psa_last_error().decode()
+
+
+@pytest.mark.parametrize("nl,paths,why", [
+    ([4, 4, 4], [[0, 1], [2, 1]], "two different parents"),
+    ([4, 4, 4], [[0, 1]], "lies on no path"),
+    ([4, 4], [[0, 5]], "out of range"),
+    ([4, -1], [[0, 1]], "negative node length"),
+    ([4, 4, 4, 4], [[0, 2], [0, 1, 3]], "pre-order"),  # 3 is a child of 1 but follows 2
+    ([4, 4], [[1, 0]], "pre-order"),  # a child before its parent
+    ([4], [[]], "empty"),
+])
+def test_tree_layout_rejected_on_host(lib, nl, paths, why):
+    st, msg = _tree(lib, nl, paths)
+    assert st == 3, (st, msg)
+    assert why in msg
+
+
+def test_tree_shape_errors(lib):
+    st, msg = _tree(lib, [4, 4], [[0, 1]], T=7)
+    assert st == 2 and "shorter" in msg
+    st, _ = _tree(lib, [4, 4], [[0, 1]], bm=0)
+    assert st == 2
+    st, _ = _tree(lib, [4, 4], [[0, 1]], bn=2048)
+    assert st == 2
+
+
+def test_token_builder_argument_errors(lib):
+    out = ctypes.c_void_p()
+    assert lib.psa_build_tile_map_tokens(16, None, None, None, 128, 128, None,
+                                         ctypes.byref(out)) == 1
+    assert lib.psa_build_tile_map_tokens(16, None, None, None, 128, 128, None, None) == 1
+    assert lib.psa_build_tile_map_tokens(-1, None, None, None, 128, 128, None,
+                                         ctypes.byref(out)) == 2
+    assert lib.psa_build_tile_map_tokens(16, None, None, None, 0, 128, None,
+                                         ctypes.byref(out)) == 2
+
+
+def test_attention_argument_errors(lib):
+    assert lib.psa_fwd(None, 1, 16, 2, 2, 128, 0.0, None, None, None, None, None, None) == 1
+    n = ctypes.c_size_t()
+    assert lib.psa_bwd_workspace_size(None, 1, 16, 2, 2, 128, ctypes.byref(n)) == 1
+    assert lib.psa_bwd(None, 1, 0, 16, 2, 2, 128, 0.0, *([None] * 9), None, 0, None) == 1
+    assert lib.psa_tile_map_info_get(None, None) == 1
+    assert lib.psa_tile_map_export(None, *([None] * 8)) == 1
+    lib.psa_tile_map_destroy(None)  # no-op
