@@ -1,0 +1,268 @@
+"""Benchmark of the shared-prefix attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+One step = one pass of the whole path over one batch of synthetic input: build the
+tile map from the per-token labels (label scan -> interval ends -> classification ->
+CSR/CSC), the forward (O, LSE), then the backward (prepare, dK/dV, dQ).  Inputs and
+outputs stay resident in HBM; nothing is skipped inside the timed region.
+
+The default workload is the 8-group rollout batch (P = 512, G = 8 completions of
+R = 256 each, T = 20480, 32 q heads / 8 kv heads, head_dim 128, bf16, dO ~ N(0,1)).
+Prints one JSON line: effective TFLOP/s over unmasked 128x128 tiles (fwd 4*d and
+bwd 10*d FLOPs per pair per q head), its share of the bf16 MFMA peak, tokens/s, a
+roofline entry for the dominant kernel (timed live with HIP events on the stream the
+kernels run on) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (unmasked tiles) fwd+bwd, % bf16 MFMA peak; tokens/s"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA
+HBM_PEAK_GBS = 8000.0
+TILE = 128
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd.hip", "attn_bwd.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "shared_prefix_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kept_pairs(lay) -> int:
+    """Exact number of kept (q, kv) pairs of a packed layout (per q head)."""
+    if lay.kind == "tokens":
+        return sum(p * (p + 1) // 2 + sum(r * p + r * (r + 1) // 2 for r in rs)
+                   for p, rs in lay.specs)
+    anc = {}
+    for path in lay.sample_paths:
+        acc = 0
+        for n in path:
+            anc[n] = acc
+            acc += lay.node_lengths[n]
+    return sum(ln * (ln + 1) // 2 + ln * anc[n] for n, ln in enumerate(lay.node_lengths))
+
+
+def describe(cfg, lay) -> str:
+    if lay.kind == "tokens":
+        ps = sorted({p for p, _ in lay.specs})
+        layout = (f"{len(lay.specs)} groups, P={ps[0]}" if len(ps) == 1
+                  else f"{len(lay.specs)} groups, P in [{ps[0]},{ps[-1]}]")
+        rs = sorted({r for _, r_ in lay.specs for r in r_})
+        g = {len(r_) for _, r_ in lay.specs}
+        layout += f", G={'/'.join(map(str, sorted(g)))}, R=" + (
+            str(rs[0]) if len(rs) == 1 else f"[{rs[0]},{rs[-1]}]")
+    else:
+        layout = "8 trees: root 1024 -> 4 x 256 -> 4 x 384 leaves"
+    return (f"shared-prefix attention fwd+bwd: {layout}, T={lay.T}, "
+            f"hq={cfg.hq}/hkv={cfg.hkv}, d={cfg.d}, {cfg.dtype}")
+
+
+def cpu_baseline(cfg, lay, sample_seconds_hint=20.0):
+    """Time the float64 oracle on one group of the workload, all heads; scale to the
+    whole workload's effective FLOPs.  Returns the cpu_baseline dict."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as oa
+    from oracle.mask import meta_from_layout
+    from shared_prefix_block_amd import workloads as wl
+
+    if lay.kind == "tokens":
+        p, rs = lay.specs[0]
+        sub = wl.tokens_layout([(p, rs)])
+        frac = kept_pairs(sub) / kept_pairs(lay)
+        what = f"group 0 of {len(lay.specs)} (T={sub.T}), all {cfg.hq} q heads"
+    else:
+        nl = lay.node_lengths[:21]
+        sp = [pth for pth in lay.sample_paths if max(pth) < 21]
+        sub = wl.tree_layout(nl, sp)
+        frac = kept_pairs(sub) / kept_pairs(lay)
+        what = f"tree 0 of 8 (T={sub.T}), all {cfg.hq} q heads"
+    q, k, v, do = wl.make_tensors(sub.T, cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.sigma, cfg.idx)
+    meta = meta_from_layout(sub)
+    t0 = time.perf_counter()
+    if cfg.passes == "fwd":
+        oa.forward(meta, q, k, v)
+    else:
+        oa.backward(meta, q, k, v, do)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return {"sample": what, "frac": frac, "seconds": dt, "cores": int(threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"])
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures the single-GPU hot path only: the shared-prefix attention "
+              "path has no cross-GPU step here (groups and heads shard with no communication); "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from shared_prefix_block_amd import psa
+    from shared_prefix_block_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    psa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = wl.CONFIGS[args.config]
+    lay = wl.layout_for(cfg)
+    q, k, v, do = wl.config_tensors(cfg, lay)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    backward = cfg.passes != "fwd"
+    do = do.to(dev) if backward else None
+    if lay.kind == "tokens":
+        labels = (torch.as_tensor(lay.group).to(dev), torch.as_tensor(lay.suffix).to(dev),
+                  torch.as_tensor(lay.is_prefix).to(dev))
+    tdt = q.dtype
+    gdt = torch.float32 if args.grad_dtype == "fp32" else tdt
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.hq, lay.T, device=dev, dtype=torch.float32)
+    grads = (torch.empty(q.shape, dtype=gdt, device=dev), torch.empty(k.shape, dtype=gdt, device=dev),
+             torch.empty(v.shape, dtype=gdt, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def build_map():
+        if lay.kind == "tokens":
+            return psa.build_tile_map_tokens(*labels, TILE, TILE)
+        return psa.build_tile_map_tree(lay.node_lengths, lay.sample_paths, lay.T, dev, TILE, TILE)
+
+    m0 = build_map()
+    ws = torch.empty(max(psa.bwd_workspace_size(m0, q, k), 1), dtype=torch.uint8, device=dev)
+    info = dict(m0.info)
+    del m0
+
+    names = ["map", "fwd"] + (["bwd_prepare", "bwd_dkdv", "bwd_dq"] if backward else [])
+    stage_of = {"bwd_prepare": psa.STAGE_PREPARE, "bwd_dkdv": psa.STAGE_DKDV,
+                "bwd_dq": psa.STAGE_DQ}
+
+    def step(events=None):
+        ev = (lambda i: events[i].record(stream)) if events else (lambda i: None)
+        ev(0)
+        m = build_map()
+        ev(1)
+        psa.fwd(m, q, k, v, out=o, lse=lse)
+        ev(2)
+        if backward:
+            for i, nm in enumerate(names[2:]):
+                psa.bwd(m, q, k, v, o, lse, do, workspace=ws, grad_dtype=gdt,
+                        stages=stage_of[nm], out=grads)
+                ev(3 + i)
+        return m
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # timed region: K full steps, wall clock between two device synchronisations
+    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                  for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    maps = []
+    for s in range(args.steps):
+        maps.append(step(all_events[s]))
+        if len(maps) > 2:
+            maps.pop(0)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    del maps
+
+    per = {nm: [] for nm in names}
+    for evs in all_events:
+        for i, nm in enumerate(names):
+            per[nm].append(evs[i].elapsed_time(evs[i + 1]))
+    avg = {nm: sum(x) / len(x) for nm, x in per.items()}
+
+    kept = kept_pairs(lay)
+    tiles = info["n_full"] + info["n_partial"]
+    d, hq = cfg.d, cfg.hq
+    f_fwd, f_bwd = 4 * d, 10 * d
+    tile_flops = tiles * TILE * TILE * hq * (f_fwd + (f_bwd if backward else 0))
+    kept_flops = kept * hq * (f_fwd + (f_bwd if backward else 0))
+    ms_step = wall * 1e3 / args.steps
+    value = tile_flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+
+    # dominant kernel: algorithmic FLOPs per launch (fwd 4d; dK/dV 8d = S, dP, dV, dK;
+    # dQ 2d: its S and dP are recomputations) per kept pair per q head
+    algo = {"fwd": 4 * d, "bwd_dkdv": 8 * d, "bwd_dq": 2 * d}
+    cand = {k_: avg[k_] for k_ in algo if k_ in avg}
+    dom = max(cand, key=cand.get)
+    achieved = kept * hq * algo[dom] / (avg[dom] * 1e-3) / 1e12
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_config{cfg.idx}.json")
+    if os.path.exists(tpath):
+        with open(tpath) as fh:
+            t = json.load(fh)
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0, sigma) Q/K/V/dO; layout as the workload states)",
+        "config": {"workload": describe(cfg, lay), "T": lay.T, "T_real": lay.T_real,
+                   "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": d,
+                   "passes": cfg.passes, "grad_dtype": args.grad_dtype,
+                   "tiles_128": {"full": info["n_full"], "partial": info["n_partial"]},
+                   "kept_pairs_per_head": kept},
+        "pct_bf16_peak" if cfg.dtype == "bf16" else "pct_fp32_peak": round(100 * value / peak, 2),
+        "kept_pair_tflops": round(kept_flops / (ms_step * 1e-3) / 1e12, 2),
+        "tokens_per_s": round(lay.T_real / (ms_step * 1e-3), 1),
+        "stage_ms": {nm: round(avg[nm], 4) for nm in names},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "algorithmic_flops_per_launch": kept * hq * algo[dom],
+                     "avg_launch_ms": round(avg[dom], 4)},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(cfg, lay)
+        work_tile_flops = tile_flops * cb["frac"]
+        out["cpu_baseline"] = {"value": round(work_tile_flops / cb["seconds"] / 1e12, 6),
+                               "unit": "TFLOP/s", "cores": cb["cores"], "kind": "oracle",
+                               "sample": f"{cb['sample']}: {cb['seconds']:.2f} s of float64 "
+                                         f"dense-mask oracle "
+                                         f"({'fwd' if not backward else 'fwd+bwd'}), "
+                                         f"scaled by its share {cb['frac']:.4f} of the "
+                                         f"workload's kept pairs"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

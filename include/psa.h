@@ -181,6 +181,28 @@ psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtyp
                    const void* dout, void* dq, void* dk, void* dv, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/*
+ * The backward in stages, for callers that time or overlap them (psa_bwd runs all
+ * three in order).  stages is a nonzero OR of:
+ *   PSA_STAGE_PREPARE  D = rowsum(dO * O) and LSE in log2 units, into the workspace
+ *                      (reads o, lse, dout);
+ *   PSA_STAGE_DKDV     dK, dV (reads q, k, v, dout and the prepared workspace);
+ *   PSA_STAGE_DQ       dQ (reads q, k, v, dout and the prepared workspace).
+ * DKDV and DQ depend only on PREPARE, not on each other.  Arguments and errors as
+ * psa_bwd (pointers a requested stage does not read may be NULL), plus PSA_ERR_VALUE
+ * for an empty or unknown stage set.
+ */
+#define PSA_STAGE_PREPARE 1
+#define PSA_STAGE_DKDV 2
+#define PSA_STAGE_DQ 4
+#define PSA_STAGE_ALL 7
+psa_status psa_bwd_stages(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype,
+                          int64_t T, int32_t hq, int32_t hkv, int32_t d, float scale,
+                          const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, int32_t stages,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -452,26 +452,41 @@ psa_status psa_bwd_workspace_size(const psa_tile_map* map, psa_dtype dtype, int6
   return PSA_OK;
 }
 
-psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype, int64_t T,
-                   int32_t hq, int32_t hkv, int32_t d, float scale, const void* q,
-                   const void* k, const void* v, const void* o, const float* lse,
-                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+psa_status psa_bwd_stages(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype,
+                          int64_t T, int32_t hq, int32_t hkv, int32_t d, float scale,
+                          const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, int32_t stages,
+                          void* stream) {
   psa_status st = check_attn_args(map, dtype, T, hq, hkv, d, scale, PSA_PASS_BWD);
   if (st != PSA_OK) return st;
   if (grad_dtype != PSA_FP32 && grad_dtype != dtype)
     return psa_set_error(PSA_ERR_DTYPE, "grad_dtype must be PSA_FP32 or the input dtype");
+  if (stages <= 0 || stages > PSA_STAGE_ALL)
+    return psa_set_error(PSA_ERR_VALUE, "stages must be a nonzero subset of PSA_STAGE_ALL");
   if (T == 0) return PSA_OK;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+  const bool pre = stages & PSA_STAGE_PREPARE, kv = stages & PSA_STAGE_DKDV,
+             dqs = stages & PSA_STAGE_DQ;
+  if ((pre && (!o || !lse || !dout)) || ((kv || dqs) && (!q || !k || !v || !dout)) ||
+      (kv && (!dk || !dv)) || (dqs && !dq))
     return psa_set_error(PSA_ERR_NULL, "tensor pointer is NULL");
   AttnShape s{T, hq, hkv, d, scale > 0.f ? scale : 1.0f / std::sqrt(float(d))};
   size_t need = bwd_workspace_bytes(s);
   if (!workspace || workspace_bytes < need)
     return psa_set_error(PSA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
-  hipError_t e = launch_bwd(*map, dtype, grad_dtype, s, q, k, v, o, lse, dout, dq, dk, dv, workspace,
-                            static_cast<hipStream_t>(stream));
+  hipError_t e = launch_bwd(*map, dtype, grad_dtype, s, q, k, v, o, lse, dout, dq, dk, dv,
+                            workspace, stages, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return psa_hip_error(e, "backward launch");
   return PSA_OK;
+}
+
+psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype, int64_t T,
+                   int32_t hq, int32_t hkv, int32_t d, float scale, const void* q,
+                   const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return psa_bwd_stages(map, dtype, grad_dtype, T, hq, hkv, d, scale, q, k, v, o, lse, dout,
+                        dq, dk, dv, workspace, workspace_bytes, PSA_STAGE_ALL, stream);
 }
 
 }  // extern "C"

@@ -390,7 +390,7 @@ template <typename T, typename G, int D>
 hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void* q,
                         const void* k, const void* v, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                        hipStream_t stream) {
+                        int stages, hipStream_t stream) {
   BwdParams p;
   p.q = q;
   p.k = k;
@@ -420,21 +420,25 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.c = s.scale * kLog2e;
   const int rep = s.hq / s.hkv;
 
-  const int64_t rows = s.T * s.hq;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(unsigned((rows + 15) / 16)), dim3(256), 0,
-                     stream, p);
-
-  p.n_work = map.nk * s.hkv;
-  p.chunk = 2;
-  int64_t per = 8 * int64_t(p.chunk);
-  int64_t grid = (p.n_work + per - 1) / per * per;
-  hipLaunchKernelGGL((dkdv_kernel<T, G, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
-
-  p.n_work = map.nq * s.hq;
-  p.chunk = rep * 2;
-  per = 8 * int64_t(p.chunk);
-  grid = (p.n_work + per - 1) / per * per;
-  hipLaunchKernelGGL((dq_kernel<T, G, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+  if (stages & PSA_STAGE_PREPARE) {
+    const int64_t rows = s.T * s.hq;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(unsigned((rows + 15) / 16)), dim3(256), 0,
+                       stream, p);
+  }
+  if (stages & PSA_STAGE_DKDV) {
+    p.n_work = map.nk * s.hkv;
+    p.chunk = 2;
+    const int64_t per = 8 * int64_t(p.chunk);
+    const int64_t grid = (p.n_work + per - 1) / per * per;
+    hipLaunchKernelGGL((dkdv_kernel<T, G, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+  }
+  if (stages & PSA_STAGE_DQ) {
+    p.n_work = map.nq * s.hq;
+    p.chunk = rep * 2;
+    const int64_t per = 8 * int64_t(p.chunk);
+    const int64_t grid = (p.n_work + per - 1) / per * per;
+    hipLaunchKernelGGL((dq_kernel<T, G, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -450,10 +454,11 @@ size_t bwd_workspace_bytes(const AttnShape& s) {
 hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype gdt, const AttnShape& s,
                       const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                      void* workspace, hipStream_t stream) {
+                      void* workspace, int stages, hipStream_t stream) {
   using psa::bf16_t;
-#define PSA_BWD(T, G, D) \
-  return psa::launch_bwd_t<T, G, D>(map, s, q, k, v, o, lse, dout, dq, dk, dv, workspace, stream)
+#define PSA_BWD(T, G, D)                                                                    \
+  return psa::launch_bwd_t<T, G, D>(map, s, q, k, v, o, lse, dout, dq, dk, dv, workspace, \
+                                    stages, stream)
   if (dt == PSA_BF16 && gdt == PSA_FP32) {
     switch (s.d) {
       case 64: PSA_BWD(bf16_t, float, 64);

@@ -31,7 +31,8 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_LAYOUT
 EXPORTS = ["psa_abi_version", "psa_status_string", "psa_last_error", "psa_tile_shape",
            "psa_build_tile_map_tokens", "psa_build_tile_map_tree", "psa_tile_map_info_get",
            "psa_tile_map_export", "psa_tile_map_destroy", "psa_fwd", "psa_bwd_workspace_size",
-           "psa_bwd"]
+           "psa_bwd", "psa_bwd_stages"]
+STAGE_PREPARE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 
 
 class PsaError(RuntimeError):
@@ -81,6 +82,8 @@ def load() -> ctypes.CDLL:
                                                       ctypes.POINTER(SZ)]),
             "psa_bwd": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, I64, I32, I32, I32, F, P, P,
                                        P, P, P, P, P, P, P, P, SZ, P]),
+            "psa_bwd_stages": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, I64, I32, I32, I32, F,
+                                              P, P, P, P, P, P, P, P, P, P, SZ, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -256,8 +259,12 @@ def bwd_workspace_size(m: TileMap, q: torch.Tensor, k: torch.Tensor) -> int:
 
 
 def bwd(m: TileMap, q, k, v, o, lse, do, scale: Optional[float] = None,
-        workspace: Optional[torch.Tensor] = None, grad_dtype: torch.dtype = torch.float32):
-    """dQ, dK, dV in ``grad_dtype`` (float32, the default, or q's dtype)."""
+        workspace: Optional[torch.Tensor] = None, grad_dtype: torch.dtype = torch.float32,
+        stages: int = STAGE_ALL, out=None):
+    """dQ, dK, dV in ``grad_dtype`` (float32, the default, or q's dtype).
+
+    ``stages`` selects backward stages (psa_bwd_stages); ``out`` = (dq, dk, dv) reuses
+    output buffers."""
     lib = load()
     _check_qkv(q, k, v)
     for t in (o, do):
@@ -271,14 +278,18 @@ def bwd(m: TileMap, q, k, v, o, lse, do, scale: Optional[float] = None,
     ws = workspace
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
-    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
-    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    if out is None:
+        dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+        dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+        dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    else:
+        dq, dk, dv = out
     with torch.cuda.device(q.device):
-        _check(lib.psa_bwd(m.handle, _dtype_code(q.dtype), _dtype_code(grad_dtype), T, hq, hkv, d,
-                           0.0 if scale is None else float(scale), _ptr(q), _ptr(k), _ptr(v),
-                           _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
-                           ws.numel() * ws.element_size(), _stream(q.device)))
+        _check(lib.psa_bwd_stages(m.handle, _dtype_code(q.dtype), _dtype_code(grad_dtype), T, hq,
+                                  hkv, d, 0.0 if scale is None else float(scale), _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), stages,
+                                  _stream(q.device)))
     return dq, dk, dv
 
 
