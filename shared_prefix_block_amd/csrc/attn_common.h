@@ -295,6 +295,97 @@ __device__ __forceinline__ void stage_rows_t(T* dst, const T* src, int64_t ld, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined staging: load() issues the global reads of a tile into
+// registers, store() writes them to LDS later, so the reads of tile i+1 are in
+// flight while tile i is being computed.
+// ---------------------------------------------------------------------------
+// Row-major: dst[r * S + c], 16 bytes per lane per chunk, consecutive lanes read
+// consecutive 16-byte pieces of a row.
+template <typename T, int R, int D, int S, int NT>
+struct RowStage {
+  static constexpr int E = 16 / int(sizeof(T));
+  static constexpr int CPR = D / E;
+  static constexpr int N = R * CPR / NT;
+  static_assert((R * CPR) % NT == 0, "tile must split evenly over the threads");
+  u32x4 r[N];
+  __device__ __forceinline__ void load(const T* src, int64_t ld, int nvalid) {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int c = it * NT + int(threadIdx.x);
+      const int row = c / CPR, cc = (c % CPR) * E;
+      r[it] = row < nvalid ? *reinterpret_cast<const u32x4*>(src + int64_t(row) * ld + cc)
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(T* dst) const {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int c = it * NT + int(threadIdx.x);
+      const int row = c / CPR, cc = (c % CPR) * E;
+      *reinterpret_cast<u32x4*>(dst + row * S + cc) = r[it];
+    }
+  }
+};
+
+// Transposed + row-permuted (see stage_rows_t), for operands whose element type has
+// no LDS transpose read (fp32).
+template <typename T, int R, int D, int S, int NT>
+struct TransStage {
+  static constexpr int CG = D / 4;
+  static constexpr int N = (R / 4) * CG / NT;
+  static_assert(((R / 4) * CG) % NT == 0, "tile must split evenly over the threads");
+  Vec4<T> rows[N][4];
+  __device__ __forceinline__ void load(const T* src, int64_t ld, int nvalid) {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int b = it * NT + int(threadIdx.x);
+      const int r0 = (b / CG) * 4, c0 = (b % CG) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        rows[it][k] =
+            (r0 + k < nvalid) ? vec4_load(src + int64_t(r0 + k) * ld + c0) : vec4_zero<T>();
+    }
+  }
+  __device__ __forceinline__ void store(T* dst) const {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int b = it * NT + int(threadIdx.x);
+      const int r0 = (b / CG) * 4, c0 = (b % CG) * 4;
+      Vec4<T> cols[4];
+      transpose4(rows[it], cols);
+      const int pos = perm_pos(r0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vec4_store(dst + (c0 + j) * S + pos, cols[j]);
+    }
+  }
+};
+
+// A-operand fragment of a product whose reduction index runs over the ROWS of a
+// row-major bf16 LDS tile (row stride S elements): lane l gets column
+// col0 + (l % 32) and the 8 rows row0 + {4h .. 4h+3, 8+4h .. 8+4h+3}, h = l / 32,
+// which is the row order of the accumulator-derived B operand.  Two
+// ds_read_b64_tr_b16: within each 16-lane group, lane s addresses row (s / 4) and
+// columns 4 (s % 4) .. +3 of a 4-row x 16-column block, and the hardware hands lane
+// i the 4 rows of column i.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Frag<bf16_t> frag_load_tr(const bf16_t* tile, int S, int row0,
+                                                     int col0) {
+  const int lane = threadIdx.x & 63;
+  const int s16 = lane & 15, g16 = lane >> 4, h = lane >> 5;
+  const int row = row0 + 4 * h + (s16 >> 2);
+  const int col = col0 + (g16 & 1) * 16 + (s16 & 3) * 4;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const lds_i16x4* p0 = (const lds_i16x4*)(tile + row * S + col);
+  const lds_i16x4* p1 = (const lds_i16x4*)(tile + (row + 8) * S + col);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p1));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  Frag<bf16_t> f;
+  f.v = u32x4{ua[0], ua[1], ub[0], ub[1]};
+  return f;
+}
+
 // blockIdx -> work item so that runs of `chunk` consecutive items land on one XCD
 // (work-groups are dealt to the 8 XCDs round-robin).  `grid` is a multiple of 8*chunk.
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t chunk) {

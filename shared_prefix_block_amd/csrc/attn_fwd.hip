@@ -3,20 +3,30 @@
 // One work-group = one q-tile of 128 rows (4 waves x 32 rows) for one q head.  It
 // walks the q-tile's CSR list of non-empty kv-tiles (ascending, so for a completion
 // row the prompt run comes first and its own completion run after it) in sub-steps
-// of BN keys: K (row-major) and V (transposed, rows permuted) are staged in LDS,
-// S^T = K Q^T runs on MFMA with Q held in registers, the per-element mask
-// kv <= q < end[kv] is applied only on partial tiles, the running max / sum are
-// updated (exp2 with log2(e) folded into the scale), and O^T += V^T P^T runs on MFMA
-// with P taken from registers.  The epilogue divides by the row sum and writes
-// O and LSE = ln 2 * (m + log2 l); rows that saw no key get O = 0, LSE = -inf.
+// of BN keys.  The K and V tiles of a sub-step live in one of two LDS buffers; the
+// global reads of the next sub-step are issued into registers before the current
+// one is computed and written to the other buffer after it, so each sub-step needs
+// one barrier and its loads overlap the math.  Per sub-step and wave:
+//   S^T = K Q^T on MFMA (Q stays in registers);
+//   the mask kv <= q < end[kv], as a select, on partial tiles only;
+//   the online softmax in the exp2 domain (log2(e) folded into the scale); the
+//   running max is raised only when a row's max grows by more than 2^8 (the
+//   result is the same: m cancels between O and l; it only bounds P by 2^8), so
+//   the O rescale is skipped on almost every sub-step;
+//   O^T += V^T P^T on MFMA with P from registers.  bf16 V stays row-major in LDS and
+//   its transposed fragments come from the LDS transpose read; fp32 V is staged
+//   transposed.
+// The epilogue writes O = O / l and LSE = ln 2 * (m + log2 l); rows that saw no key
+// get O = 0 and LSE = -inf.
 //
 // Sources: unsloth "prefix_grouper_kernel.py" (module docstring: masked blocks are
-// skipped and the P + G*R saving is realised; the comment on the flash block sizes:
-// the two disjoint key runs of a completion row go through one online softmax;
+// skipped, realising the P + G*R saving; the comment on the flash block sizes: a
+// completion row's two disjoint key runs go through one online softmax;
 // flex_shared_prefix_attention: layout, GQA, default scale).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.h"
 #include "psa_internal.h"
@@ -42,28 +52,33 @@ struct FwdParams {
   int32_t chunk;
 };
 
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays below 2^8
+
 template <typename T, int D>
 struct FwdCfg {
+  static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static constexpr int NW = 4;
   static constexpr int NT = NW * 64;
   static constexpr int BM = 32 * NW;
   static_assert(BM == kTileM, "q-tile must match the map");
-  static constexpr int BN = (D * int(sizeof(T)) > 256) ? 32 : 64;  // keys per sub-step
   static constexpr int EB = int(sizeof(T));
-  static constexpr int KS = D + 16 / EB;   // K tile row stride (elements)
-  static constexpr int VS = BN + 16 / EB;  // V^T tile row stride (elements)
+  static constexpr int BN = (!kBf16 && D * EB > 256) ? 32 : 64;  // keys per sub-step
+  static constexpr int NSUB = kTileN / BN;
+  static constexpr int KS = D + 16 / EB;                  // K row stride (elements)
+  static constexpr int VS = kBf16 ? D + 32 / EB : BN + 16 / EB;  // V (row-major) or V^T
   static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int LDS_BYTES = (K_ELEMS + V_ELEMS) * EB + BN * 4;
+  static constexpr int V_ELEMS = kBf16 ? BN * VS : D * VS;
+  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * EB + 2 * BN * 4;
+  static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D>::WAVES_PER_EU))) void fwd_kernel(FwdParams p) {
   using C = FwdCfg<T, D>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vt = Ks + C::K_ELEMS;
-  int32_t* Es = reinterpret_cast<int32_t*>(Vt + C::V_ELEMS);
+  T* const buf0 = reinterpret_cast<T*>(smem);
+  int32_t* const es0 = reinterpret_cast<int32_t*>(smem + 2 * C::BUF_ELEMS * C::EB);
 
   const int64_t w_id = xcd_remap(blockIdx.x, p.chunk);
   if (w_id >= p.n_work) return;
@@ -96,83 +111,129 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   float m = -INFINITY, l = 0.f;
   const float c = p.c;
   const int64_t ldk = int64_t(hkv) * D;
+  const int64_t koff = int64_t(hk) * D;
 
+  // Sub-steps of the CSR list: every kv-tile gives NSUB of them, except a tile that
+  // crosses T (always the last of the list) which stops at T.
   const int e0 = p.row_ptr[qt], e1 = p.row_ptr[qt + 1];
-  for (int e = e0; e < e1; ++e) {
-    const int j = p.col[e];
-    const bool partial = p.kind[e] == 1;
-    for (int sub = 0; sub < kTileN / C::BN; ++sub) {
-      const int64_t kv0 = int64_t(j) * kTileN + sub * C::BN;
-      if (kv0 >= ntok) break;
-      const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
-      const int kv0i = int(kv0);
-      __syncthreads();
-      const T* kp = K + kv0 * ldk + int64_t(hk) * D;
-      const T* vp = V + kv0 * ldk + int64_t(hk) * D;
-      stage_rows<T, C::BN, D, C::KS, C::NT>(Ks, kp, ldk, nvalid);
-      stage_rows_t<T, C::BN, D, C::VS, C::NT>(Vt, vp, ldk, nvalid);
-      if (partial && threadIdx.x < C::BN) {
-        const int r = threadIdx.x;
-        Es[r] = r < nvalid ? p.end[kv0 + r] : int32_t(kv0 + r);
-      }
-      __syncthreads();
+  int n_steps = (e1 - e0) * C::NSUB;
+  if (e1 > e0) {
+    const int64_t last0 = int64_t(p.col[e1 - 1]) * kTileN;
+    const int64_t left = ntok - last0;
+    if (left < kTileN) n_steps -= C::NSUB - int((left + C::BN - 1) / C::BN);
+  }
 
-      // S^T = K Q^T for BN keys x 32 queries (this wave)
-      float sv[C::BN / 32][16];
+  RowStage<T, C::BN, D, C::KS, C::NT> kst;
+  using VStage = typename std::conditional<C::kBf16, RowStage<T, C::BN, D, C::VS, C::NT>,
+                                           TransStage<T, C::BN, D, C::VS, C::NT>>::type;
+  VStage vst;
+  int32_t e_reg = 0;
+
+  auto issue = [&](int n) {  // global reads of sub-step n into registers
+    const int e = e0 + n / C::NSUB;
+    const int64_t kv0 = int64_t(p.col[e]) * kTileN + (n % C::NSUB) * C::BN;
+    const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
+    kst.load(K + kv0 * ldk + koff, ldk, nvalid);
+    vst.load(V + kv0 * ldk + koff, ldk, nvalid);
+    if (threadIdx.x < C::BN) {
+      const int r = threadIdx.x;
+      e_reg = r < nvalid ? p.end[kv0 + r] : int32_t(kv0 + r);
+    }
+  };
+  auto commit = [&](int b) {  // registers -> LDS buffer b
+    T* kb = buf0 + b * C::BUF_ELEMS;
+    kst.store(kb);
+    vst.store(kb + C::K_ELEMS);
+    if (threadIdx.x < C::BN) es0[b * C::BN + threadIdx.x] = e_reg;
+  };
+
+  if (n_steps > 0) {
+    issue(0);
+    commit(0);
+  }
+  __syncthreads();
+
+  for (int n = 0; n < n_steps; ++n) {
+    const int b = n & 1;
+    const int e = e0 + n / C::NSUB;
+    const bool partial = p.kind[e] == 1;
+    const int kv0i = p.col[e] * kTileN + (n % C::NSUB) * C::BN;
+    if (n + 1 < n_steps) issue(n + 1);
+
+    const T* Ks = buf0 + b * C::BUF_ELEMS;
+    const T* Vs = Ks + C::K_ELEMS;
+    const int32_t* Es = es0 + b * C::BN;
+
+    // S^T = K Q^T for BN keys x 32 queries (this wave)
+    float sv[C::BN / 32][16];
 #pragma unroll
-      for (int kb = 0; kb < C::BN / 32; ++kb) {
-        f32x16 acc_s = zero16();
-        const T* kr = Ks + (32 * kb + l32) * C::KS + 8 * half;
+    for (int kb = 0; kb < C::BN / 32; ++kb) {
+      f32x16 acc_s = zero16();
+      const T* kr = Ks + (32 * kb + l32) * C::KS + 8 * half;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) mma(acc_s, frag_load(kr + 16 * s), qf[s]);
+      for (int s = 0; s < D / 16; ++s) mma(acc_s, frag_load(kr + 16 * s), qf[s]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sv[kb][i] = acc_s[i];
-      }
-      if (partial) {  // uniform branch; the mask itself is a select, no divergence
-#pragma unroll
-        for (int kb = 0; kb < C::BN / 32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kvl = 32 * kb + acc_row(i, half);
-            sv[kb][i] = visible(kv0i + kvl, qrow_i, Es[kvl]) ? sv[kb][i] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+      for (int i = 0; i < 16; ++i) sv[kb][i] = acc_s[i];
+    }
+    if (partial) {  // uniform branch; the mask itself is a select
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        for (int g = 0; g < 4; ++g) {
+          const int kvl = 32 * kb + g * 8 + half * 4;
+          const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
+          const int evs[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            sv[kb][4 * g + u] =
+                visible(kv0i + kvl + u, qrow_i, evs[u]) ? sv[kb][4 * g + u] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    // raise the running max only when it grows by more than the slack
+    const bool grow = mx > m + kRescaleSlack || (m == -INFINITY && mx > -INFINITY);
+    if (__ballot(grow)) {  // wave-uniform branch
+      const float m_new = grow ? mx : m;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;  // 0 if m = -inf
       m = m_new;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-      float rs = 0.f;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < C::BN / 32; ++kb)
+    for (int kb = 0; kb < C::BN / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sv[kb][i], c, -m_use));
-          sv[kb][i] = pv;
-          rs += pv;
-        }
-      l += rs;
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sv[kb][i], c, -m_use));
+        sv[kb][i] = pv;
+        rs += pv;
+      }
+    l += rs;
 
-      // O^T += V^T P^T, 16 keys per step
+    // O^T += V^T P^T, 16 keys per step
 #pragma unroll
-      for (int t = 0; t < C::BN / 16; ++t) {
-        float pv[8];
+    for (int t = 0; t < C::BN / 16; ++t) {
+      const Frag<T> pf = frag_from<T>(&sv[t >> 1][(t & 1) * 8]);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pv[jj] = sv[t >> 1][(t & 1) * 8 + jj];
-        const Frag<T> pf = frag_from<T>(pv);
-        const T* vr = Vt + l32 * C::VS + 16 * t + 8 * half;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) mma(acc[db], frag_load(vr + 32 * db * C::VS), pf);
+      for (int db = 0; db < D / 32; ++db) {
+        Frag<T> va;
+        if constexpr (C::kBf16)
+          va = frag_load_tr(Vs, C::VS, 16 * t, 32 * db);
+        else
+          va = frag_load(Vs + (32 * db + l32) * C::VS + 16 * t + 8 * half);
+        mma(acc[db], va, pf);
       }
     }
+
+    if (n + 1 < n_steps) commit(b ^ 1);
+    __syncthreads();
   }
 
   const float lt = l + __shfl_xor(l, 32);
