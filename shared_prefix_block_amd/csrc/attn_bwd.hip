@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.h"
 #include "psa_internal.h"
@@ -89,33 +90,36 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dkdv
+// dkdv: K and V of this work-group's 32 keys per wave stay in registers; the q
+// sub-steps (CSC entries x q heads of the group x BMS-row slices) are staged in a
+// double-buffered LDS pipeline.  bf16 needs only row-major Q and dO tiles: the
+// transposed operands of dV^T += dO^T P and dK^T += Q^T dS come from the LDS
+// transpose read.  fp32 stages transposed copies instead.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DkdvCfg {
+  static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static constexpr int NW = 4;
   static constexpr int NT = NW * 64;
   static constexpr int BK = 32 * NW;  // keys per work-group
   static_assert(BK == kTileN, "kv-tile must match the map");
   static constexpr int EB = int(sizeof(T));
   static constexpr int BMS = (D * EB > 256) ? 32 : 64;  // q rows per sub-step
-  static constexpr int NS = D + 16 / EB;                // row-major tile stride
-  static constexpr int TS = BMS + 16 / EB;              // transposed tile stride
+  static constexpr int NSUB = kTileM / BMS;
+  static constexpr int NS = D + 16 / EB;  // row-major tile stride (elements)
+  static constexpr int TS = BMS + 16 / EB;  // transposed tile stride (fp32 only)
   static constexpr int N_ELEMS = BMS * NS;
-  static constexpr int T_ELEMS = D * TS;
-  static constexpr int LDS_BYTES = 2 * (N_ELEMS + T_ELEMS) * EB + 2 * BMS * 4;
+  static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
+  static constexpr int BUF_ELEMS = 2 * (N_ELEMS + T_ELEMS);
+  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * EB + 2 * 2 * BMS * 4;
 };
 
 template <typename T, typename G, int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   using C = DkdvCfg<T, D>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-  T* Qs = reinterpret_cast<T*>(smem);
-  T* Qt = Qs + C::N_ELEMS;
-  T* Gs = Qt + C::T_ELEMS;  // dO row-major
-  T* Gt = Gs + C::N_ELEMS;  // dO transposed
-  float* Ls = reinterpret_cast<float*>(Gt + C::T_ELEMS);
-  float* Dsh = Ls + C::BMS;
+  T* const buf0 = reinterpret_cast<T*>(smem);
+  float* const ld0 = reinterpret_cast<float*>(smem + 2 * C::BUF_ELEMS * C::EB);  // [2][2][BMS]
 
   const int64_t w_id = xcd_remap(blockIdx.x, p.chunk);
   if (w_id >= p.n_work) return;
@@ -154,78 +158,142 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const float c = p.c;
   const int64_t ldq = int64_t(hq) * D;
 
+  // Steps: (CSC entry, q head of the group, BMS-row slice).  Only the last entry's
+  // q-tile can cross T; it keeps the slices below T.
   const int e0 = p.col_ptr[kt], e1 = p.col_ptr[kt + 1];
-  for (int e = e0; e < e1; ++e) {
-    const int i = p.row[e];
+  int ns_last = C::NSUB;
+  if (e1 > e0) {
+    const int64_t left = ntok - int64_t(p.row[e1 - 1]) * kTileM;
+    if (left < kTileM) ns_last = int((left + C::BMS - 1) / C::BMS);
+  }
+  const int full_steps = (e1 - e0 - 1) * rep * C::NSUB;
+  const int n_steps = e1 > e0 ? full_steps + rep * ns_last : 0;
+  auto decode = [&](int n, int& e, int& h, int& sub) {
+    if (n < full_steps) {
+      e = e0 + n / (rep * C::NSUB);
+      const int rem = n % (rep * C::NSUB);
+      h = hk * rep + rem / C::NSUB;
+      sub = rem % C::NSUB;
+    } else {
+      const int rem = n - full_steps;
+      e = e1 - 1;
+      h = hk * rep + rem / ns_last;
+      sub = rem % ns_last;
+    }
+  };
+
+  RowStage<T, C::BMS, D, C::NS, C::NT> qst, gst;
+  using TStage = TransStage<T, C::BMS, D, C::TS, C::NT>;
+  typename std::conditional<C::kBf16, int, TStage>::type qtst, gtst;
+  float l2_reg = INFINITY, dl_reg = 0.f;
+
+  auto issue = [&](int n) {
+    int e, h, sub;
+    decode(n, e, h, sub);
+    const int64_t q0 = int64_t(p.row[e]) * kTileM + sub * C::BMS;
+    const int nvalid = ntok - q0 < C::BMS ? int(ntok - q0) : C::BMS;
+    const T* qp = Qg + q0 * ldq + int64_t(h) * D;
+    const T* gp = Gg + q0 * ldq + int64_t(h) * D;
+    qst.load(qp, ldq, nvalid);
+    gst.load(gp, ldq, nvalid);
+    if constexpr (!C::kBf16) {
+      qtst.load(qp, ldq, nvalid);
+      gtst.load(gp, ldq, nvalid);
+    }
+    if (threadIdx.x < C::BMS) {
+      const int rr = threadIdx.x;
+      const bool ok = rr < nvalid;
+      l2_reg = ok ? p.L2[int64_t(h) * ntok + q0 + rr] : INFINITY;
+      dl_reg = ok ? p.Dl[int64_t(h) * ntok + q0 + rr] : 0.f;
+    }
+  };
+  auto commit = [&](int b) {
+    T* base = buf0 + b * C::BUF_ELEMS;
+    qst.store(base);
+    gst.store(base + C::N_ELEMS);
+    if constexpr (!C::kBf16) {
+      qtst.store(base + 2 * C::N_ELEMS);
+      gtst.store(base + 2 * C::N_ELEMS + C::T_ELEMS);
+    }
+    if (threadIdx.x < C::BMS) {
+      ld0[(b * 2 + 0) * C::BMS + threadIdx.x] = l2_reg;
+      ld0[(b * 2 + 1) * C::BMS + threadIdx.x] = dl_reg;
+    }
+  };
+
+  if (n_steps > 0) {
+    issue(0);
+    commit(0);
+  }
+  __syncthreads();
+
+  for (int n = 0; n < n_steps; ++n) {
+    const int b = n & 1;
+    int e, h, sub;
+    decode(n, e, h, sub);
     const bool partial = p.kind_csc[e] == 1;
-    for (int r = 0; r < rep; ++r) {
-      const int h = hk * rep + r;
-      for (int sub = 0; sub < kTileM / C::BMS; ++sub) {
-        const int64_t q0 = int64_t(i) * kTileM + sub * C::BMS;
-        if (q0 >= ntok) break;
-        const int nvalid = ntok - q0 < C::BMS ? int(ntok - q0) : C::BMS;
-        const int q0i = int(q0);
-        __syncthreads();
-        const T* qp = Qg + q0 * ldq + int64_t(h) * D;
-        const T* gp = Gg + q0 * ldq + int64_t(h) * D;
-        stage_rows<T, C::BMS, D, C::NS, C::NT>(Qs, qp, ldq, nvalid);
-        stage_rows_t<T, C::BMS, D, C::TS, C::NT>(Qt, qp, ldq, nvalid);
-        stage_rows<T, C::BMS, D, C::NS, C::NT>(Gs, gp, ldq, nvalid);
-        stage_rows_t<T, C::BMS, D, C::TS, C::NT>(Gt, gp, ldq, nvalid);
-        if (threadIdx.x < C::BMS) {
-          const int rr = threadIdx.x;
-          const bool ok = rr < nvalid;
-          Ls[rr] = ok ? p.L2[int64_t(h) * ntok + q0 + rr] : INFINITY;
-          Dsh[rr] = ok ? p.Dl[int64_t(h) * ntok + q0 + rr] : 0.f;
-        }
-        __syncthreads();
+    const int q0i = p.row[e] * kTileM + sub * C::BMS;
+    if (n + 1 < n_steps) issue(n + 1);
+
+    const T* Qs = buf0 + b * C::BUF_ELEMS;
+    const T* Gs = Qs + C::N_ELEMS;
+    const T* Qt = Qs + 2 * C::N_ELEMS;
+    const T* Gt = Qt + C::T_ELEMS;
+    const float* Ls = ld0 + (b * 2 + 0) * C::BMS;
+    const float* Dsh = ld0 + (b * 2 + 1) * C::BMS;
 
 #pragma unroll
-        for (int qb = 0; qb < C::BMS / 32; ++qb) {
-          f32x16 sacc = zero16(), pacc = zero16();
-          const T* qr = Qs + (32 * qb + l32) * C::NS + 8 * half;
-          const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
+    for (int qb = 0; qb < C::BMS / 32; ++qb) {
+      f32x16 sacc = zero16(), pacc = zero16();
+      const T* qr = Qs + (32 * qb + l32) * C::NS + 8 * half;
+      const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
 #pragma unroll
-          for (int s = 0; s < D / 16; ++s) {
-            mma(sacc, frag_load(qr + 16 * s), kf[s]);
-            mma(pacc, frag_load(gr + 16 * s), vf[s]);
-          }
-          float pv[16], ds[16];
+      for (int s = 0; s < D / 16; ++s) {
+        mma(sacc, frag_load(qr + 16 * s), kf[s]);
+        mma(pacc, frag_load(gr + 16 * s), vf[s]);
+      }
+      float pv[16], ds[16];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int ql = 32 * qb + g * 8 + half * 4;
-            const f32x4 l2 = *reinterpret_cast<const f32x4*>(Ls + ql);
-            const f32x4 dl = *reinterpret_cast<const f32x4*>(Dsh + ql);
+      for (int g = 0; g < 4; ++g) {
+        const int ql = 32 * qb + g * 8 + half * 4;
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(Ls + ql);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(Dsh + ql);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int ii = 4 * g + u;
-              float pr = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2[u]));
-              if (partial) pr = visible(kvrow_i, q0i + ql + u, end_kv) ? pr : 0.f;
-              pv[ii] = pr;
-              ds[ii] = pr * (pacc[ii] - dl[u]);
-            }
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int ii = 4 * g + u;
+          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2[u]));
+          if (partial) pr = visible(kvrow_i, q0i + ql + u, end_kv) ? pr : 0.f;
+          pv[ii] = pr;
+          ds[ii] = pr * (pacc[ii] - dl[u]);
+        }
+      }
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            Frag<T> pf, pl, sf, sl;
-            frag_split<T>(pv + 8 * t, pf, pl);
-            frag_split<T>(ds + 8 * t, sf, sl);
+      for (int t = 0; t < 2; ++t) {
+        Frag<T> pf, pl, sf, sl;
+        frag_split<T>(pv + 8 * t, pf, pl);
+        frag_split<T>(ds + 8 * t, sf, sl);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          Frag<T> ga, qa;
+          if constexpr (C::kBf16) {
+            ga = frag_load_tr(Gs, C::NS, 32 * qb + 16 * t, 32 * db);
+            qa = frag_load_tr(Qs, C::NS, 32 * qb + 16 * t, 32 * db);
+          } else {
             const int col0 = 32 * qb + 16 * t + 8 * half;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              const Frag<T> ga = frag_load(Gt + (32 * db + l32) * C::TS + col0);
-              const Frag<T> qa = frag_load(Qt + (32 * db + l32) * C::TS + col0);
-              mma(adv[db], ga, pf);
-              mma(adk[db], qa, sf);
-              if constexpr (NeedsSplit<T>::value) {
-                mma(adv[db], ga, pl);
-                mma(adk[db], qa, sl);
-              }
-            }
+            ga = frag_load(Gt + (32 * db + l32) * C::TS + col0);
+            qa = frag_load(Qt + (32 * db + l32) * C::TS + col0);
+          }
+          mma(adv[db], ga, pf);
+          mma(adk[db], qa, sf);
+          if constexpr (NeedsSplit<T>::value) {
+            mma(adv[db], ga, pl);
+            mma(adk[db], qa, sl);
           }
         }
       }
     }
+    if (n + 1 < n_steps) commit(b ^ 1);
+    __syncthreads();
   }
 
   if (kvvalid) {
@@ -247,31 +315,37 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dq
+// dq: the forward's walk over the CSR list with K and V staged row-major in a
+// double-buffered LDS pipeline; Q and dO stay in registers.  bf16 takes K^T for
+// dQ^T += K^T dS^T from the LDS transpose read of the K tile; fp32 stages K^T.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DqCfg {
+  static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static constexpr int NW = 4;
   static constexpr int NT = NW * 64;
   static constexpr int BM = 32 * NW;
   static_assert(BM == kTileM, "q-tile must match the map");
   static constexpr int EB = int(sizeof(T));
-  static constexpr int BN = (D * EB > 256) ? 32 : 64;  // keys per sub-step
+  // keys per sub-step: 32 where 64 would not fit two waves per SIMD in registers
+  static constexpr int BN = (D * EB > (kBf16 ? 128 : 256)) ? 32 : 64;
+  static constexpr int NSUB = kTileN / BN;
   static constexpr int NS = D + 16 / EB;
   static constexpr int TS = BN + 16 / EB;
   static constexpr int N_ELEMS = BN * NS;
-  static constexpr int T_ELEMS = D * TS;
-  static constexpr int LDS_BYTES = (2 * N_ELEMS + T_ELEMS) * EB + BN * 4;
+  static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
+  static constexpr int BUF_ELEMS = 2 * N_ELEMS + T_ELEMS;
+  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * EB + 2 * BN * 4;
+  static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
 };
 
 template <typename T, typename G, int D>
-__global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, D>::WAVES_PER_EU)))
+void dq_kernel(BwdParams p) {
   using C = DqCfg<T, D>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vs = Ks + C::N_ELEMS;
-  T* Kt = Vs + C::N_ELEMS;
-  int32_t* Es = reinterpret_cast<int32_t*>(Kt + C::T_ELEMS);
+  T* const buf0 = reinterpret_cast<T*>(smem);
+  int32_t* const es0 = reinterpret_cast<int32_t*>(smem + 2 * C::BUF_ELEMS * C::EB);
 
   const int64_t w_id = xcd_remap(blockIdx.x, p.chunk);
   if (w_id >= p.n_work) return;
@@ -308,65 +382,106 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdParams p) {
   for (int db = 0; db < D / 32; ++db) adq[db] = zero16();
   const float c = p.c;
   const int64_t ldk = int64_t(hkv) * D;
+  const int64_t koff = int64_t(hk) * D;
 
   const int e0 = p.row_ptr[qt], e1 = p.row_ptr[qt + 1];
-  for (int e = e0; e < e1; ++e) {
-    const int j = p.col[e];
-    const bool partial = p.kind[e] == 1;
-    for (int sub = 0; sub < kTileN / C::BN; ++sub) {
-      const int64_t kv0 = int64_t(j) * kTileN + sub * C::BN;
-      if (kv0 >= ntok) break;
-      const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
-      const int kv0i = int(kv0);
-      __syncthreads();
-      const T* kp = Kg + kv0 * ldk + int64_t(hk) * D;
-      const T* vp = Vg + kv0 * ldk + int64_t(hk) * D;
-      stage_rows<T, C::BN, D, C::NS, C::NT>(Ks, kp, ldk, nvalid);
-      stage_rows<T, C::BN, D, C::NS, C::NT>(Vs, vp, ldk, nvalid);
-      stage_rows_t<T, C::BN, D, C::TS, C::NT>(Kt, kp, ldk, nvalid);
-      if (partial && threadIdx.x < C::BN) {
-        const int r = threadIdx.x;
-        Es[r] = r < nvalid ? p.end[kv0 + r] : int32_t(kv0 + r);
-      }
-      __syncthreads();
+  int n_steps = (e1 - e0) * C::NSUB;
+  if (e1 > e0) {
+    const int64_t left = ntok - int64_t(p.col[e1 - 1]) * kTileN;
+    if (left < kTileN) n_steps -= C::NSUB - int((left + C::BN - 1) / C::BN);
+  }
 
-      f32x16 ds[C::BN / 32];
+  RowStage<T, C::BN, D, C::NS, C::NT> kst, vst;
+  using TStage = TransStage<T, C::BN, D, C::TS, C::NT>;
+  typename std::conditional<C::kBf16, int, TStage>::type ktst;
+  int32_t e_reg = 0;
+
+  auto issue = [&](int n) {
+    const int e = e0 + n / C::NSUB;
+    const int64_t kv0 = int64_t(p.col[e]) * kTileN + (n % C::NSUB) * C::BN;
+    const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
+    kst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
+    vst.load(Vg + kv0 * ldk + koff, ldk, nvalid);
+    if constexpr (!C::kBf16) ktst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
+    if (threadIdx.x < C::BN) {
+      const int r = threadIdx.x;
+      e_reg = r < nvalid ? p.end[kv0 + r] : int32_t(kv0 + r);
+    }
+  };
+  auto commit = [&](int b) {
+    T* base = buf0 + b * C::BUF_ELEMS;
+    kst.store(base);
+    vst.store(base + C::N_ELEMS);
+    if constexpr (!C::kBf16) ktst.store(base + 2 * C::N_ELEMS);
+    if (threadIdx.x < C::BN) es0[b * C::BN + threadIdx.x] = e_reg;
+  };
+
+  if (n_steps > 0) {
+    issue(0);
+    commit(0);
+  }
+  __syncthreads();
+
+  for (int n = 0; n < n_steps; ++n) {
+    const int b = n & 1;
+    const int e = e0 + n / C::NSUB;
+    const bool partial = p.kind[e] == 1;
+    const int kv0i = p.col[e] * kTileN + (n % C::NSUB) * C::BN;
+    if (n + 1 < n_steps) issue(n + 1);
+
+    const T* Ks = buf0 + b * C::BUF_ELEMS;
+    const T* Vs = Ks + C::N_ELEMS;
+    const T* Kt = Ks + 2 * C::N_ELEMS;
+    const int32_t* Es = es0 + b * C::BN;
+
+    float ds[C::BN / 32][16];
 #pragma unroll
-      for (int kb = 0; kb < C::BN / 32; ++kb) {
-        f32x16 sacc = zero16(), pacc = zero16();
-        const T* kr = Ks + (32 * kb + l32) * C::NS + 8 * half;
-        const T* vr = Vs + (32 * kb + l32) * C::NS + 8 * half;
+    for (int kb = 0; kb < C::BN / 32; ++kb) {
+      f32x16 sacc = zero16(), pacc = zero16();
+      const T* kr = Ks + (32 * kb + l32) * C::NS + 8 * half;
+      const T* vr = Vs + (32 * kb + l32) * C::NS + 8 * half;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          mma(sacc, frag_load(kr + 16 * s), qf[s]);
-          mma(pacc, frag_load(vr + 16 * s), gf[s]);
+      for (int s = 0; s < D / 16; ++s) {
+        mma(sacc, frag_load(kr + 16 * s), qf[s]);
+        mma(pacc, frag_load(vr + 16 * s), gf[s]);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kvl = 32 * kb + g * 8 + half * 4;
+        int evs[4] = {0, 0, 0, 0};
+        if (partial) {
+          const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
+          evs[0] = ev.x;
+          evs[1] = ev.y;
+          evs[2] = ev.z;
+          evs[3] = ev.w;
         }
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
+        for (int u = 0; u < 4; ++u) {
+          const int ii = 4 * g + u;
           float pr = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2));
-          if (partial) {
-            const int kvl = 32 * kb + acc_row(ii, half);
-            pr = visible(kv0i + kvl, qrow_i, Es[kvl]) ? pr : 0.f;
-          }
+          if (partial) pr = visible(kv0i + kvl + u, qrow_i, evs[u]) ? pr : 0.f;
           ds[kb][ii] = pr * (pacc[ii] - dl);
         }
       }
+    }
 #pragma unroll
-      for (int t = 0; t < C::BN / 16; ++t) {
-        float sv[8];
+    for (int t = 0; t < C::BN / 16; ++t) {
+      Frag<T> sf, sl;
+      frag_split<T>(&ds[t >> 1][(t & 1) * 8], sf, sl);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) sv[jj] = ds[t >> 1][(t & 1) * 8 + jj];
-        Frag<T> sf, sl;
-        frag_split<T>(sv, sf, sl);
-        const T* kr = Kt + l32 * C::TS + 16 * t + 8 * half;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const Frag<T> ka = frag_load(kr + 32 * db * C::TS);
-          mma(adq[db], ka, sf);
-          if constexpr (NeedsSplit<T>::value) mma(adq[db], ka, sl);
-        }
+      for (int db = 0; db < D / 32; ++db) {
+        Frag<T> ka;
+        if constexpr (C::kBf16)
+          ka = frag_load_tr(Ks, C::NS, 16 * t, 32 * db);
+        else
+          ka = frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half);
+        mma(adq[db], ka, sf);
+        if constexpr (NeedsSplit<T>::value) mma(adq[db], ka, sl);
       }
     }
+    if (n + 1 < n_steps) commit(b ^ 1);
+    __syncthreads();
   }
 
   if (qvalid) {
