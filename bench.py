@@ -113,6 +113,10 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--calib-mb", type=int, default=0,
+                    help="before warm-up, run one elementwise negation over this many MiB of "
+                         "fp32 (reads and writes that many bytes): the reference kernel the "
+                         "HBM byte counters are scaled by")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -174,6 +178,13 @@ def main():
                         stages=stage_of[nm], out=grads)
                 ev(3 + i)
         return m
+
+    if args.calib_mb:
+        src = torch.ones(args.calib_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize(dev)
+        del src, dst
 
     for _ in range(args.warmup):
         step()

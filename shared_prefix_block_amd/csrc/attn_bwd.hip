@@ -106,7 +106,9 @@ struct DkdvCfg {
   static constexpr int EB = int(sizeof(T));
   static constexpr int BMS = (D * EB > 256) ? 32 : 64;  // q rows per sub-step
   static constexpr int NSUB = kTileM / BMS;
-  static constexpr int NS = D + 16 / EB;  // row-major tile stride (elements)
+  // row-major tile stride: bf16 tiles are read both as rows (16 B per lane) and
+  // through the transpose read; a 32-byte pad keeps both free of bank conflicts
+  static constexpr int NS = D + (kBf16 ? 32 : 16) / EB;
   static constexpr int TS = BMS + 16 / EB;  // transposed tile stride (fp32 only)
   static constexpr int N_ELEMS = BMS * NS;
   static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const int64_t kvrow = int64_t(kt) * C::BK + 32 * wave + l32;
   const bool kvvalid = kvrow < ntok;
   const int kvrow_i = int(kvrow);
-  const int32_t end_kv = kvvalid ? p.end[kvrow] : kvrow_i;
+  const int32_t reach = kvvalid ? p.end[kvrow] - kvrow_i : 0;  // rows kv .. kv+reach-1
 
   const T* Kg = static_cast<const T*>(p.k);
   const T* Vg = static_cast<const T*>(p.v);
@@ -242,52 +244,59 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const float* Ls = ld0 + (b * 2 + 0) * C::BMS;
     const float* Dsh = ld0 + (b * 2 + 1) * C::BMS;
 
+    {
+      const int qd0 = q0i - kvrow_i;  // q - kv at the sub-step's first row
 #pragma unroll
-    for (int qb = 0; qb < C::BMS / 32; ++qb) {
-      f32x16 sacc = zero16(), pacc = zero16();
-      const T* qr = Qs + (32 * qb + l32) * C::NS + 8 * half;
-      const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
+      for (int qb = 0; qb < C::BMS / 32; ++qb) {
+        f32x16 sacc = zero16(), pacc = zero16();
+        const T* qr = Qs + (32 * qb + l32) * C::NS + 8 * half;
+        const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        mma(sacc, frag_load(qr + 16 * s), kf[s]);
-        mma(pacc, frag_load(gr + 16 * s), vf[s]);
-      }
-      float pv[16], ds[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = 32 * qb + g * 8 + half * 4;
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(Ls + ql);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(Dsh + ql);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ii = 4 * g + u;
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2[u]));
-          if (partial) pr = visible(kvrow_i, q0i + ql + u, end_kv) ? pr : 0.f;
-          pv[ii] = pr;
-          ds[ii] = pr * (pacc[ii] - dl[u]);
+        for (int s = 0; s < D / 16; ++s) {
+          mma(sacc, frag_load(qr + 16 * s), kf[s]);
+          mma(pacc, frag_load(gr + 16 * s), vf[s]);
         }
-      }
+        float pv[16], ds[16];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        Frag<T> pf, pl, sf, sl;
-        frag_split<T>(pv + 8 * t, pf, pl);
-        frag_split<T>(ds + 8 * t, sf, sl);
+        for (int g = 0; g < 4; ++g) {
+          const int ql = 32 * qb + g * 8 + half * 4;
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(Ls + ql);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          Frag<T> ga, qa;
-          if constexpr (C::kBf16) {
-            ga = frag_load_tr(Gs, C::NS, 32 * qb + 16 * t, 32 * db);
-            qa = frag_load_tr(Qs, C::NS, 32 * qb + 16 * t, 32 * db);
-          } else {
-            const int col0 = 32 * qb + 16 * t + 8 * half;
-            ga = frag_load(Gt + (32 * db + l32) * C::TS + col0);
-            qa = frag_load(Qt + (32 * db + l32) * C::TS + col0);
-          }
-          mma(adv[db], ga, pf);
-          mma(adk[db], qa, sf);
-          if constexpr (NeedsSplit<T>::value) {
-            mma(adv[db], ga, pl);
-            mma(adk[db], qa, sl);
+          for (int u = 0; u < 4; ++u) pv[4 * g + u] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + u], c, -l2[u]));
+        }
+        if (partial) {  // uniform branch; full tiles skip the mask
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii)
+            pv[ii] = visible_u(qd0 + 32 * qb + acc_row(ii, half), reach) ? pv[ii] : 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 dl = *reinterpret_cast<const f32x4*>(Dsh + 32 * qb + g * 8 + half * 4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ds[4 * g + u] = pv[4 * g + u] * (pacc[4 * g + u] - dl[u]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          Frag<T> pf, pl, sf, sl;
+          frag_split<T>(pv + 8 * t, pf, pl);
+          frag_split<T>(ds + 8 * t, sf, sl);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            Frag<T> ga, qa;
+            if constexpr (C::kBf16) {
+              ga = frag_load_tr(Gs, C::NS, 32 * qb + 16 * t, 32 * db);
+              qa = frag_load_tr(Qs, C::NS, 32 * qb + 16 * t, 32 * db);
+            } else {
+              const int col0 = 32 * qb + 16 * t + 8 * half;
+              ga = frag_load(Gt + (32 * db + l32) * C::TS + col0);
+              qa = frag_load(Qt + (32 * db + l32) * C::TS + col0);
+            }
+            mma(adv[db], ga, pf);
+            mma(adk[db], qa, sf);
+            if constexpr (NeedsSplit<T>::value) {
+              mma(adv[db], ga, pl);
+              mma(adk[db], qa, sl);
+            }
           }
         }
       }
@@ -330,7 +339,7 @@ struct DqCfg {
   // keys per sub-step: 32 where 64 would not fit two waves per SIMD in registers
   static constexpr int BN = (D * EB > (kBf16 ? 128 : 256)) ? 32 : 64;
   static constexpr int NSUB = kTileN / BN;
-  static constexpr int NS = D + 16 / EB;
+  static constexpr int NS = D + (kBf16 ? 32 : 16) / EB;  // see DkdvCfg::NS
   static constexpr int TS = BN + 16 / EB;
   static constexpr int N_ELEMS = BN * NS;
   static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
@@ -405,7 +414,7 @@ void dq_kernel(BwdParams p) {
     if constexpr (!C::kBf16) ktst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
     if (threadIdx.x < C::BN) {
       const int r = threadIdx.x;
-      e_reg = r < nvalid ? p.end[kv0 + r] : int32_t(kv0 + r);
+      e_reg = r < nvalid ? p.end[kv0 + r] - int32_t(kv0 + r) : 0;  // reach
     }
   };
   auto commit = [&](int b) {
@@ -434,50 +443,50 @@ void dq_kernel(BwdParams p) {
     const T* Kt = Ks + 2 * C::N_ELEMS;
     const int32_t* Es = es0 + b * C::BN;
 
-    float ds[C::BN / 32][16];
+    {
+      const int qd = qrow_i - kv0i;
+      float ds[C::BN / 32][16];
 #pragma unroll
-    for (int kb = 0; kb < C::BN / 32; ++kb) {
-      f32x16 sacc = zero16(), pacc = zero16();
-      const T* kr = Ks + (32 * kb + l32) * C::NS + 8 * half;
-      const T* vr = Vs + (32 * kb + l32) * C::NS + 8 * half;
+      for (int kb = 0; kb < C::BN / 32; ++kb) {
+        f32x16 sacc = zero16(), pacc = zero16();
+        const T* kr = Ks + (32 * kb + l32) * C::NS + 8 * half;
+        const T* vr = Vs + (32 * kb + l32) * C::NS + 8 * half;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        mma(sacc, frag_load(kr + 16 * s), qf[s]);
-        mma(pacc, frag_load(vr + 16 * s), gf[s]);
-      }
+        for (int s = 0; s < D / 16; ++s) {
+          mma(sacc, frag_load(kr + 16 * s), qf[s]);
+          mma(pacc, frag_load(vr + 16 * s), gf[s]);
+        }
+        float pv[16];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int kvl = 32 * kb + g * 8 + half * 4;
-        int evs[4] = {0, 0, 0, 0};
-        if (partial) {
-          const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
-          evs[0] = ev.x;
-          evs[1] = ev.y;
-          evs[2] = ev.z;
-          evs[3] = ev.w;
+        for (int ii = 0; ii < 16; ++ii) pv[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2));
+        if (partial) {  // uniform branch; full tiles skip the mask
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int kvl = 32 * kb + g * 8 + half * 4;
+            const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
+            const int rv[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              pv[4 * g + u] = visible_u(qd - kvl - u, rv[u]) ? pv[4 * g + u] : 0.f;
+          }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ii = 4 * g + u;
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2));
-          if (partial) pr = visible(kv0i + kvl + u, qrow_i, evs[u]) ? pr : 0.f;
-          ds[kb][ii] = pr * (pacc[ii] - dl);
-        }
+        for (int ii = 0; ii < 16; ++ii) ds[kb][ii] = pv[ii] * (pacc[ii] - dl);
       }
-    }
 #pragma unroll
-    for (int t = 0; t < C::BN / 16; ++t) {
-      Frag<T> sf, sl;
-      frag_split<T>(&ds[t >> 1][(t & 1) * 8], sf, sl);
+      for (int t = 0; t < C::BN / 16; ++t) {
+        Frag<T> sf, sl;
+        frag_split<T>(&ds[t >> 1][(t & 1) * 8], sf, sl);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        Frag<T> ka;
-        if constexpr (C::kBf16)
-          ka = frag_load_tr(Ks, C::NS, 16 * t, 32 * db);
-        else
-          ka = frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half);
-        mma(adq[db], ka, sf);
-        if constexpr (NeedsSplit<T>::value) mma(adq[db], ka, sl);
+        for (int db = 0; db < D / 32; ++db) {
+          Frag<T> ka;
+          if constexpr (C::kBf16)
+            ka = frag_load_tr(Ks, C::NS, 16 * t, 32 * db);
+          else
+            ka = frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half);
+          mma(adq[db], ka, sf);
+          if constexpr (NeedsSplit<T>::value) mma(adq[db], ka, sl);
+        }
       }
     }
     if (n + 1 < n_steps) commit(b ^ 1);

@@ -106,10 +106,13 @@ __device__ __forceinline__ Frag<float> frag_from<float>(const float* x) {
   return f;
 }
 
-// Split of 8 fp32 values into hi = bf16(x) and lo = bf16(x - hi): a product with
-// hi + lo (two MFMAs, exact bf16 x bf16 products, fp32 sums) keeps about 16 significant
-// bits of x instead of 8.  The backward uses it for P and dS, whose bf16 rounding
-// would otherwise dominate the error of dQ, dK and dV.  fp32 fragments need no split.
+// Split of 8 fp32 values into two bf16 fragments hi + lo whose sum keeps about 16
+// significant bits of x instead of 8: hi = x with its low 16 bits cleared (the pair
+// packed with one byte permute), lo = bf16(x - hi) (x - hi is exact in fp32).  A
+// product with hi and one with lo (exact bf16 x bf16 products, fp32 sums) then
+// carries x to ~2^-16 relative.  The backward uses it for P and dS, whose bf16
+// rounding would otherwise dominate the error of dQ, dK and dV.  fp32 fragments need
+// no split.
 template <typename T>
 struct NeedsSplit {
   static constexpr bool value = false;
@@ -119,20 +122,20 @@ struct NeedsSplit<bf16_t> {
   static constexpr bool value = true;
 };
 
-__device__ __forceinline__ float bf16_round(float x) {
-  return __builtin_bit_cast(float, uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)))
-                                       << 16);
-}
-
 template <typename T>
 __device__ __forceinline__ void frag_split(const float* x, Frag<T>& hi, Frag<T>& lo) {
-  hi = frag_from<T>(x);
   if constexpr (NeedsSplit<T>::value) {
-    float r[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = x[j] - bf16_round(x[j]);
-    lo = frag_from<T>(r);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = __builtin_bit_cast(uint32_t, x[2 * j]);
+      const uint32_t b = __builtin_bit_cast(uint32_t, x[2 * j + 1]);
+      hi.v[j] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // high halves of a, b
+      const float la = x[2 * j] - __builtin_bit_cast(float, a & 0xffff0000u);
+      const float lb = x[2 * j + 1] - __builtin_bit_cast(float, b & 0xffff0000u);
+      lo.v[j] = pack_bf16x2(la, lb);
+    }
   } else {
+    hi = frag_from<T>(x);
     lo = hi;  // unused
   }
 }
@@ -159,10 +162,11 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// The mask in interval form: key kv is visible to row q iff kv <= q < end[kv].
-// Evaluated as one select (no short-circuit branch) so it stays a v_cndmask.
-__device__ __forceinline__ bool visible(int kv, int q, int end_kv) {
-  return (kv <= q) & (q < end_kv);
+// The mask in interval form: key kv is visible to row q iff kv <= q < end[kv], i.e.
+// (unsigned)(q - kv) < reach[kv] with reach = end - kv >= 0 (0 for a pad: never
+// visible).  One compare, used as a select (no short-circuit branch).
+__device__ __forceinline__ bool visible_u(int q_minus_kv, int reach) {
+  return uint32_t(q_minus_kv) < uint32_t(reach);
 }
 
 // Row (within a 32x32 accumulator block) of element i for lane half h.

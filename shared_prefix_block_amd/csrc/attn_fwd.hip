@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     vst.load(V + kv0 * ldk + koff, ldk, nvalid);
     if (threadIdx.x < C::BN) {
       const int r = threadIdx.x;
-      e_reg = r < nvalid ? p.end[kv0 + r] : int32_t(kv0 + r);
+      e_reg = r < nvalid ? p.end[kv0 + r] - int32_t(kv0 + r) : 0;  // reach
     }
   };
   auto commit = [&](int b) {  // registers -> LDS buffer b
@@ -164,71 +164,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     const T* Vs = Ks + C::K_ELEMS;
     const int32_t* Es = es0 + b * C::BN;
 
-    // S^T = K Q^T for BN keys x 32 queries (this wave)
-    float sv[C::BN / 32][16];
+    {
+      // S^T = K Q^T for BN keys x 32 queries (this wave)
+      float sv[C::BN / 32][16];
 #pragma unroll
-    for (int kb = 0; kb < C::BN / 32; ++kb) {
-      f32x16 acc_s = zero16();
-      const T* kr = Ks + (32 * kb + l32) * C::KS + 8 * half;
+      for (int kb = 0; kb < C::BN / 32; ++kb) {
+        f32x16 acc_s = zero16();
+        const T* kr = Ks + (32 * kb + l32) * C::KS + 8 * half;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) mma(acc_s, frag_load(kr + 16 * s), qf[s]);
+        for (int s = 0; s < D / 16; ++s) mma(acc_s, frag_load(kr + 16 * s), qf[s]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sv[kb][i] = acc_s[i];
-    }
-    if (partial) {  // uniform branch; the mask itself is a select
+        for (int i = 0; i < 16; ++i) sv[kb][i] = acc_s[i];
+      }
+      if (partial) {  // uniform branch; full tiles skip the mask
+        const int qd = qrow_i - kv0i;  // q - kv for the sub-step's first key
+#pragma unroll
+        for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int kvl = 32 * kb + g * 8 + half * 4;
+            const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
+            const int rv[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              sv[kb][4 * g + u] =
+                  visible_u(qd - kvl - u, rv[u]) ? sv[kb][4 * g + u] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int kvl = 32 * kb + g * 8 + half * 4;
-          const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
-          const int evs[4] = {ev.x, ev.y, ev.z, ev.w};
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      // raise the running max only when it grows by more than the slack
+      const bool grow = mx > m + kRescaleSlack || (m == -INFINITY && mx > -INFINITY);
+      if (__ballot(grow)) {  // wave-uniform branch
+        const float m_new = grow ? mx : m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;  // 0 if m = -inf
+        m = m_new;
+        l *= alpha;
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            sv[kb][4 * g + u] =
-                visible(kv0i + kvl + u, qrow_i, evs[u]) ? sv[kb][4 * g + u] : -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::BN / 32; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-    // raise the running max only when it grows by more than the slack
-    const bool grow = mx > m + kRescaleSlack || (m == -INFINITY && mx > -INFINITY);
-    if (__ballot(grow)) {  // wave-uniform branch
-      const float m_new = grow ? mx : m;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;  // 0 if m = -inf
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-    }
-    const float m_use = m == -INFINITY ? 0.f : m;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < C::BN / 32; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sv[kb][i], c, -m_use));
-        sv[kb][i] = pv;
-        rs += pv;
+        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
       }
-    l += rs;
+      const float m_use = m == -INFINITY ? 0.f : m;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sv[kb][i], c, -m_use));
+          sv[kb][i] = pv;
+          rs += pv;
+        }
+      l += rs;
 
-    // O^T += V^T P^T, 16 keys per step
+      // O^T += V^T P^T, 16 keys per step
 #pragma unroll
-    for (int t = 0; t < C::BN / 16; ++t) {
-      const Frag<T> pf = frag_from<T>(&sv[t >> 1][(t & 1) * 8]);
+      for (int t = 0; t < C::BN / 16; ++t) {
+        const Frag<T> pf = frag_from<T>(&sv[t >> 1][(t & 1) * 8]);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        Frag<T> va;
-        if constexpr (C::kBf16)
-          va = frag_load_tr(Vs, C::VS, 16 * t, 32 * db);
-        else
-          va = frag_load(Vs + (32 * db + l32) * C::VS + 16 * t + 8 * half);
-        mma(acc[db], va, pf);
+        for (int db = 0; db < D / 32; ++db) {
+          Frag<T> va;
+          if constexpr (C::kBf16)
+            va = frag_load_tr(Vs, C::VS, 16 * t, 32 * db);
+          else
+            va = frag_load(Vs + (32 * db + l32) * C::VS + 16 * t + 8 * half);
+          mma(acc[db], va, pf);
+        }
       }
     }
 
