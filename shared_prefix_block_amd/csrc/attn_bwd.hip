@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const int64_t kvrow = int64_t(kt) * C::BK + 32 * wave + l32;
   const bool kvvalid = kvrow < ntok;
   const int kvrow_i = int(kvrow);
-  const int32_t reach = kvvalid ? p.end[kvrow] - kvrow_i : 0;  // rows kv .. kv+reach-1
+  int32_t reach = kvvalid ? p.end[kvrow] - kvrow_i : 0;  // rows kv .. kv+reach-1
 
   const T* Kg = static_cast<const T*>(p.k);
   const T* Vg = static_cast<const T*>(p.v);
@@ -150,6 +150,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       kf[s] = kvvalid ? frag_load(Kg + off + 16 * s) : frag_zero<T>();
       vf[s] = kvvalid ? frag_load(Vg + off + 16 * s) : frag_zero<T>();
     }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      mark_ready(kf[s]);
+      mark_ready(vf[s]);
+    }
+    mark_ready(reach);
   }
   f32x16 adk[D / 32], adv[D / 32];
 #pragma unroll
@@ -188,6 +194,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   using TStage = TransStage<T, C::BMS, D, C::TS, C::NT>;
   typename std::conditional<C::kBf16, int, TStage>::type qtst, gtst;
   float l2_reg = INFINITY, dl_reg = 0.f;
+  bool l2_valid = false;
 
   auto issue = [&](int n) {
     int e, h, sub;
@@ -196,17 +203,18 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const int nvalid = ntok - q0 < C::BMS ? int(ntok - q0) : C::BMS;
     const T* qp = Qg + q0 * ldq + int64_t(h) * D;
     const T* gp = Gg + q0 * ldq + int64_t(h) * D;
+    {  // the per-row values first, loaded by every lane; rows past the end read 0
+      const int rr = int(threadIdx.x) & (C::BMS - 1);
+      const int64_t at = int64_t(h) * ntok + q0;
+      l2_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.L2 + at, nvalid * 4), rr * 4));
+      dl_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.Dl + at, nvalid * 4), rr * 4));
+      l2_valid = rr < nvalid;
+    }
     qst.load(qp, ldq, nvalid);
     gst.load(gp, ldq, nvalid);
     if constexpr (!C::kBf16) {
       qtst.load(qp, ldq, nvalid);
       gtst.load(gp, ldq, nvalid);
-    }
-    if (threadIdx.x < C::BMS) {
-      const int rr = threadIdx.x;
-      const bool ok = rr < nvalid;
-      l2_reg = ok ? p.L2[int64_t(h) * ntok + q0 + rr] : INFINITY;
-      dl_reg = ok ? p.Dl[int64_t(h) * ntok + q0 + rr] : 0.f;
     }
   };
   auto commit = [&](int b) {
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       gtst.store(base + 2 * C::N_ELEMS + C::T_ELEMS);
     }
     if (threadIdx.x < C::BMS) {
-      ld0[(b * 2 + 0) * C::BMS + threadIdx.x] = l2_reg;
+      ld0[(b * 2 + 0) * C::BMS + threadIdx.x] = l2_valid ? l2_reg : INFINITY;
       ld0[(b * 2 + 1) * C::BMS + threadIdx.x] = dl_reg;
     }
   };
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const int b = n & 1;
     int e, h, sub;
     decode(n, e, h, sub);
-    const bool partial = p.kind_csc[e] == 1;
+    const bool partial = tile_kind(p.kind_csc, e) == 1;
     const int q0i = p.row[e] * kTileM + sub * C::BMS;
     if (n + 1 < n_steps) issue(n + 1);
 
@@ -384,8 +392,15 @@ void dq_kernel(BwdParams p) {
       gf[s] = qvalid ? frag_load(Gg + off + 16 * s) : frag_zero<T>();
     }
   }
-  const float l2 = qvalid ? p.L2[int64_t(h) * ntok + qrow] : INFINITY;
-  const float dl = qvalid ? p.Dl[int64_t(h) * ntok + qrow] : 0.f;
+  float l2 = qvalid ? p.L2[int64_t(h) * ntok + qrow] : INFINITY;
+  float dl = qvalid ? p.Dl[int64_t(h) * ntok + qrow] : 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    mark_ready(qf[s]);
+    mark_ready(gf[s]);
+  }
+  mark_ready(l2);
+  mark_ready(dl);
   f32x16 adq[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adq[db] = zero16();
@@ -403,26 +418,27 @@ void dq_kernel(BwdParams p) {
   RowStage<T, C::BN, D, C::NS, C::NT> kst, vst;
   using TStage = TransStage<T, C::BN, D, C::TS, C::NT>;
   typename std::conditional<C::kBf16, int, TStage>::type ktst;
-  int32_t e_reg = 0;
+  int32_t e_reg = 0, kv_reg = 0;
 
   auto issue = [&](int n) {
     const int e = e0 + n / C::NSUB;
     const int64_t kv0 = int64_t(p.col[e]) * kTileN + (n % C::NSUB) * C::BN;
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
+    {  // every lane loads; a key past the end reads end = 0 and gets reach 0
+      const int r = int(threadIdx.x) & (C::BN - 1);
+      e_reg = int32_t(buf_load4(buf_rsrc(p.end + kv0, nvalid * 4), r * 4));
+      kv_reg = r < nvalid ? int32_t(kv0 + r) : 0;
+    }
     kst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
     vst.load(Vg + kv0 * ldk + koff, ldk, nvalid);
     if constexpr (!C::kBf16) ktst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
-    if (threadIdx.x < C::BN) {
-      const int r = threadIdx.x;
-      e_reg = r < nvalid ? p.end[kv0 + r] - int32_t(kv0 + r) : 0;  // reach
-    }
   };
   auto commit = [&](int b) {
     T* base = buf0 + b * C::BUF_ELEMS;
     kst.store(base);
     vst.store(base + C::N_ELEMS);
     if constexpr (!C::kBf16) ktst.store(base + 2 * C::N_ELEMS);
-    if (threadIdx.x < C::BN) es0[b * C::BN + threadIdx.x] = e_reg;
+    if (threadIdx.x < C::BN) es0[b * C::BN + threadIdx.x] = e_reg - kv_reg;  // reach
   };
 
   if (n_steps > 0) {
@@ -434,7 +450,7 @@ void dq_kernel(BwdParams p) {
   for (int n = 0; n < n_steps; ++n) {
     const int b = n & 1;
     const int e = e0 + n / C::NSUB;
-    const bool partial = p.kind[e] == 1;
+    const bool partial = tile_kind(p.kind, e) == 1;
     const int kv0i = p.col[e] * kTileN + (n % C::NSUB) * C::BN;
     if (n + 1 < n_steps) issue(n + 1);
 

@@ -82,10 +82,12 @@ __device__ __forceinline__ Frag<float> frag_load(const float* p) {
   return f;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);  // round to nearest even
-  return uint32_t(__builtin_bit_cast(uint16_t, x)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // Fragment from 8 fp32 values (probabilities or score gradients).
@@ -169,6 +171,14 @@ __device__ __forceinline__ bool visible_u(int q_minus_kv, int reach) {
   return uint32_t(q_minus_kv) < uint32_t(reach);
 }
 
+// Tile kind of list entry e (0 empty, 1 partial, 2 full) read as part of an aligned
+// dword: a wave-uniform 4-byte load goes through the scalar unit, so testing it never
+// waits on the vector loads in flight (a byte load would be a vector load).
+__device__ __forceinline__ int tile_kind(const uint8_t* kinds, int e) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(kinds)[e >> 2];
+  return int((w >> (8 * (e & 3))) & 0xffu);
+}
+
 // Row (within a 32x32 accumulator block) of element i for lane half h.
 __device__ __forceinline__ int acc_row(int i, int half) { return (i >> 2) * 8 + half * 4 + (i & 3); }
 
@@ -192,6 +202,39 @@ struct Vec4<float> {
   f32x4 v;
 };
 
+// ---------------------------------------------------------------------------
+// Buffer loads. A raw (stride 0) buffer resource spans `bytes` bytes from `base`;
+// a load at an offset at or past that returns zeros. Built per tile over its valid
+// rows, it zero-fills the rows past the end of the sequence without a branch, and
+// the per-lane offsets stay loop-invariant 32-bit registers (no 64-bit address
+// arithmetic per load). Word 3 selects 32-bit data format, as gfx9 raw buffers use.
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), bytes, kBufWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Make the wait-count pass wait here for the loads that produced a value. A loop
+// keeps its operand fragments in registers; without this the pass, which merges all
+// paths into the loop header, leaves their loads pending there and makes the loop's
+// first MFMA wait for the tile prefetch issued just before it as well. The empty asm
+// passes the value through; it is not volatile and touches no memory, so uniform
+// loads in the loop still go through the scalar unit.
+__device__ __forceinline__ void mark_ready(u32x4& v) { asm("" : "+v"(v)); }
+__device__ __forceinline__ void mark_ready(f32x4& v) { asm("" : "+v"(v)); }
+__device__ __forceinline__ void mark_ready(float& v) { asm("" : "+v"(v)); }
+__device__ __forceinline__ void mark_ready(int32_t& v) { asm("" : "+v"(v)); }
+__device__ __forceinline__ void mark_ready(Frag<bf16_t>& f) { mark_ready(f.v); }
+__device__ __forceinline__ void mark_ready(Frag<float>& f) {
+  mark_ready(f.lo);
+  mark_ready(f.hi);
+}
+
 __device__ __forceinline__ Vec4<bf16_t> vec4_load(const bf16_t* p) {
   Vec4<bf16_t> r;
   r.v = *reinterpret_cast<const u32x2*>(p);
@@ -201,6 +244,12 @@ __device__ __forceinline__ Vec4<float> vec4_load(const float* p) {
   Vec4<float> r;
   r.v = *reinterpret_cast<const f32x4*>(p);
   return r;
+}
+__device__ __forceinline__ void vec4_bload(Vec4<bf16_t>& v, __amdgpu_buffer_rsrc_t r, int off) {
+  v.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void vec4_bload(Vec4<float>& v, __amdgpu_buffer_rsrc_t r, int off) {
+  v.v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 template <typename T>
 __device__ __forceinline__ Vec4<T> vec4_zero();
@@ -313,13 +362,15 @@ struct RowStage {
   static constexpr int N = R * CPR / NT;
   static_assert((R * CPR) % NT == 0, "tile must split evenly over the threads");
   u32x4 r[N];
+  // rows >= nvalid read as zeros; nvalid * ld * sizeof(T) must fit in an int
   __device__ __forceinline__ void load(const T* src, int64_t ld, int nvalid) {
+    const int pitch = int(ld) * int(sizeof(T));
+    const auto rs = buf_rsrc(src, nvalid * pitch);
 #pragma unroll
     for (int it = 0; it < N; ++it) {
       const int c = it * NT + int(threadIdx.x);
       const int row = c / CPR, cc = (c % CPR) * E;
-      r[it] = row < nvalid ? *reinterpret_cast<const u32x4*>(src + int64_t(row) * ld + cc)
-                           : u32x4{0u, 0u, 0u, 0u};
+      r[it] = buf_load16(rs, row * pitch + cc * int(sizeof(T)));
     }
   }
   __device__ __forceinline__ void store(T* dst) const {
@@ -340,15 +391,17 @@ struct TransStage {
   static constexpr int N = (R / 4) * CG / NT;
   static_assert(((R / 4) * CG) % NT == 0, "tile must split evenly over the threads");
   Vec4<T> rows[N][4];
+  // rows >= nvalid read as zeros; nvalid * ld * sizeof(T) must fit in an int
   __device__ __forceinline__ void load(const T* src, int64_t ld, int nvalid) {
+    const int pitch = int(ld) * int(sizeof(T));
+    const auto rs = buf_rsrc(src, nvalid * pitch);
 #pragma unroll
     for (int it = 0; it < N; ++it) {
       const int b = it * NT + int(threadIdx.x);
       const int r0 = (b / CG) * 4, c0 = (b % CG) * 4;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        rows[it][k] =
-            (r0 + k < nvalid) ? vec4_load(src + int64_t(r0 + k) * ld + c0) : vec4_zero<T>();
+        vec4_bload(rows[it][k], rs, (r0 + k) * pitch + c0 * int(sizeof(T)));
     }
   }
   __device__ __forceinline__ void store(T* dst) const {

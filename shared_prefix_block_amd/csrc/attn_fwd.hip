@@ -103,6 +103,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     const T* qp = Q + (qrow * hq + h) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = qvalid ? frag_load(qp + 16 * s) : frag_zero<T>();
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) mark_ready(qf[s]);
   }
 
   f32x16 acc[D / 32];
@@ -127,24 +129,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   using VStage = typename std::conditional<C::kBf16, RowStage<T, C::BN, D, C::VS, C::NT>,
                                            TransStage<T, C::BN, D, C::VS, C::NT>>::type;
   VStage vst;
-  int32_t e_reg = 0;
+  int32_t e_reg = 0, kv_reg = 0;
 
   auto issue = [&](int n) {  // global reads of sub-step n into registers
     const int e = e0 + n / C::NSUB;
     const int64_t kv0 = int64_t(p.col[e]) * kTileN + (n % C::NSUB) * C::BN;
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
+    // end[] first: the loads retire in order, so waiting for it at commit does not
+    // wait for the K/V reads issued after it
+    {  // every lane loads; a key past the end reads end = 0 and gets reach 0
+      const int r = int(threadIdx.x) & (C::BN - 1);
+      e_reg = int32_t(buf_load4(buf_rsrc(p.end + kv0, nvalid * 4), r * 4));
+      kv_reg = r < nvalid ? int32_t(kv0 + r) : 0;
+    }
     kst.load(K + kv0 * ldk + koff, ldk, nvalid);
     vst.load(V + kv0 * ldk + koff, ldk, nvalid);
-    if (threadIdx.x < C::BN) {
-      const int r = threadIdx.x;
-      e_reg = r < nvalid ? p.end[kv0 + r] - int32_t(kv0 + r) : 0;  // reach
-    }
   };
   auto commit = [&](int b) {  // registers -> LDS buffer b
     T* kb = buf0 + b * C::BUF_ELEMS;
     kst.store(kb);
     vst.store(kb + C::K_ELEMS);
-    if (threadIdx.x < C::BN) es0[b * C::BN + threadIdx.x] = e_reg;
+    if (threadIdx.x < C::BN) es0[b * C::BN + threadIdx.x] = e_reg - kv_reg;  // reach
   };
 
   if (n_steps > 0) {
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   for (int n = 0; n < n_steps; ++n) {
     const int b = n & 1;
     const int e = e0 + n / C::NSUB;
-    const bool partial = p.kind[e] == 1;
+    const bool partial = tile_kind(p.kind, e) == 1;
     const int kv0i = p.col[e] * kTileN + (n % C::NSUB) * C::BN;
     if (n + 1 < n_steps) issue(n + 1);
 
