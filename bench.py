@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--split", action="store_true",
+                    help="backward with P and dS as hi + lo bf16 pairs (PSA_BWD_SPLIT_PDS)")
     ap.add_argument("--calib-mb", type=int, default=0,
                     help="before warm-up, run one elementwise negation over this many MiB of "
                          "fp32 (reads and writes that many bytes): the reference kernel the "
@@ -175,7 +177,7 @@ def main():
         if backward:
             for i, nm in enumerate(names[2:]):
                 psa.bwd(m, q, k, v, o, lse, do, workspace=ws, grad_dtype=gdt,
-                        stages=stage_of[nm], out=grads)
+                        stages=stage_of[nm], out=grads, split=args.split)
                 ev(3 + i)
         return m
 
@@ -250,6 +252,7 @@ def main():
         "config": {"workload": describe(cfg, lay), "T": lay.T, "T_real": lay.T_real,
                    "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": d,
                    "passes": cfg.passes, "grad_dtype": args.grad_dtype,
+                   "bwd_p_ds": "hi+lo bf16" if args.split else "bf16, hi+lo where large",
                    "tiles_128": {"full": info["n_full"], "partial": info["n_partial"]},
                    "kept_pairs_per_head": kept},
         "pct_bf16_peak" if cfg.dtype == "bf16" else "pct_fp32_peak": round(100 * value / peak, 2),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PSA_ABI_VERSION 1
+#define PSA_ABI_VERSION 2
 
 typedef enum {
   PSA_OK = 0,
@@ -183,24 +183,31 @@ psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtyp
 
 /*
  * The backward in stages, for callers that time or overlap them (psa_bwd runs all
- * three in order).  stages is a nonzero OR of:
+ * three in order), with options.  flags is the OR of a nonzero set of stages:
  *   PSA_STAGE_PREPARE  D = rowsum(dO * O) and LSE in log2 units, into the workspace
  *                      (reads o, lse, dout);
  *   PSA_STAGE_DKDV     dK, dV (reads q, k, v, dout and the prepared workspace);
  *   PSA_STAGE_DQ       dQ (reads q, k, v, dout and the prepared workspace).
- * DKDV and DQ depend only on PREPARE, not on each other.  Arguments and errors as
- * psa_bwd (pointers a requested stage does not read may be NULL), plus PSA_ERR_VALUE
- * for an empty or unknown stage set.
+ * DKDV and DQ depend only on PREPARE, not on each other.  And optionally:
+ *   PSA_BWD_SPLIT_PDS  carry P and dS into the dV, dK and dQ products as a pair of
+ *                      bf16 fragments hi + lo (about 16 significant bits instead of
+ *                      8, at two MFMAs per product instead of one).  Without it P
+ *                      and dS are rounded to bf16 once before those products, as in
+ *                      FlashAttention-2; psa_bwd runs without it.  No effect on fp32
+ *                      inputs, whose products are fp32 throughout.
+ * Arguments and errors as psa_bwd (pointers a requested stage does not read may be
+ * NULL), plus PSA_ERR_VALUE for an empty stage set or an unknown bit.
  */
 #define PSA_STAGE_PREPARE 1
 #define PSA_STAGE_DKDV 2
 #define PSA_STAGE_DQ 4
 #define PSA_STAGE_ALL 7
+#define PSA_BWD_SPLIT_PDS 16
 psa_status psa_bwd_stages(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype,
                           int64_t T, int32_t hq, int32_t hkv, int32_t d, float scale,
                           const void* q, const void* k, const void* v, const void* o,
                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                          void* workspace, size_t workspace_bytes, int32_t stages,
+                          void* workspace, size_t workspace_bytes, int32_t flags,
                           void* stream);
 
 #ifdef __cplusplus

@@ -456,14 +456,17 @@ psa_status psa_bwd_stages(const psa_tile_map* map, psa_dtype dtype, psa_dtype gr
                           int64_t T, int32_t hq, int32_t hkv, int32_t d, float scale,
                           const void* q, const void* k, const void* v, const void* o,
                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                          void* workspace, size_t workspace_bytes, int32_t stages,
+                          void* workspace, size_t workspace_bytes, int32_t flags,
                           void* stream) {
   psa_status st = check_attn_args(map, dtype, T, hq, hkv, d, scale, PSA_PASS_BWD);
   if (st != PSA_OK) return st;
   if (grad_dtype != PSA_FP32 && grad_dtype != dtype)
     return psa_set_error(PSA_ERR_DTYPE, "grad_dtype must be PSA_FP32 or the input dtype");
-  if (stages <= 0 || stages > PSA_STAGE_ALL)
-    return psa_set_error(PSA_ERR_VALUE, "stages must be a nonzero subset of PSA_STAGE_ALL");
+  const int32_t stages = flags & PSA_STAGE_ALL;
+  const bool split = (flags & PSA_BWD_SPLIT_PDS) != 0;
+  if (stages == 0 || (flags & ~(PSA_STAGE_ALL | PSA_BWD_SPLIT_PDS)) != 0)
+    return psa_set_error(PSA_ERR_VALUE,
+                         "flags must hold a nonzero set of stages and no unknown bit");
   if (T == 0) return PSA_OK;
   const bool pre = stages & PSA_STAGE_PREPARE, kv = stages & PSA_STAGE_DKDV,
              dqs = stages & PSA_STAGE_DQ;
@@ -475,7 +478,7 @@ psa_status psa_bwd_stages(const psa_tile_map* map, psa_dtype dtype, psa_dtype gr
   if (!workspace || workspace_bytes < need)
     return psa_set_error(PSA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
   hipError_t e = launch_bwd(*map, dtype, grad_dtype, s, q, k, v, o, lse, dout, dq, dk, dv,
-                            workspace, stages, static_cast<hipStream_t>(stream));
+                            workspace, stages, split, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return psa_hip_error(e, "backward launch");
   return PSA_OK;
 }

@@ -58,6 +58,36 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------------------
+// Precision of P and dS in the products that form dV, dK and dQ (bf16 inputs).
+// kSplitAdaptive: a wave's fragment (16 queries x 32 keys) is rounded to bf16 once,
+// unless its largest P exceeds kTauP or its largest |dS| exceeds kTauS; then the
+// residual (frag_residual) goes through a second MFMA per product.  A rounded element
+// is off by at most 2^-9 of itself, so a rounded fragment adds at most 2^-9 * tau per
+// element times the other operand to a gradient, while the few large entries (rows
+// that see few keys, where the softmax concentrates) keep about 16 bits.
+// kSplitAll: every fragment gets the residual pass.  fp32 inputs have nothing to split.
+// ---------------------------------------------------------------------------
+constexpr int kSplitAdaptive = 0, kSplitAll = 1;
+constexpr float kTauP = 0.125f, kTauS = 1.0f;
+
+template <typename T, int MODE, bool WITH_P>
+__device__ __forceinline__ bool split_wanted(const float* p8, const float* s8) {
+  if constexpr (!std::is_same<T, bf16_t>::value) {
+    return false;
+  } else if constexpr (MODE == kSplitAll) {
+    return true;
+  } else {
+    float mp = 0.f, ms = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (WITH_P) mp = fmaxf(mp, p8[j]);  // P >= 0
+      ms = fmaxf(ms, fabsf(s8[j]));
+    }
+    return __any(mp > kTauP || ms > kTauS);  // wave-uniform
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bwd_pre: 16 lanes per (row, head); 16 rows per 256-thread block.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
@@ -116,7 +146,7 @@ struct DkdvCfg {
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * EB + 2 * 2 * BMS * 4;
 };
 
-template <typename T, typename G, int D>
+template <typename T, typename G, int D, int MODE>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   using C = DkdvCfg<T, D>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
@@ -285,27 +315,28 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          Frag<T> pf, pl, sf, sl;
-          frag_split<T>(pv + 8 * t, pf, pl);
-          frag_split<T>(ds + 8 * t, sf, sl);
+          // dV += dO^T P and dK += Q^T dS over these 16 queries: P and dS rounded to
+          // the MFMA type, then, where split_wanted, the residuals in a second pass
+          auto products = [&](const Frag<T>& pf, const Frag<T>& sf) {
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            Frag<T> ga, qa;
-            if constexpr (C::kBf16) {
-              ga = frag_load_tr(Gs, C::NS, 32 * qb + 16 * t, 32 * db);
-              qa = frag_load_tr(Qs, C::NS, 32 * qb + 16 * t, 32 * db);
-            } else {
-              const int col0 = 32 * qb + 16 * t + 8 * half;
-              ga = frag_load(Gt + (32 * db + l32) * C::TS + col0);
-              qa = frag_load(Qt + (32 * db + l32) * C::TS + col0);
+            for (int db = 0; db < D / 32; ++db) {
+              Frag<T> ga, qa;
+              if constexpr (C::kBf16) {
+                ga = frag_load_tr(Gs, C::NS, 32 * qb + 16 * t, 32 * db);
+                qa = frag_load_tr(Qs, C::NS, 32 * qb + 16 * t, 32 * db);
+              } else {
+                const int col0 = 32 * qb + 16 * t + 8 * half;
+                ga = frag_load(Gt + (32 * db + l32) * C::TS + col0);
+                qa = frag_load(Qt + (32 * db + l32) * C::TS + col0);
+              }
+              mma(adv[db], ga, pf);
+              mma(adk[db], qa, sf);
             }
-            mma(adv[db], ga, pf);
-            mma(adk[db], qa, sf);
-            if constexpr (NeedsSplit<T>::value) {
-              mma(adv[db], ga, pl);
-              mma(adk[db], qa, sl);
-            }
-          }
+          };
+          const Frag<T> pf = frag_from<T>(pv + 8 * t), sf = frag_from<T>(ds + 8 * t);
+          products(pf, sf);
+          if (split_wanted<T, MODE, true>(pv + 8 * t, ds + 8 * t))
+            products(frag_residual(pv + 8 * t, pf), frag_residual(ds + 8 * t, sf));
         }
       }
     }
@@ -356,7 +387,7 @@ struct DqCfg {
   static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
 };
 
-template <typename T, typename G, int D>
+template <typename T, typename G, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, D>::WAVES_PER_EU)))
 void dq_kernel(BwdParams p) {
   using C = DqCfg<T, D>;
@@ -491,18 +522,23 @@ void dq_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int t = 0; t < C::BN / 16; ++t) {
-        Frag<T> sf, sl;
-        frag_split<T>(&ds[t >> 1][(t & 1) * 8], sf, sl);
+        // dQ^T += K^T dS^T over these 16 keys: dS rounded, then where split_wanted its
+        // residual in a second pass
+        const float* dst = &ds[t >> 1][(t & 1) * 8];
+        auto products = [&](const Frag<T>& sf) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          Frag<T> ka;
-          if constexpr (C::kBf16)
-            ka = frag_load_tr(Ks, C::NS, 16 * t, 32 * db);
-          else
-            ka = frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half);
-          mma(adq[db], ka, sf);
-          if constexpr (NeedsSplit<T>::value) mma(adq[db], ka, sl);
-        }
+          for (int db = 0; db < D / 32; ++db) {
+            Frag<T> ka;
+            if constexpr (C::kBf16)
+              ka = frag_load_tr(Ks, C::NS, 16 * t, 32 * db);
+            else
+              ka = frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half);
+            mma(adq[db], ka, sf);
+          }
+        };
+        const Frag<T> sf = frag_from<T>(dst);
+        products(sf);
+        if (split_wanted<T, MODE, false>(nullptr, dst)) products(frag_residual(dst, sf));
       }
     }
     if (n + 1 < n_steps) commit(b ^ 1);
@@ -526,7 +562,7 @@ void dq_kernel(BwdParams p) {
 
 size_t ws_align(size_t x) { return (x + 255) / 256 * 256; }
 
-template <typename T, typename G, int D>
+template <typename T, typename G, int D, int MODE>
 hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void* q,
                         const void* k, const void* v, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, void* workspace,
@@ -570,14 +606,14 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
     p.chunk = 2;
     const int64_t per = 8 * int64_t(p.chunk);
     const int64_t grid = (p.n_work + per - 1) / per * per;
-    hipLaunchKernelGGL((dkdv_kernel<T, G, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
   }
   if (stages & PSA_STAGE_DQ) {
     p.n_work = map.nq * s.hq;
     p.chunk = rep * 2;
     const int64_t per = 8 * int64_t(p.chunk);
     const int64_t grid = (p.n_work + per - 1) / per * per;
-    hipLaunchKernelGGL((dq_kernel<T, G, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((dq_kernel<T, G, D, MODE>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -594,29 +630,33 @@ size_t bwd_workspace_bytes(const AttnShape& s) {
 hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype gdt, const AttnShape& s,
                       const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                      void* workspace, int stages, hipStream_t stream) {
+                      void* workspace, int stages, bool split, hipStream_t stream) {
   using psa::bf16_t;
-#define PSA_BWD(T, G, D)                                                                    \
-  return psa::launch_bwd_t<T, G, D>(map, s, q, k, v, o, lse, dout, dq, dk, dv, workspace, \
-                                    stages, stream)
+#define PSA_BWD(T, G, D, MODE)                                                      \
+  return psa::launch_bwd_t<T, G, D, MODE>(map, s, q, k, v, o, lse, dout, dq, dk, dv, \
+                                          workspace, stages, stream)
+#define PSA_BWD_BF16(G, D)                          \
+  if (split) PSA_BWD(bf16_t, G, D, psa::kSplitAll); \
+  PSA_BWD(bf16_t, G, D, psa::kSplitAdaptive)
   if (dt == PSA_BF16 && gdt == PSA_FP32) {
     switch (s.d) {
-      case 64: PSA_BWD(bf16_t, float, 64);
-      case 128: PSA_BWD(bf16_t, float, 128);
-      case 256: PSA_BWD(bf16_t, float, 256);
+      case 64: PSA_BWD_BF16(float, 64);
+      case 128: PSA_BWD_BF16(float, 128);
+      case 256: PSA_BWD_BF16(float, 256);
     }
   } else if (dt == PSA_BF16 && gdt == PSA_BF16) {
     switch (s.d) {
-      case 64: PSA_BWD(bf16_t, bf16_t, 64);
-      case 128: PSA_BWD(bf16_t, bf16_t, 128);
-      case 256: PSA_BWD(bf16_t, bf16_t, 256);
+      case 64: PSA_BWD_BF16(bf16_t, 64);
+      case 128: PSA_BWD_BF16(bf16_t, 128);
+      case 256: PSA_BWD_BF16(bf16_t, 256);
     }
-  } else if (dt == PSA_FP32 && gdt == PSA_FP32) {
+  } else if (dt == PSA_FP32 && gdt == PSA_FP32) {  // fp32 products: nothing to split
     switch (s.d) {
-      case 64: PSA_BWD(float, float, 64);
-      case 128: PSA_BWD(float, float, 128);
+      case 64: PSA_BWD(float, float, 64, psa::kSplitAdaptive);
+      case 128: PSA_BWD(float, float, 128, psa::kSplitAdaptive);
     }
   }
+#undef PSA_BWD_BF16
 #undef PSA_BWD
   return hipErrorInvalidValue;
 }

@@ -108,38 +108,28 @@ __device__ __forceinline__ Frag<float> frag_from<float>(const float* x) {
   return f;
 }
 
-// Split of 8 fp32 values into two bf16 fragments hi + lo whose sum keeps about 16
-// significant bits of x instead of 8: hi = x with its low 16 bits cleared (the pair
-// packed with one byte permute), lo = bf16(x - hi) (x - hi is exact in fp32).  A
-// product with hi and one with lo (exact bf16 x bf16 products, fp32 sums) then
-// carries x to ~2^-16 relative.  The backward uses it for P and dS, whose bf16
-// rounding would otherwise dominate the error of dQ, dK and dV.  fp32 fragments need
-// no split.
-template <typename T>
-struct NeedsSplit {
-  static constexpr bool value = false;
-};
-template <>
-struct NeedsSplit<bf16_t> {
-  static constexpr bool value = true;
-};
-
-template <typename T>
-__device__ __forceinline__ void frag_split(const float* x, Frag<T>& hi, Frag<T>& lo) {
-  if constexpr (NeedsSplit<T>::value) {
+// Residual of a rounded fragment: with hi = frag_from(x) (x rounded to bf16), returns
+// lo = bf16(x - hi).  x - hi is exact in fp32, so hi + lo carries x to about 2^-17
+// relative instead of 2^-9, and a product with hi followed by one with lo (exact
+// bf16 x bf16 products, fp32 sums) is that much closer to the fp32 product.  The
+// backward uses it for P and dS where they are large.
+__device__ __forceinline__ Frag<bf16_t> frag_residual(const float* x, const Frag<bf16_t>& hi) {
+  Frag<bf16_t> lo;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t a = __builtin_bit_cast(uint32_t, x[2 * j]);
-      const uint32_t b = __builtin_bit_cast(uint32_t, x[2 * j + 1]);
-      hi.v[j] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // high halves of a, b
-      const float la = x[2 * j] - __builtin_bit_cast(float, a & 0xffff0000u);
-      const float lb = x[2 * j + 1] - __builtin_bit_cast(float, b & 0xffff0000u);
-      lo.v[j] = pack_bf16x2(la, lb);
-    }
-  } else {
-    hi = frag_from<T>(x);
-    lo = hi;  // unused
+  for (int j = 0; j < 4; ++j) {
+    const float h0 = __builtin_bit_cast(float, hi.v[j] << 16);          // element 2j
+    const float h1 = __builtin_bit_cast(float, hi.v[j] & 0xffff0000u);  // element 2j+1
+    lo.v[j] = pack_bf16x2(x[2 * j] - h0, x[2 * j + 1] - h1);
   }
+  return lo;
+}
+// fp32 fragments hold x exactly: the residual is 0 (the kernels never ask for it; it
+// keeps the shared code well-formed for both types).
+__device__ __forceinline__ Frag<float> frag_residual(const float*, const Frag<float>&) {
+  Frag<float> lo;
+  lo.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+  lo.hi = lo.lo;
+  return lo;
 }
 
 __device__ __forceinline__ void mma(f32x16& c, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {

@@ -87,4 +87,4 @@ size_t bwd_workspace_bytes(const AttnShape& s);
 hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype grad_dt, const AttnShape& s,
                       const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                      void* workspace, int stages, hipStream_t stream);
+                      void* workspace, int stages, bool split, hipStream_t stream);

@@ -33,6 +33,7 @@ EXPORTS = ["psa_abi_version", "psa_status_string", "psa_last_error", "psa_tile_s
            "psa_tile_map_export", "psa_tile_map_destroy", "psa_fwd", "psa_bwd_workspace_size",
            "psa_bwd", "psa_bwd_stages"]
 STAGE_PREPARE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
+BWD_SPLIT_PDS = 16  # option bit of psa_bwd_stages: P and dS as hi + lo bf16 pairs
 
 
 class PsaError(RuntimeError):
@@ -260,11 +261,12 @@ def bwd_workspace_size(m: TileMap, q: torch.Tensor, k: torch.Tensor) -> int:
 
 def bwd(m: TileMap, q, k, v, o, lse, do, scale: Optional[float] = None,
         workspace: Optional[torch.Tensor] = None, grad_dtype: torch.dtype = torch.float32,
-        stages: int = STAGE_ALL, out=None):
+        stages: int = STAGE_ALL, out=None, split: bool = False):
     """dQ, dK, dV in ``grad_dtype`` (float32, the default, or q's dtype).
 
-    ``stages`` selects backward stages (psa_bwd_stages); ``out`` = (dq, dk, dv) reuses
-    output buffers."""
+    ``stages`` selects backward stages (psa_bwd_stages); ``split`` carries P and dS as
+    hi + lo bf16 pairs (PSA_BWD_SPLIT_PDS); ``out`` = (dq, dk, dv) reuses output
+    buffers."""
     lib = load()
     _check_qkv(q, k, v)
     for t in (o, do):
@@ -288,8 +290,8 @@ def bwd(m: TileMap, q, k, v, o, lse, do, scale: Optional[float] = None,
         _check(lib.psa_bwd_stages(m.handle, _dtype_code(q.dtype), _dtype_code(grad_dtype), T, hq,
                                   hkv, d, 0.0 if scale is None else float(scale), _ptr(q), _ptr(k),
                                   _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                                  _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), stages,
-                                  _stream(q.device)))
+                                  _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
+                                  stages | (BWD_SPLIT_PDS if split else 0), _stream(q.device)))
     return dq, dk, dv
 
 

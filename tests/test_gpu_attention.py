@@ -22,7 +22,7 @@ def _gpu():
 
 
 def _run(lay, hq, hkv, d, dtype, seed, sigma=1.0, backward=True, scale=None,
-         grad_dtype=torch.float32):
+         grad_dtype=torch.float32, split=False):
     q, k, v, do = wl.make_tensors(lay.T, hq, hkv, d, dtype, sigma, seed)
     tdt = DT[dtype]
     m = psa.layout_tile_map(lay, "cuda", dtype=tdt, d=d)
@@ -30,7 +30,8 @@ def _run(lay, hq, hkv, d, dtype, seed, sigma=1.0, backward=True, scale=None,
     o, lse = psa.fwd(m, qd, kd, vd, scale)
     out = {"o": o, "lse": lse}
     if backward:
-        dq, dk, dv = psa.bwd(m, qd, kd, vd, o, lse, dod, scale, grad_dtype=grad_dtype)
+        dq, dk, dv = psa.bwd(m, qd, kd, vd, o, lse, dod, scale, grad_dtype=grad_dtype,
+                             split=split)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return (q, k, v, do), out
@@ -108,6 +109,34 @@ def test_bf16_gradient_outputs(d):
         compare(name, got[name], ref, torch.bfloat16, out_round=2.0 ** -9)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_split_mode_is_more_accurate(d):
+    """PSA_BWD_SPLIT_PDS carries P and dS to ~17 bits.  dV = P^T dO then sits within a
+    tenth of the bf16 bar; dK and dQ also carry the rounding of the bf16 O that
+    D = rowsum(dO * O) is formed from (part of the interface), so they get the bar."""
+    rng = np.random.default_rng(60 + d)
+    specs = wl.random_group_specs(rng, max_groups=3, max_p=300, max_g=4, max_r=200)
+    lay = wl.tokens_layout(specs, pad_multiple=32)
+    say(f"split mode d={d} T={lay.T}")
+    (q, k, v, do), got = _run(lay, 4, 2, d, "bf16", 11, split=True)
+    _, _, dq, dk, dv = oa.backward(meta_from_layout(lay), q, k, v, do)
+    err = float((got["dv"].double().cpu() - torch.as_tensor(dv)).abs().max())
+    assert err <= 2e-3, ("dv", err)
+    compare("dq", got["dq"], dq, torch.bfloat16)
+    compare("dk", got["dk"], dk, torch.bfloat16)
+
+
+def test_bwd_flags_rejected():
+    lay = wl.tokens_layout([(40, [30, 20])])
+    q, k, v, do = (x.cuda() for x in wl.make_tensors(lay.T, 2, 2, 64, "bf16"))
+    m = psa.layout_tile_map(lay, "cuda", dtype=torch.bfloat16, d=64)
+    o, lse = psa.fwd(m, q, k, v)
+    for bad in (0, psa.BWD_SPLIT_PDS, 32, psa.STAGE_ALL | 8, -1):
+        with pytest.raises(RuntimeError, match="flags"):
+            psa.bwd(m, q, k, v, o, lse, do, stages=bad)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("T", [1, 2, 31, 127, 128, 129, 300])
 def test_single_causal_sequence_ragged(T):
     """One group with no completion = plain causal attention, at ragged lengths."""
@@ -164,14 +193,16 @@ def _boundaries(lay):
     return pts[:400]
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
-def test_config_parity_sampled(idx):
+@pytest.mark.parametrize("idx,split", [(1, False), (2, False), (3, False), (4, False),
+                                       (5, False), (2, True), (4, True)])
+def test_config_parity_sampled(idx, split):
     cfg = wl.CONFIGS[idx]
     lay = wl.layout_for(cfg)
     backward = cfg.passes != "fwd"
-    say(f"config {idx}: T={lay.T} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d} {cfg.dtype}")
+    say(f"config {idx}: T={lay.T} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d} {cfg.dtype} "
+        f"split={split}")
     (q, k, v, do), got = _run(lay, cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.idx, cfg.sigma,
-                              backward)
+                              backward, split=split)
     meta = meta_from_layout(lay)
     tdt = DT[cfg.dtype]
     rng = np.random.default_rng(idx)
