@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <numeric>
 #include <string>
@@ -43,15 +44,64 @@ psa_status check_tiles(int64_t T, int32_t bm, int32_t bn) {
   return PSA_OK;
 }
 
+// Device memory of maps comes from a library-owned stream-ordered pool per device:
+// a map's buffers are allocated and freed on its build stream, so a map built after
+// another is destroyed reuses that memory without a device-wide wait.  If the pool
+// cannot be created the plain allocator is used instead.
+hipMemPool_t pool_for(int dev) {
+  static std::mutex mu;
+  static std::vector<hipMemPool_t> pools;
+  static std::vector<bool> tried;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 0) return nullptr;
+  if (pools.size() <= size_t(dev)) {
+    pools.resize(dev + 1, nullptr);
+    tried.resize(dev + 1, false);
+  }
+  if (!tried[dev]) {
+    tried[dev] = true;
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+      uint64_t keep = uint64_t{1} << 30;  // bytes kept for reuse across syncs
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+      pools[dev] = pool;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  return pools[dev];
+}
+
+hipError_t map_alloc(psa_tile_map* m, void** p, size_t bytes) {
+  hipMemPool_t pool = pool_for(m->device);
+  if (pool) {
+    m->pooled = true;
+    return hipMallocFromPoolAsync(p, bytes, pool, m->stream);
+  }
+  m->pooled = false;
+  return hipMalloc(p, bytes);
+}
+
+void map_free(const psa_tile_map* m, void* p) {
+  if (!p) return;
+  if (m->pooled) (void)hipFreeAsync(p, m->stream);
+  else (void)hipFree(p);
+}
+
 void free_map(psa_tile_map* m) {
   if (!m) return;
-  if (m->buf1) (void)hipFree(m->buf1);
-  if (m->buf2) (void)hipFree(m->buf2);
+  map_free(m, m->buf1);
+  map_free(m, m->buf2);
   delete m;
 }
 
 // Descending-length order of CSR rows / CSC columns (stable: ties keep index order).
-void length_order(const std::vector<int32_t>& ptr, int64_t n, int32_t* out) {
+void length_order(const int32_t* ptr, int64_t n, int32_t* out) {
   std::vector<int32_t> idx(n);
   std::iota(idx.begin(), idx.end(), 0);
   std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
@@ -60,21 +110,30 @@ void length_order(const std::vector<int32_t>& ptr, int64_t n, int32_t* out) {
   std::copy(idx.begin(), idx.end(), out);
 }
 
-// Phase 1 allocation + classification; the per-token `end` array must be filled by
-// the caller's launch between alloc_phase1 and finish_build.
-psa_status alloc_phase1(psa_tile_map* m, size_t* info_off, size_t* scratch_off,
-                        size_t* flag_off) {
+// Phase-1 allocation.  Layout: end | kinds | scratch | info (8 x int64) | row_ptr |
+// col_ptr, the last three contiguous so that one copy brings them back.
+struct Phase1 {
+  int32_t* scratch = nullptr;  // per-k-tile summaries, then reused by nothing else
+  int32_t* tok_scratch = nullptr;
+  int64_t* info = nullptr;     // nnz, n_full, n_partial, first layout error
+  size_t readback_bytes = 0;   // info .. end of col_ptr
+};
+
+psa_status alloc_phase1(psa_tile_map* m, Phase1* ph) {
   Carver c;
+  const int64_t nk1 = std::max<int64_t>(m->nk, 1);
   size_t o_end = c.take<int32_t>(std::max<int64_t>(m->T, 1));
   size_t o_kinds = c.take<uint8_t>(std::max<int64_t>(m->nq * m->nk, 1));
+  size_t o_scr = c.take<int32_t>(2 * align_up(nk1, 64));
+  size_t o_tok = c.take<int32_t>(std::max<int64_t>(tokens_scratch_ints(m->T), 1));
+  size_t o_info = c.take<int64_t>(8);
   size_t o_rp = c.take<int32_t>(m->nq + 1);
   size_t o_cp = c.take<int32_t>(m->nk + 1);
-  size_t o_kmin = c.take<int32_t>(std::max<int64_t>(m->nk, 1));
-  size_t o_kmax = c.take<int32_t>(std::max<int64_t>(m->nk, 1));
-  size_t o_info = c.take<int64_t>(8);
-  size_t o_flag = c.take<int32_t>(4);
-  if (hipMalloc(&m->buf1, c.off) != hipSuccess) {
+  const size_t total = c.off;
+  hipError_t e = map_alloc(m, &m->buf1, total);
+  if (e != hipSuccess) {
     m->buf1 = nullptr;
+    (void)hipGetLastError();
     return psa_set_error(PSA_ERR_ALLOC, "device allocation of the tile map failed");
   }
   char* b = static_cast<char*>(m->buf1);
@@ -82,48 +141,46 @@ psa_status alloc_phase1(psa_tile_map* m, size_t* info_off, size_t* scratch_off,
   m->kinds = reinterpret_cast<uint8_t*>(b + o_kinds);
   m->row_ptr = reinterpret_cast<int32_t*>(b + o_rp);
   m->col_ptr = reinterpret_cast<int32_t*>(b + o_cp);
-  *scratch_off = o_kmin;
-  (void)o_kmax;
-  *info_off = o_info;
-  *flag_off = o_flag;
+  ph->scratch = reinterpret_cast<int32_t*>(b + o_scr);
+  ph->tok_scratch = reinterpret_cast<int32_t*>(b + o_tok);
+  ph->info = reinterpret_cast<int64_t*>(b + o_info);
+  ph->readback_bytes = o_cp + size_t(m->nk + 1) * 4 - o_info;
+  e = launch_map_init(m->nk, m->row_ptr, m->col_ptr, ph->info, m->stream);
+  if (e != hipSuccess) return psa_hip_error(e, "tile map init launch");
   return PSA_OK;
 }
 
-psa_status finish_build(psa_tile_map* m, size_t info_off, size_t scratch_off, size_t flag_off,
-                        bool check_flag, psa_tile_map** out) {
-  char* b = static_cast<char*>(m->buf1);
-  int32_t* kmin = reinterpret_cast<int32_t*>(b + scratch_off);
-  int32_t* kmax = kmin + align_up(std::max<int64_t>(m->nk, 1) * 4, 256) / 4;
-  int64_t* info = reinterpret_cast<int64_t*>(b + info_off);
-  int32_t* flag = reinterpret_cast<int32_t*>(b + flag_off);
+psa_status finish_build(psa_tile_map* m, const Phase1& ph, psa_tile_map** out) {
+  int32_t* kmin = ph.scratch;
+  int32_t* kmax = ph.scratch + align_up(std::max<int64_t>(m->nk, 1), 64);
   hipError_t e = launch_classify(m->T, m->bm, m->bn, m->nq, m->nk, m->end, m->kinds,
-                                 m->row_ptr, m->col_ptr, kmin, kmax, info, m->stream);
+                                 m->row_ptr, m->col_ptr, kmin, kmax, ph.info, m->stream);
   if (e != hipSuccess) return psa_hip_error(e, "tile classification launch");
 
-  // one wait: info, flag and both pointer arrays come back together
-  std::vector<int64_t> info_h(8, 0);
-  int32_t flag_h[4] = {0, 0, 0, 0};
-  std::vector<int32_t> rp_h(m->nq + 1), cp_h(m->nk + 1);
-  if ((e = hipMemcpyAsync(info_h.data(), info, 8 * sizeof(int64_t), hipMemcpyDeviceToHost,
-                          m->stream)) != hipSuccess ||
-      (e = hipMemcpyAsync(flag_h, flag, sizeof(flag_h), hipMemcpyDeviceToHost, m->stream)) !=
+  // the one wait: info and both pointer arrays come back in one copy
+  std::vector<char> rb(ph.readback_bytes);
+  if ((e = hipMemcpyAsync(rb.data(), ph.info, rb.size(), hipMemcpyDeviceToHost, m->stream)) !=
           hipSuccess ||
-      (e = hipMemcpyAsync(rp_h.data(), m->row_ptr, rp_h.size() * 4, hipMemcpyDeviceToHost,
-                          m->stream)) != hipSuccess ||
-      (e = hipMemcpyAsync(cp_h.data(), m->col_ptr, cp_h.size() * 4, hipMemcpyDeviceToHost,
-                          m->stream)) != hipSuccess ||
       (e = hipStreamSynchronize(m->stream)) != hipSuccess)
     return psa_hip_error(e, "tile map readback");
-  if (check_flag && flag_h[0] != 0) {
+  const int64_t* info_h = reinterpret_cast<const int64_t*>(rb.data());
+  const char* rp_at = rb.data() + (reinterpret_cast<char*>(m->row_ptr) -
+                                   reinterpret_cast<char*>(ph.info));
+  const char* cp_at = rb.data() + (reinterpret_cast<char*>(m->col_ptr) -
+                                   reinterpret_cast<char*>(ph.info));
+  const int32_t* rp_h = reinterpret_cast<const int32_t*>(rp_at);
+  const int32_t* cp_h = reinterpret_cast<const int32_t*>(cp_at);
+  if (info_h[3] != -1) {
     static const char* why[] = {
         "",
         "group ids decrease along the sequence (groups must be contiguous, ascending runs)",
         "a group is split by pad tokens",
         "a prompt token follows a completion token of the same group",
         "completion ids decrease within a group (completions must be contiguous runs)"};
-    int code = flag_h[0] >= 1 && flag_h[0] <= 4 ? flag_h[0] : 0;
+    const uint64_t word = uint64_t(info_h[3]);
+    const int code = int(word & 7) >= 1 && int(word & 7) <= 4 ? int(word & 7) : 0;
     return psa_set_error(PSA_ERR_LAYOUT, std::string("token layout rejected at position ") +
-                                             std::to_string(flag_h[1] - 1) + ": " + why[code]);
+                                             std::to_string(word >> 3) + ": " + why[code]);
   }
   m->nnz = info_h[0];
   m->n_full = info_h[1];
@@ -134,10 +191,10 @@ psa_status finish_build(psa_tile_map* m, size_t info_off, size_t scratch_off, si
   size_t o_kind = c.take<uint8_t>(std::max<int64_t>(m->nnz, 1));
   size_t o_row = c.take<int32_t>(std::max<int64_t>(m->nnz, 1));
   size_t o_kc = c.take<uint8_t>(std::max<int64_t>(m->nnz, 1));
-  size_t o_qo = c.take<int32_t>(std::max<int64_t>(m->nq, 1));
-  size_t o_ko = c.take<int32_t>(std::max<int64_t>(m->nk, 1));
-  if ((e = hipMalloc(&m->buf2, c.off)) != hipSuccess) {
+  size_t o_qo = c.take<int32_t>(std::max<int64_t>(m->nq + m->nk, 1));  // qorder | korder
+  if ((e = map_alloc(m, &m->buf2, c.off)) != hipSuccess) {
     m->buf2 = nullptr;
+    (void)hipGetLastError();
     return psa_set_error(PSA_ERR_ALLOC, "device allocation of the tile lists failed");
   }
   char* b2 = static_cast<char*>(m->buf2);
@@ -146,7 +203,7 @@ psa_status finish_build(psa_tile_map* m, size_t info_off, size_t scratch_off, si
   m->row = reinterpret_cast<int32_t*>(b2 + o_row);
   m->kind_csc = reinterpret_cast<uint8_t*>(b2 + o_kc);
   m->qorder = reinterpret_cast<int32_t*>(b2 + o_qo);
-  m->korder = reinterpret_cast<int32_t*>(b2 + o_ko);
+  m->korder = m->qorder + m->nq;
 
   if (m->nnz > 0) {
     e = launch_fill_lists(m->nq, m->nk, m->kinds, m->row_ptr, m->col_ptr, m->col, m->kind,
@@ -157,9 +214,7 @@ psa_status finish_build(psa_tile_map* m, size_t info_off, size_t scratch_off, si
   length_order(rp_h, m->nq, m->host_orders.data());
   length_order(cp_h, m->nk, m->host_orders.data() + m->nq);
   if (m->nq > 0) {
-    if ((e = hipMemcpyAsync(m->qorder, m->host_orders.data(), m->nq * 4, hipMemcpyHostToDevice,
-                            m->stream)) != hipSuccess ||
-        (e = hipMemcpyAsync(m->korder, m->host_orders.data() + m->nq, m->nk * 4,
+    if ((e = hipMemcpyAsync(m->qorder, m->host_orders.data(), (m->nq + m->nk) * 4,
                             hipMemcpyHostToDevice, m->stream)) != hipSuccess)
       return psa_hip_error(e, "tile order upload");
   }
@@ -263,18 +318,18 @@ psa_status psa_build_tile_map_tokens(int64_t T, const int32_t* group, const int3
     free_map(m);
     return psa_hip_error(e, "hipGetDevice");
   }
-  size_t info_off, scratch_off, flag_off;
-  if ((st = alloc_phase1(m, &info_off, &scratch_off, &flag_off)) != PSA_OK) {
+  Phase1 ph;
+  if ((st = alloc_phase1(m, &ph)) != PSA_OK) {
     free_map(m);
     return st;
   }
-  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(m->buf1) + flag_off);
-  e = launch_tokens_end(T, group, suffix, is_prefix, m->end, flag, m->stream);
+  e = launch_tokens_end(T, group, suffix, is_prefix, m->end, ph.tok_scratch, ph.info,
+                        m->stream);
   if (e != hipSuccess) {
     free_map(m);
     return psa_hip_error(e, "label scan launch");
   }
-  st = finish_build(m, info_off, scratch_off, flag_off, true, out);
+  st = finish_build(m, ph, out);
   if (st != PSA_OK) free_map(m);
   return st;
 }
@@ -355,20 +410,21 @@ psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
     free_map(m);
     return psa_hip_error(e, "hipGetDevice");
   }
-  size_t info_off, scratch_off, flag_off;
-  if ((st = alloc_phase1(m, &info_off, &scratch_off, &flag_off)) != PSA_OK) {
+  Phase1 ph;
+  if ((st = alloc_phase1(m, &ph)) != PSA_OK) {
     free_map(m);
     return st;
   }
   void* d_table = nullptr;
   if (n_nodes > 0) {
-    if ((e = hipMalloc(&d_table, table.size() * sizeof(int64_t))) != hipSuccess) {
+    if ((e = map_alloc(m, &d_table, table.size() * sizeof(int64_t))) != hipSuccess) {
+      (void)hipGetLastError();
       free_map(m);
       return psa_set_error(PSA_ERR_ALLOC, "device allocation of the node table failed");
     }
     if ((e = hipMemcpyAsync(d_table, table.data(), table.size() * sizeof(int64_t),
                             hipMemcpyHostToDevice, m->stream)) != hipSuccess) {
-      (void)hipFree(d_table);
+      map_free(m, d_table);
       free_map(m);
       return psa_hip_error(e, "node table upload");
     }
@@ -376,13 +432,12 @@ psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
   const int64_t* dt = static_cast<const int64_t*>(d_table);
   e = launch_tree_end(T, n_nodes, dt, dt ? dt + n_nodes : nullptr, start[n_nodes], m->end,
                       m->stream);
+  map_free(m, d_table);  // stream-ordered after the launch (or the plain free's wait)
   if (e != hipSuccess) {
-    if (d_table) (void)hipFree(d_table);
     free_map(m);
     return psa_hip_error(e, "tree expansion launch");
   }
-  st = finish_build(m, info_off, scratch_off, flag_off, false, out);
-  if (d_table) (void)hipFree(d_table);  // finish_build waited on the stream
+  st = finish_build(m, ph, out);
   if (st != PSA_OK) free_map(m);
   return st;
 }

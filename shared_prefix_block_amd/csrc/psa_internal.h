@@ -17,7 +17,8 @@ struct psa_tile_map {
   int64_t nq = 0, nk = 0;
   int64_t nnz = 0, n_full = 0, n_partial = 0;
   int device = 0;
-  hipStream_t stream = nullptr;  // build stream (export waits on it)
+  hipStream_t stream = nullptr;  // build stream (export waits on it; buffers freed on it)
+  bool pooled = false;           // buffers from the library's stream-ordered pool
 
   // phase-1 allocation (sized before the sync)
   void* buf1 = nullptr;
@@ -43,17 +44,21 @@ psa_status psa_hip_error(hipError_t e, const char* what);
 // ---------------------------------------------------------------------------
 // tilemap.hip
 // ---------------------------------------------------------------------------
-// Per-token interval ends from labels; flag[0] receives a nonzero layout-error code
-// (the first offending position + 1 in flag[1]).
+// Zero the pointer arrays' counts and info (info[3], the first layout error, = -1).
+hipError_t launch_map_init(int64_t nk, int32_t* row_ptr, int32_t* col_ptr, int64_t* info,
+                           hipStream_t stream);
+// Per-token interval ends from labels.  info[3] receives the first layout error as
+// position * 8 + code (codes 1..4), or stays -1.  scratch: tokens_scratch_ints(T) ints.
+int64_t tokens_scratch_ints(int64_t T);
 hipError_t launch_tokens_end(int64_t T, const int32_t* group, const int32_t* suffix,
-                             const uint8_t* is_prefix, int32_t* end, int32_t* flag,
-                             hipStream_t stream);
+                             const uint8_t* is_prefix, int32_t* end, int32_t* scratch,
+                             int64_t* info, hipStream_t stream);
 // Per-token interval ends from a per-node table (node token start, node subtree end).
 hipError_t launch_tree_end(int64_t T, int64_t n_nodes, const int64_t* node_start,
                            const int64_t* node_subtree_end, int64_t t_real, int32_t* end,
                            hipStream_t stream);
-// Classification + counts + pointer scans.  info (device, 8 x int64) receives
-// nnz, n_full, n_partial.
+// Classification + counts + pointer scans (after launch_map_init).  info (device,
+// 8 x int64) receives nnz, n_full, n_partial.
 hipError_t launch_classify(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk,
                            const int32_t* end, uint8_t* kinds, int32_t* row_ptr,
                            int32_t* col_ptr, int32_t* ktile_min_end, int32_t* ktile_max_end,

@@ -25,8 +25,6 @@
 namespace {
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 4;
-constexpr int kChunk = kScanThreads * kScanItems;
 
 // Inclusive scan over the 1024 threads of a block (Hillis-Steele in LDS), each
 // thread sitting at position `slot` (a permutation of the thread ids).  On return
@@ -46,119 +44,153 @@ __device__ T scan_slot(T v, int slot, T* sh, Op op) {
   return v;
 }
 
-struct MaxOp {
-  __device__ long long operator()(long long a, long long b) const { return a > b ? a : b; }
-};
-struct MinOp {
-  __device__ long long operator()(long long a, long long b) const { return a < b ? a : b; }
-};
 struct AddOp {
   __device__ long long operator()(long long a, long long b) const { return a + b; }
 };
 
 // ---------------------------------------------------------------------------
-// Step 1a: labels -> end[], with the layout checks.  One block, chunked scans.
-// flag[0] = error code (0 ok), flag[1] = first offending position + 1.
+// Step 1a: labels -> end[], with the layout checks, in two passes over chunks of
+// kTokChunk tokens (one block each).  A "group break" at e (0 < e <= T) means tokens
+// e-1 and e are not of the same group (or either is a pad, or e = T); a "run break"
+// is a group break or a change of completion.  end[t] is the first group break after
+// t for a prompt token, the first run break after t for a completion token, and t for
+// a pad.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kScanThreads) void k_tokens_end(
+constexpr int kTokThreads = 256;
+constexpr int kTokItems = 4;
+constexpr int kTokChunk = kTokThreads * kTokItems;
+constexpr int32_t kNone = INT_MAX;
+
+__device__ inline bool group_break(int64_t T, const int32_t* group, int64_t e) {
+  if (e >= T) return true;
+  const int32_t a = group[e - 1], b = group[e];
+  return a < 0 || b < 0 || a != b;
+}
+__device__ inline bool run_break(int64_t T, const int32_t* group, const int32_t* suffix,
+                                 const uint8_t* is_prefix, int64_t e) {
+  return group_break(T, group, e) || is_prefix[e] != is_prefix[e - 1] ||
+         suffix[e] != suffix[e - 1];
+}
+
+// Minimum of v over the threads of the block with a larger thread id (kNone if none).
+__device__ inline int32_t block_min_after(int32_t v, int32_t* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t x = v;  // inclusive minimum over lanes >= lane of this wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_down(x, off);
+    if (lane + off < 64) x = y < x ? y : x;
+  }
+  const int32_t nxt = __shfl_down(x, 1);  // every lane takes part in the shuffle
+  const int32_t after_in_wave = lane < 63 ? nxt : kNone;
+  if (lane == 0) sh[w] = x;
+  __syncthreads();
+  int32_t r = after_in_wave;
+  for (int k = w + 1; k < kTokThreads / 64; ++k) r = sh[k] < r ? sh[k] : r;
+  __syncthreads();
+  return r;
+}
+
+// Pass 1: layout checks (the first offending position and its code, atomically
+// minimised into *err as position * 8 + code) and, per chunk, its first group break
+// and first run break (kNone if none).
+__global__ __launch_bounds__(kTokThreads) void k_tokens_check(
     int64_t T, const int32_t* __restrict__ group, const int32_t* __restrict__ suffix,
-    const uint8_t* __restrict__ is_prefix, int32_t* __restrict__ end, int32_t* flag) {
-  __shared__ long long sh[kScanThreads];
-  const int tid = threadIdx.x;
-  const int rt = kScanThreads - 1 - tid;  // reversed slot for suffix scans
-
-  // Forward pass: pr = last real index before t; layout checks.
-  long long carry_prev = -1;
-  for (int64_t c0 = 0; c0 < T; c0 += kChunk) {
-    const int64_t t0 = c0 + int64_t(tid) * kScanItems;
-    long long local_last = -1;
-    for (int i = 0; i < kScanItems; ++i) {
-      int64_t t = t0 + i;
-      if (t < T && group[t] >= 0) local_last = t;
-    }
-    __syncthreads();
-    scan_slot(local_last, tid, sh, MaxOp());
-    long long excl = tid > 0 ? sh[tid - 1] : -1;
-    const long long chunk_max = sh[kScanThreads - 1];
-    __syncthreads();
-    long long pr = excl > carry_prev ? excl : carry_prev;
-    long long err = LLONG_MAX;  // position * 8 + code
-    for (int i = 0; i < kScanItems; ++i) {
-      int64_t t = t0 + i;
-      if (t >= T) break;
-      int32_t g = group[t];
-      if (g < 0) continue;
+    const uint8_t* __restrict__ is_prefix, int32_t* first_g, int32_t* first_r,
+    unsigned long long* err) {
+  __shared__ int32_t sh[kTokThreads / 64];
+  const int64_t t0 = int64_t(blockIdx.x) * kTokChunk + int64_t(threadIdx.x) * kTokItems;
+  unsigned long long my_err = ~0ull;
+  int32_t fg = kNone, fr = kNone;
+  for (int i = 0; i < kTokItems; ++i) {
+    const int64_t t = t0 + i;
+    if (t >= T) break;
+    const int32_t g = group[t];
+    if (g >= 0 && t > 0 && my_err == ~0ull) {
       int code = 0;
-      if (pr >= 0) {
-        int32_t gp = group[pr];
-        if (g < gp) code = 1;
-        else if (g == gp && pr != t - 1) code = 2;
+      const int32_t gp = group[t - 1];
+      if (gp >= 0) {
+        if (g < gp) {
+          code = 1;
+        } else if (g == gp) {  // the same group continues
+          const bool pf = is_prefix[t] != 0, ppf = is_prefix[t - 1] != 0;
+          if (pf && !ppf) code = 3;
+          else if (!pf && !ppf && suffix[t] < suffix[t - 1]) code = 4;
+        }
+      } else {  // after a pad run: compare with the last real token before it
+        int64_t pr = t - 2;
+        while (pr >= 0 && group[pr] < 0) --pr;
+        if (pr >= 0) {
+          const int32_t gr = group[pr];
+          if (g < gr) code = 1;
+          else if (g == gr) code = 2;
+        }
       }
-      if (code == 0 && t > 0 && group[t - 1] == g) {  // the same group continues
-        bool p = is_prefix[t] != 0, pp = is_prefix[t - 1] != 0;
-        if (p && !pp) code = 3;
-        else if (!p && !pp && suffix[t] < suffix[t - 1]) code = 4;
-      }
-      if (code && err == LLONG_MAX) err = (long long)t * 8 + code;
-      pr = t;
+      if (code) my_err = (unsigned long long)t * 8 + code;
     }
-    scan_slot(err, tid, sh, MinOp());
-    const long long first_err = sh[kScanThreads - 1];
-    __syncthreads();
-    if (first_err != LLONG_MAX) {  // uniform branch: every thread read the same value
-      if (tid == 0) {
-        flag[0] = int32_t(first_err & 7);
-        flag[1] = int32_t(first_err >> 3) + 1;
-      }
-      return;
-    }
-    if (chunk_max > carry_prev) carry_prev = chunk_max;
+    const int64_t e = t + 1;  // break between t and t + 1 ?
+    if (fg == kNone && group_break(T, group, e)) fg = int32_t(e);
+    if (fr == kNone && run_break(T, group, suffix, is_prefix, e)) fr = int32_t(e);
   }
-  if (tid == 0) {
-    flag[0] = 0;
-    flag[1] = 0;
+  if (my_err != ~0ull) atomicMin(err, my_err);
+  // the chunk's first breaks: the minimum over its threads
+  const int32_t g_after = block_min_after(fg, sh);
+  const int32_t r_after = block_min_after(fr, sh);
+  if (threadIdx.x == 0) {
+    first_g[blockIdx.x] = fg < g_after ? fg : g_after;
+    first_r[blockIdx.x] = fr < r_after ? fr : r_after;
   }
+}
 
-  // Backward pass: first group break / completion break after each t.
-  long long carry_g = T, carry_s = T;
-  const int64_t n_chunks = (T + kChunk - 1) / kChunk;
-  for (int64_t c = n_chunks - 1; c >= 0; --c) {
-    const int64_t t0 = c * kChunk + int64_t(tid) * kScanItems;
-    bool gb[kScanItems], sb[kScanItems];
-    long long lg = LLONG_MAX, ls = LLONG_MAX;  // first break position in this thread
-    for (int i = 0; i < kScanItems; ++i) {
-      const int64_t t = t0 + i, e = t + 1;  // break between t and t+1 ?
-      gb[i] = sb[i] = false;
-      if (t >= T) continue;
-      if (e >= T) {
-        gb[i] = sb[i] = true;
-      } else {
-        const int32_t ge = group[e], gt = group[t];
-        gb[i] = ge < 0 || gt < 0 || ge != gt;
-        sb[i] = gb[i] || is_prefix[e] != is_prefix[t] || suffix[e] != suffix[t];
+// First break at or after chunk c + 1 (T if none): wave 0 scans 64 chunks at a time.
+__device__ inline int32_t next_break(const int32_t* first, int64_t c, int64_t n_chunks,
+                                     int64_t T, int32_t* sh) {
+  if (threadIdx.x < 64) {
+    int32_t found = kNone;
+    for (int64_t c0 = c + 1; c0 < n_chunks && found == kNone; c0 += 64) {
+      const int64_t cc = c0 + threadIdx.x;
+      int32_t v = cc < n_chunks ? first[cc] : kNone;
+      for (int off = 32; off >= 1; off >>= 1) {
+        const int32_t y = __shfl_xor(v, off);
+        v = y < v ? y : v;
       }
-      if (gb[i] && lg == LLONG_MAX) lg = e;
-      if (sb[i] && ls == LLONG_MAX) ls = e;
+      found = v;  // wave-uniform
     }
-    __syncthreads();
-    scan_slot(lg, rt, sh, MinOp());
-    long long after_g = rt > 0 ? sh[rt - 1] : LLONG_MAX;  // threads with larger tid
-    const long long all_g = sh[kScanThreads - 1];
-    __syncthreads();
-    scan_slot(ls, rt, sh, MinOp());
-    long long after_s = rt > 0 ? sh[rt - 1] : LLONG_MAX;
-    const long long all_s = sh[kScanThreads - 1];
-    long long ng = after_g < carry_g ? after_g : carry_g;
-    long long ns = after_s < carry_s ? after_s : carry_s;
-    for (int i = kScanItems - 1; i >= 0; --i) {
-      const int64_t t = t0 + i;
-      if (t >= T) continue;
-      if (gb[i]) ng = t + 1;
-      if (sb[i]) ns = t + 1;
-      end[t] = group[t] < 0 ? int32_t(t) : int32_t(is_prefix[t] ? ng : ns);
-    }
-    if (all_g < carry_g) carry_g = all_g;
-    if (all_s < carry_s) carry_s = all_s;
+    if (threadIdx.x == 0) sh[0] = found == kNone ? int32_t(T) : found;
+  }
+  __syncthreads();
+  const int32_t r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+// Pass 2: end[] per chunk, from the breaks inside the chunk and the first ones after.
+__global__ __launch_bounds__(kTokThreads) void k_tokens_end(
+    int64_t T, const int32_t* __restrict__ group, const int32_t* __restrict__ suffix,
+    const uint8_t* __restrict__ is_prefix, const int32_t* __restrict__ first_g,
+    const int32_t* __restrict__ first_r, int32_t* __restrict__ end) {
+  __shared__ int32_t sh[kTokThreads / 64];
+  const int64_t c = blockIdx.x, n_chunks = gridDim.x;
+  const int64_t t0 = c * kTokChunk + int64_t(threadIdx.x) * kTokItems;
+  bool gb[kTokItems], rb[kTokItems];
+  int32_t fg = kNone, fr = kNone;
+  for (int i = 0; i < kTokItems; ++i) {
+    const int64_t t = t0 + i, e = t + 1;
+    gb[i] = t < T && group_break(T, group, e);
+    rb[i] = t < T && run_break(T, group, suffix, is_prefix, e);
+    if (fg == kNone && gb[i]) fg = int32_t(e);
+    if (fr == kNone && rb[i]) fr = int32_t(e);
+  }
+  const int32_t later_g = next_break(first_g, c, n_chunks, T, sh);
+  const int32_t later_r = next_break(first_r, c, n_chunks, T, sh);
+  int32_t ng = block_min_after(fg, sh), nr = block_min_after(fr, sh);
+  ng = later_g < ng ? later_g : ng;
+  nr = later_r < nr ? later_r : nr;
+  for (int i = kTokItems - 1; i >= 0; --i) {
+    const int64_t t = t0 + i;
+    if (t >= T) continue;
+    if (gb[i]) ng = int32_t(t + 1);
+    if (rb[i]) nr = int32_t(t + 1);
+    end[t] = group[t] < 0 ? int32_t(t) : (is_prefix[t] ? ng : nr);
   }
 }
 
@@ -186,9 +218,10 @@ __global__ void k_tree_end(int64_t T, int64_t n_nodes, const int64_t* __restrict
 // ---------------------------------------------------------------------------
 // Step 2: classification
 // ---------------------------------------------------------------------------
+// info[0..2] = nnz, n_full, n_partial; info[3] = first layout error (all ones: none).
 __global__ void k_map_init(int64_t nk, int32_t* row_ptr, int32_t* col_ptr, int64_t* info) {
   for (int64_t j = threadIdx.x; j <= nk; j += blockDim.x) col_ptr[j] = 0;
-  if (threadIdx.x < 8) info[threadIdx.x] = 0;
+  if (threadIdx.x < 8) info[threadIdx.x] = threadIdx.x == 3 ? -1 : 0;
   if (threadIdx.x == 0) row_ptr[0] = 0;
 }
 
@@ -370,11 +403,26 @@ __global__ __launch_bounds__(kFillThreads) void k_fill_csc(int64_t nq, int64_t n
 
 }  // namespace
 
+hipError_t launch_map_init(int64_t nk, int32_t* row_ptr, int32_t* col_ptr, int64_t* info,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(k_map_init, dim3(1), dim3(1024), 0, stream, nk, row_ptr, col_ptr, info);
+  return hipGetLastError();
+}
+
+int64_t tokens_scratch_ints(int64_t T) { return 2 * ((T + kTokChunk - 1) / kTokChunk); }
+
 hipError_t launch_tokens_end(int64_t T, const int32_t* group, const int32_t* suffix,
-                             const uint8_t* is_prefix, int32_t* end, int32_t* flag,
-                             hipStream_t stream) {
-  hipLaunchKernelGGL(k_tokens_end, dim3(1), dim3(kScanThreads), 0, stream, T, group, suffix,
-                     is_prefix, end, flag);
+                             const uint8_t* is_prefix, int32_t* end, int32_t* scratch,
+                             int64_t* info, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int64_t n_chunks = (T + kTokChunk - 1) / kTokChunk;
+  int32_t* first_g = scratch;
+  int32_t* first_r = scratch + n_chunks;
+  unsigned long long* err = reinterpret_cast<unsigned long long*>(info + 3);
+  hipLaunchKernelGGL(k_tokens_check, dim3(unsigned(n_chunks)), dim3(kTokThreads), 0, stream, T,
+                     group, suffix, is_prefix, first_g, first_r, err);
+  hipLaunchKernelGGL(k_tokens_end, dim3(unsigned(n_chunks)), dim3(kTokThreads), 0, stream, T,
+                     group, suffix, is_prefix, first_g, first_r, end);
   return hipGetLastError();
 }
 
@@ -393,7 +441,6 @@ hipError_t launch_classify(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_
                            const int32_t* end, uint8_t* kinds, int32_t* row_ptr,
                            int32_t* col_ptr, int32_t* kmin, int32_t* kmax, int64_t* info,
                            hipStream_t stream) {
-  hipLaunchKernelGGL(k_map_init, dim3(1), dim3(1024), 0, stream, nk, row_ptr, col_ptr, info);
   if (nk > 0) {
     hipLaunchKernelGGL(k_ktile_summary, dim3(unsigned(nk)), dim3(64), 0, stream, T, bn, nk, end,
                        kmin, kmax);
