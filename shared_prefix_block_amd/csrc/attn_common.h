@@ -31,6 +31,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct bf16_t {  // raw bfloat16 storage
   uint16_t bits;
@@ -166,6 +167,14 @@ __device__ __forceinline__ bool visible_u(int q_minus_kv, int reach) {
 // waits on the vector loads in flight (a byte load would be a vector load).
 __device__ __forceinline__ int tile_kind(const uint8_t* kinds, int e) {
   const uint32_t w = reinterpret_cast<const uint32_t*>(kinds)[e >> 2];
+  return int((w >> (8 * (e & 3))) & 0xffu);
+}
+// The same in two halves, for reading a sub-step ahead: the dword holding entry e,
+// and the kind extracted from it when it is needed.
+__device__ __forceinline__ uint32_t tile_kind_word(const uint8_t* kinds, int e) {
+  return reinterpret_cast<const uint32_t*>(kinds)[e >> 2];
+}
+__device__ __forceinline__ int kind_from_word(uint32_t w, int e) {
   return int((w >> (8 * (e & 3))) & 0xffu);
 }
 
@@ -373,6 +382,133 @@ struct RowStage {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Swizzled bf16 tiles filled by direct-to-LDS buffer loads.
+//
+// A tile of R rows x D bf16 is stored row-major without padding; the 16-byte chunk c
+// of row r sits at chunk slot c ^ swz(r).  The swizzle spreads the rows that one
+// LDS pass serves over distinct bank groups, both for fragment reads along a row
+// (ds_read_b128: 16 consecutive rows, one chunk each) and for transposed reads
+// (ds_read_b64_tr_b16: 4 consecutive rows, 4 consecutive chunks each), which row
+// padding would otherwise do.
+// The tile is written by buffer_load_dwordx4 ... lds: each lane of a wave fetches
+// 16 bytes from global memory and the hardware stores lane i at LDS base + 16 i, so
+// lane i is given the global chunk whose swizzled slot is i.  Rows past `nvalid`
+// are outside the buffer resource and come in as zeros.  The loads bypass the
+// registers; the caller waits for them (vmcnt) before the barrier that publishes
+// the tile.
+// ---------------------------------------------------------------------------
+template <int NC>
+__device__ __forceinline__ int swz(int r) {
+  return NC >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void* to_lds(void* p) { return (lds_void*)p; }
+
+// Direct-to-LDS buffer loads, written as inline assembly: the compiler's wait-count
+// pass does not model them, so it cannot add conservative vmcnt waits in front of
+// unrelated LDS reads (it does so for the transposed reads, which carry no memory
+// operand).  The caller waits for them with wait_vmcnt before the barrier that
+// publishes the data; other vector loads only ever wait longer because of them.
+// The descriptor and the LDS address are made wave-uniform explicitly (SGPR operands).
+struct DmaRsrc {
+  u32x4 d;
+};
+__device__ __forceinline__ DmaRsrc dma_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  DmaRsrc r;
+  r.d = u32x4{uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a))),
+              uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xffffu)),
+              uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(bytes))), uint32_t(kBufWord3)};
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_addr_u(void* p) {
+  return uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(to_lds(p)))));
+}
+// 16 bytes per lane from byte offset voff of the buffer; lane i lands at dst + 16 i.
+__device__ __forceinline__ void dma_load16(const DmaRsrc& r, int voff, void* dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r.d), "s"(lds_addr_u(dst))
+               : "memory");
+}
+// 4 bytes per lane; lane i lands at dst + 4 i.
+__device__ __forceinline__ void dma_load4(const DmaRsrc& r, int voff, void* dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r.d), "s"(lds_addr_u(dst))
+               : "memory");
+}
+
+template <int R, int D, int NT>
+struct DmaTile {
+  static constexpr int NC = D / 8;  // 16-byte chunks per row
+  static constexpr int NW = NT / 64;
+  static constexpr int N = R * NC / NT;  // wave loads per tile
+  static constexpr int BYTES = R * D * 2;
+  static_assert((R * NC) % NT == 0, "tile must split evenly over the waves");
+  int voff[N];  // global byte offset (relative to the tile's first row) of each load
+  __device__ __forceinline__ void init(int pitch_bytes) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int k = (j * NW + w) * 64 + lane;  // chunk slot this lane fills
+      const int r = k / NC, c = (k % NC) ^ swz<NC>(r);
+      voff[j] = r * pitch_bytes + c * 16;
+    }
+  }
+  // Enqueue the loads of rows [0, nvalid) of the tile at `src` into LDS at `dst`.
+  __device__ __forceinline__ void load(const void* src, int nvalid, int pitch_bytes,
+                                       char* dst) const {
+    const DmaRsrc rs = dma_rsrc(src, nvalid * pitch_bytes);
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < N; ++j) dma_load16(rs, voff[j], dst + (j * NW + w) * 1024);
+  }
+};
+
+// Byte offset of (row r, 16-byte chunk c) inside a swizzled tile with NC chunks a row.
+template <int NC>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  return r * NC * 16 + ((c ^ swz<NC>(r)) << 4);
+}
+
+// frag_load from a swizzled tile: 8 bf16 at row r, chunk c.
+template <int NC>
+__device__ __forceinline__ Frag<bf16_t> frag_load_swz(const char* tile, int r, int c) {
+  Frag<bf16_t> f;
+  f.v = *reinterpret_cast<const u32x4*>(tile + swz_off<NC>(r, c));
+  return f;
+}
+
+// frag_load_tr (same lane mapping) from a swizzled tile; col0 is a multiple of 32.
+template <int NC>
+__device__ __forceinline__ Frag<bf16_t> frag_load_tr_swz(const char* tile, int row0, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int s16 = lane & 15, g16 = lane >> 4, h = lane >> 5;
+  const int row = row0 + 4 * h + (s16 >> 2);
+  const int chunk = (col0 >> 3) + (g16 & 1) * 2 + ((s16 & 3) >> 1);
+  const int byte = (s16 & 1) * 8;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const lds_i16x4* p0 = (const lds_i16x4*)(tile + swz_off<NC>(row, chunk) + byte);
+  const lds_i16x4* p1 = (const lds_i16x4*)(tile + swz_off<NC>(row + 8, chunk) + byte);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p1));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  Frag<bf16_t> f;
+  f.v = u32x4{ua[0], ua[1], ub[0], ub[1]};
+  return f;
+}
+
+// s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Transposed + row-permuted (see stage_rows_t), for operands whose element type has
 // no LDS transpose read (fp32).
 template <typename T, int R, int D, int S, int NT>
@@ -415,7 +551,6 @@ struct TransStage {
 // ds_read_b64_tr_b16: within each 16-lane group, lane s addresses row (s / 4) and
 // columns 4 (s % 4) .. +3 of a 4-row x 16-column block, and the hardware hands lane
 // i the 4 rows of column i.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ Frag<bf16_t> frag_load_tr(const bf16_t* tile, int S, int row0,
                                                      int col0) {
   const int lane = threadIdx.x & 63;

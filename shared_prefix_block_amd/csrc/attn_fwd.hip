@@ -69,7 +69,12 @@ struct FwdCfg {
   static constexpr int K_ELEMS = BN * KS;
   static constexpr int V_ELEMS = kBf16 ? BN * VS : D * VS;
   static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * EB + 2 * BN * 4;
+  // bf16 tiles come in by direct-to-LDS loads into swizzled, unpadded tiles (two
+  // stages of K | V | end[]); fp32 tiles go through registers into padded tiles.
+  static constexpr bool kDma = kBf16;
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + BN * 4;
+  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * BN * 4;
   static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
 };
 
@@ -125,27 +130,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     if (left < kTileN) n_steps -= C::NSUB - int((left + C::BN - 1) / C::BN);
   }
 
+  // CSR entries (kv-tile index | kind << 30) of a 64-entry window in one register,
+  // lane i holding entry wbase + i; the loop reads them with readlane, so it issues
+  // no scalar loads and the wait counts below see only the tile loads.
+  int wbase = 0;
+  uint32_t wreg = 0;
+  auto window_load = [&](int base) {
+    wbase = base;
+    const int e = e0 + base + lane;
+    wreg = e < e1 ? uint32_t(p.col[e]) | (uint32_t(p.kind[e]) << 30) : 0u;
+  };
+  auto entry = [&](int n) {  // packed entry of sub-step n (inside the window)
+    return uint32_t(__builtin_amdgcn_readlane(int(wreg), n / C::NSUB - wbase));
+  };
+  window_load(0);
+  mark_ready(*reinterpret_cast<int32_t*>(&wreg));
+
   RowStage<T, C::BN, D, C::KS, C::NT> kst;
   using VStage = typename std::conditional<C::kBf16, RowStage<T, C::BN, D, C::VS, C::NT>,
                                            TransStage<T, C::BN, D, C::VS, C::NT>>::type;
   VStage vst;
+  DmaTile<C::BN, D, C::NT> dt;
+  const int pitch = int(ldk) * 2;
+  if constexpr (C::kDma) dt.init(pitch);
   int32_t e_reg = 0, kv_reg = 0;
 
-  auto issue = [&](int n) {  // global reads of sub-step n into registers
-    const int e = e0 + n / C::NSUB;
-    const int64_t kv0 = int64_t(p.col[e]) * kTileN + (n % C::NSUB) * C::BN;
+  auto issue = [&](int n, int col_n) {  // global reads of sub-step n
+    const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
-    // end[] first: the loads retire in order, so waiting for it at commit does not
-    // wait for the K/V reads issued after it
-    {  // every lane loads; a key past the end reads end = 0 and gets reach 0
+    if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | end[]
+      static_assert(C::BN == 64, "one end[] value per lane");
+      char* st = smem + (n & 1) * C::STAGE_BYTES;
+      dt.load(K + kv0 * ldk + koff, nvalid, pitch, st);
+      dt.load(V + kv0 * ldk + koff, nvalid, pitch, st + C::TILE_BYTES);
+      if (wave == 0)  // keys past the end read end = 0: never visible
+        dma_load4(dma_rsrc(p.end + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
+    } else {  // into registers; commit() stores them
+      // end[] first: the loads retire in order, so waiting for it at commit does not
+      // wait for the K/V reads issued after it
       const int r = int(threadIdx.x) & (C::BN - 1);
       e_reg = int32_t(buf_load4(buf_rsrc(p.end + kv0, nvalid * 4), r * 4));
       kv_reg = r < nvalid ? int32_t(kv0 + r) : 0;
+      kst.load(K + kv0 * ldk + koff, ldk, nvalid);
+      vst.load(V + kv0 * ldk + koff, ldk, nvalid);
     }
-    kst.load(K + kv0 * ldk + koff, ldk, nvalid);
-    vst.load(V + kv0 * ldk + koff, ldk, nvalid);
   };
-  auto commit = [&](int b) {  // registers -> LDS buffer b
+  auto commit = [&](int b) {  // registers -> LDS buffer b (register path)
     T* kb = buf0 + b * C::BUF_ELEMS;
     kst.store(kb);
     vst.store(kb + C::K_ELEMS);
@@ -153,33 +183,86 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   };
 
   if (n_steps > 0) {
-    issue(0);
-    commit(0);
+    issue(0, int(entry(0) & 0x3fffffffu));
+    if constexpr (!C::kDma) commit(0);
   }
-  __syncthreads();
+  if constexpr (!C::kDma) __syncthreads();
 
   for (int n = 0; n < n_steps; ++n) {
     const int b = n & 1;
-    const int e = e0 + n / C::NSUB;
-    const bool partial = tile_kind(p.kind, e) == 1;
-    const int kv0i = p.col[e] * kTileN + (n % C::NSUB) * C::BN;
-    if (n + 1 < n_steps) issue(n + 1);
+    if constexpr (C::kDma) {
+      // this wave's loads of stage n are in; after the barrier everyone's are, and
+      // every wave is done reading stage n - 1, which the next issue overwrites
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    const uint32_t ent = entry(n);
+    const bool partial = (ent >> 30) == 1;
+    const int kv0i = int(ent & 0x3fffffffu) * kTileN + (n % C::NSUB) * C::BN;
+    if (n + 1 < n_steps) {
+      if ((n + 1) / C::NSUB - wbase >= 64) {  // next window (a vector load; rare)
+        window_load((n + 1) / C::NSUB);
+        mark_ready(*reinterpret_cast<int32_t*>(&wreg));
+      }
+      issue(n + 1, int(entry(n + 1) & 0x3fffffffu));
+    }
 
-    const T* Ks = buf0 + b * C::BUF_ELEMS;
+    const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
+    const T* Ks = buf0 + b * C::BUF_ELEMS;       // register-path buffer
     const T* Vs = Ks + C::K_ELEMS;
-    const int32_t* Es = es0 + b * C::BN;
+    const int32_t* Es = C::kDma ? reinterpret_cast<const int32_t*>(st + 2 * C::TILE_BYTES)
+                                : es0 + b * C::BN;
 
     {
       // S^T = K Q^T for BN keys x 32 queries (this wave)
+      // (the BN/32 accumulation chains are interleaved so that consecutive MFMAs do
+      // not wait on each other's results)
       float sv[C::BN / 32][16];
+      {
+        f32x16 acc_s[C::BN / 32];
 #pragma unroll
-      for (int kb = 0; kb < C::BN / 32; ++kb) {
-        f32x16 acc_s = zero16();
-        const T* kr = Ks + (32 * kb + l32) * C::KS + 8 * half;
+        for (int kb = 0; kb < C::BN / 32; ++kb) acc_s[kb] = zero16();
+        const T* kr = Ks + l32 * C::KS + 8 * half;
+        if constexpr (C::kDma) {
+          // K fragments read PF reduction steps ahead of their MFMAs, so that LDS
+          // latency overlaps the MFMAs in flight
+          constexpr int NS = D / 16, NK = C::BN / 32, PF = 3;
+          Frag<T> kq[PF][NK];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) mma(acc_s, frag_load(kr + 16 * s), qf[s]);
+          for (int s = 0; s < PF - 1; ++s)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sv[kb][i] = acc_s[i];
+            for (int kb = 0; kb < NK; ++kb)
+              kq[s][kb] = frag_load_swz<D / 8>(st, 32 * kb + l32, half + 2 * s);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (s + PF - 1 < NS) {
+#pragma unroll
+              for (int kb = 0; kb < NK; ++kb)
+                kq[(s + PF - 1) % PF][kb] =
+                    frag_load_swz<D / 8>(st, 32 * kb + l32, half + 2 * (s + PF - 1));
+            }
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb) mma(acc_s[kb], kq[s % PF][kb], qf[s]);
+          }
+          // keep that order: the first PF-1 steps' reads, then per step the reads
+          // PF-1 steps ahead followed by this step's MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, (PF - 1) * NK, 0);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (s + PF - 1 < NS) __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+            for (int kb = 0; kb < C::BN / 32; ++kb)
+              mma(acc_s[kb], frag_load(kr + 32 * kb * C::KS + 16 * s), qf[s]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sv[kb][i] = acc_s[kb][i];
       }
       if (partial) {  // uniform branch; full tiles skip the mask
         const int qd = qrow_i - kv0i;  // q - kv for the sub-step's first key
@@ -191,9 +274,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
             const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
             const int rv[4] = {ev.x, ev.y, ev.z, ev.w};
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-              sv[kb][4 * g + u] =
-                  visible_u(qd - kvl - u, rv[u]) ? sv[kb][4 * g + u] : -INFINITY;
+            for (int u = 0; u < 4; ++u) {
+              bool keep;
+              if constexpr (C::kDma)  // raw end[]: kv <= q < end
+                keep = (kvl + u <= qd) && (qrow_i < rv[u]);
+              else  // reach = end - kv
+                keep = visible_u(qd - kvl - u, rv[u]);
+              sv[kb][4 * g + u] = keep ? sv[kb][4 * g + u] : -INFINITY;
+            }
           }
       }
       float mx = -INFINITY;
@@ -231,7 +319,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           Frag<T> va;
-          if constexpr (C::kBf16)
+          if constexpr (C::kDma)
+            va = frag_load_tr_swz<D / 8>(st + C::TILE_BYTES, 16 * t, 32 * db);
+          else if constexpr (C::kBf16)
             va = frag_load_tr(Vs, C::VS, 16 * t, 32 * db);
           else
             va = frag_load(Vs + (32 * db + l32) * C::VS + 16 * t + 8 * half);
@@ -240,10 +330,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       }
     }
 
-    if (n + 1 < n_steps) commit(b ^ 1);
-    __syncthreads();
+    if constexpr (!C::kDma) {
+      if (n + 1 < n_steps) commit(b ^ 1);
+      __syncthreads();
+    }
   }
 
+  if constexpr (C::kDma) wait_vmcnt<0>();  // no load into LDS outlives the work-group
   const float lt = l + __shfl_xor(l, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qvalid) {
