@@ -71,10 +71,11 @@ def describe(cfg, lay) -> str:
             f"hq={cfg.hq}/hkv={cfg.hkv}, d={cfg.d}, {cfg.dtype}")
 
 
-def cpu_baseline(cfg, lay, sample_seconds_hint=20.0):
-    """Time the float64 oracle on one group of the workload, all heads; scale to the
-    whole workload's effective FLOPs.  Returns the cpu_baseline dict."""
-    import numpy as np
+def cpu_baseline(cfg, lay, min_seconds=10.0):
+    """Time the float64 oracle on whole groups (trees) of the workload, all heads, one
+    after another until at least min_seconds of CPU work (or the whole workload) is
+    done; scale to the workload's effective FLOPs by the sample's share of the kept
+    pairs.  Groups never see each other, so a group is a self-contained slice."""
     from threadpoolctl import threadpool_info
 
     from oracle import attention as oa
@@ -82,27 +83,92 @@ def cpu_baseline(cfg, lay, sample_seconds_hint=20.0):
     from shared_prefix_block_amd import workloads as wl
 
     if lay.kind == "tokens":
-        p, rs = lay.specs[0]
-        sub = wl.tokens_layout([(p, rs)])
-        frac = kept_pairs(sub) / kept_pairs(lay)
-        what = f"group 0 of {len(lay.specs)} (T={sub.T}), all {cfg.hq} q heads"
+        parts = [wl.tokens_layout([spec]) for spec in lay.specs]
+        unit = "group"
     else:
-        nl = lay.node_lengths[:21]
-        sp = [pth for pth in lay.sample_paths if max(pth) < 21]
-        sub = wl.tree_layout(nl, sp)
-        frac = kept_pairs(sub) / kept_pairs(lay)
-        what = f"tree 0 of 8 (T={sub.T}), all {cfg.hq} q heads"
-    q, k, v, do = wl.make_tensors(sub.T, cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.sigma, cfg.idx)
-    meta = meta_from_layout(sub)
-    t0 = time.perf_counter()
-    if cfg.passes == "fwd":
-        oa.forward(meta, q, k, v)
-    else:
-        oa.backward(meta, q, k, v, do)
-    dt = time.perf_counter() - t0
+        per = 21  # root, 4 branches, 16 leaves
+        parts = []
+        for t in range(len(lay.node_lengths) // per):
+            nodes = set(range(per * t, per * t + per))
+            paths = [[n - per * t for n in pth] for pth in lay.sample_paths if pth[0] in nodes]
+            parts.append(wl.tree_layout(lay.node_lengths[per * t:per * t + per], paths))
+        unit = "tree"
+    done, pairs, dt = 0, 0, 0.0
+    for sub in parts:
+        q, k, v, do = wl.make_tensors(sub.T, cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.sigma,
+                                      cfg.idx)
+        meta = meta_from_layout(sub)
+        t0 = time.perf_counter()
+        if cfg.passes == "fwd":
+            oa.forward(meta, q, k, v)
+        else:
+            oa.backward(meta, q, k, v, do)
+        dt += time.perf_counter() - t0
+        done += 1
+        pairs += kept_pairs(sub)
+        if dt >= min_seconds:
+            break
+    frac = pairs / kept_pairs(lay)
+    what = f"{done} of {len(parts)} {unit}s (first {done}), all {cfg.hq} q heads"
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     return {"sample": what, "frac": frac, "seconds": dt, "cores": int(threads)}
+
+
+KERNEL_STAGE = {"fwd_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bwd_dq"}
+TRAFFIC_PASSES = ("FETCH_SIZE", "WRITE_SIZE")
+
+
+def traffic_summary(pmc_dir: str, config: int, calib_mb: int, command: str) -> None:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, each
+    with --calib-mb) into profiles/traffic_<stage>_config<N>.json, one per attention
+    kernel: the counters (KiB per dispatch) scaled so that the reference negation over
+    calib_mb MiB reads and writes exactly calib_mb MiB."""
+    import csv
+    import glob
+
+    def per_dispatch(counter):
+        vals = {}
+        for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    key = (r["Kernel_Name"], r["Dispatch_Id"])
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        by_kernel = {}
+        for (name, _), v in vals.items():
+            by_kernel.setdefault(name, []).append(v)
+        return {k: sum(v) / len(v) for k, v in by_kernel.items()}
+
+    out = {}
+    ref_kib = calib_mb * 1024.0
+    for counter in TRAFFIC_PASSES:
+        avg = per_dispatch(counter)
+        calib = [v for k, v in avg.items() if "elementwise_kernel" in k and v > 0.25 * ref_kib]
+        if not calib:
+            raise SystemExit(f"no reference negation kernel found for {counter} in {pmc_dir}")
+        factor = ref_kib / max(calib)
+        for name, kib in avg.items():
+            for sym, stage in KERNEL_STAGE.items():
+                if sym in name and "bf16" in name:
+                    short = name.replace("void ", "").replace("(anonymous namespace)::", "")
+                    short = short.replace("psa::", "").rsplit("(", 1)[0]
+                    e = out.setdefault(stage, {"kernel": short})
+                    e[counter + "_KiB"] = kib
+                    e[counter + "_scale"] = factor
+    src_hash = kernel_source_hash()
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for stage, e in out.items():
+        if not all(c + "_KiB" in e for c in TRAFFIC_PASSES):
+            continue
+        e["bytes_per_launch"] = int(sum(e[c + "_KiB"] * e[c + "_scale"] * 1024 for c in TRAFFIC_PASSES))
+        e["kernel_source_hash"] = src_hash
+        e["command"] = command
+        path = os.path.join(ROOT, "profiles", f"traffic_{stage}_config{config}.json")
+        with open(path, "w") as fh:
+            json.dump(e, fh, indent=1)
+        print(path, e["bytes_per_launch"])
 
 
 def main():
@@ -119,7 +185,16 @@ def main():
                     help="before warm-up, run one elementwise negation over this many MiB of "
                          "fp32 (reads and writes that many bytes): the reference kernel the "
                          "HBM byte counters are scaled by")
+    ap.add_argument("--traffic-summary", metavar="PMC_DIR",
+                    help="no timing: write the profiles/traffic_*.json files from the two "
+                         "rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) under PMC_DIR")
+    ap.add_argument("--traffic-command", default="",
+                    help="with --traffic-summary: the command line the passes ran, recorded")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary, args.config, args.calib_mb or 512,
+                        args.traffic_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures the single-GPU hot path only: the shared-prefix attention "
