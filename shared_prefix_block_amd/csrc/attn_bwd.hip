@@ -143,7 +143,12 @@ struct DkdvCfg {
   static constexpr int N_ELEMS = BMS * NS;
   static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
   static constexpr int BUF_ELEMS = 2 * (N_ELEMS + T_ELEMS);
-  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * EB + 2 * 2 * BMS * 4;
+  // bf16: Q | dO | L2 | D stages filled by direct-to-LDS loads into swizzled,
+  // unpadded tiles (as the forward's K and V); fp32: through registers.
+  static constexpr bool kDma = kBf16;
+  static constexpr int TILE_BYTES = BMS * D * 2;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * BMS * 4;
+  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * 2 * BMS * 4;
 };
 
 template <typename T, typename G, int D, int MODE>
@@ -220,34 +225,65 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     }
   };
 
+  // CSC entries (q-tile index | kind << 30) of a 64-entry window in one register,
+  // lane i holding entry e0 + wbase + i; read with readlane, so the loop issues no
+  // scalar loads and the explicit wait counts see only the tile loads.
+  int wbase = 0;
+  uint32_t wreg = 0;
+  auto window_load = [&](int base) {
+    wbase = base;
+    const int e = e0 + base + lane;
+    wreg = e < e1 ? uint32_t(p.row[e]) | (uint32_t(p.kind_csc[e]) << 30) : 0u;
+  };
+  auto entry = [&](int e) {  // packed entry e (inside the window)
+    return uint32_t(__builtin_amdgcn_readlane(int(wreg), e - e0 - wbase));
+  };
+  window_load(0);
+  mark_ready(*reinterpret_cast<int32_t*>(&wreg));
+
   RowStage<T, C::BMS, D, C::NS, C::NT> qst, gst;
   using TStage = TransStage<T, C::BMS, D, C::TS, C::NT>;
   typename std::conditional<C::kBf16, int, TStage>::type qtst, gtst;
   float l2_reg = INFINITY, dl_reg = 0.f;
   bool l2_valid = false;
+  DmaTile<C::BMS, D, C::NT> dt;
+  const int pitch = int(ldq) * 2;
+  if constexpr (C::kDma) dt.init(pitch);
 
-  auto issue = [&](int n) {
+  auto issue = [&](int n, int q_tile) {
     int e, h, sub;
     decode(n, e, h, sub);
-    const int64_t q0 = int64_t(p.row[e]) * kTileM + sub * C::BMS;
+    const int64_t q0 = int64_t(q_tile) * kTileM + sub * C::BMS;
     const int nvalid = ntok - q0 < C::BMS ? int(ntok - q0) : C::BMS;
     const T* qp = Qg + q0 * ldq + int64_t(h) * D;
     const T* gp = Gg + q0 * ldq + int64_t(h) * D;
-    {  // the per-row values first, loaded by every lane; rows past the end read 0
-      const int rr = int(threadIdx.x) & (C::BMS - 1);
-      const int64_t at = int64_t(h) * ntok + q0;
-      l2_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.L2 + at, nvalid * 4), rr * 4));
-      dl_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.Dl + at, nvalid * 4), rr * 4));
-      l2_valid = rr < nvalid;
-    }
-    qst.load(qp, ldq, nvalid);
-    gst.load(gp, ldq, nvalid);
-    if constexpr (!C::kBf16) {
-      qtst.load(qp, ldq, nvalid);
-      gtst.load(gp, ldq, nvalid);
+    const int64_t at = int64_t(h) * ntok + q0;
+    if constexpr (C::kDma) {  // straight into LDS stage n & 1: Q | dO | L2 | D
+      char* st = smem + (n & 1) * C::STAGE_BYTES;
+      dt.load(qp, nvalid, pitch, st);
+      dt.load(gp, nvalid, pitch, st + C::TILE_BYTES);
+      // rows past T read L2 = D = 0; they sit in a partial tile and are masked
+      if (wave == 0 && lane < C::BMS)
+        dma_load4(dma_rsrc(p.L2 + at, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
+      if (wave == 1 && lane < C::BMS)
+        dma_load4(dma_rsrc(p.Dl + at, nvalid * 4), lane * 4,
+                  st + 2 * C::TILE_BYTES + C::BMS * 4);
+    } else {
+      {  // the per-row values first, loaded by every lane; rows past the end read 0
+        const int rr = int(threadIdx.x) & (C::BMS - 1);
+        l2_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.L2 + at, nvalid * 4), rr * 4));
+        dl_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.Dl + at, nvalid * 4), rr * 4));
+        l2_valid = rr < nvalid;
+      }
+      qst.load(qp, ldq, nvalid);
+      gst.load(gp, ldq, nvalid);
+      if constexpr (!C::kBf16) {
+        qtst.load(qp, ldq, nvalid);
+        gtst.load(gp, ldq, nvalid);
+      }
     }
   };
-  auto commit = [&](int b) {
+  auto commit = [&](int b) {  // register path
     T* base = buf0 + b * C::BUF_ELEMS;
     qst.store(base);
     gst.store(base + C::N_ELEMS);
@@ -262,25 +298,44 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   };
 
   if (n_steps > 0) {
-    issue(0);
-    commit(0);
+    int e, h, sub;
+    decode(0, e, h, sub);
+    issue(0, int(entry(e) & 0x3fffffffu));
+    if constexpr (!C::kDma) commit(0);
   }
-  __syncthreads();
+  if constexpr (!C::kDma) __syncthreads();
 
   for (int n = 0; n < n_steps; ++n) {
     const int b = n & 1;
+    if constexpr (C::kDma) {
+      // this wave's loads of stage n are in; after the barrier everyone's are, and
+      // every wave is done with stage n - 1, which the next issue overwrites
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
     int e, h, sub;
     decode(n, e, h, sub);
-    const bool partial = tile_kind(p.kind_csc, e) == 1;
-    const int q0i = p.row[e] * kTileM + sub * C::BMS;
-    if (n + 1 < n_steps) issue(n + 1);
+    const uint32_t ent = entry(e);
+    const bool partial = (ent >> 30) == 1;
+    const int q0i = int(ent & 0x3fffffffu) * kTileM + sub * C::BMS;
+    if (n + 1 < n_steps) {
+      int e1n, h1n, s1n;
+      decode(n + 1, e1n, h1n, s1n);
+      if (e1n - e0 - wbase >= 64) {  // next window (a vector load; rare)
+        window_load(e1n - e0);
+        mark_ready(*reinterpret_cast<int32_t*>(&wreg));
+      }
+      issue(n + 1, int(entry(e1n) & 0x3fffffffu));
+    }
 
-    const T* Qs = buf0 + b * C::BUF_ELEMS;
+    const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
+    const T* Qs = buf0 + b * C::BUF_ELEMS;       // register-path buffer
     const T* Gs = Qs + C::N_ELEMS;
     const T* Qt = Qs + 2 * C::N_ELEMS;
     const T* Gt = Qt + C::T_ELEMS;
-    const float* Ls = ld0 + (b * 2 + 0) * C::BMS;
-    const float* Dsh = ld0 + (b * 2 + 1) * C::BMS;
+    const float* Ls = C::kDma ? reinterpret_cast<const float*>(st + 2 * C::TILE_BYTES)
+                              : ld0 + (b * 2 + 0) * C::BMS;
+    const float* Dsh = C::kDma ? Ls + C::BMS : ld0 + (b * 2 + 1) * C::BMS;
 
     {
       const int qd0 = q0i - kvrow_i;  // q - kv at the sub-step's first row
@@ -291,8 +346,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          mma(sacc, frag_load(qr + 16 * s), kf[s]);
-          mma(pacc, frag_load(gr + 16 * s), vf[s]);
+          if constexpr (C::kDma) {
+            mma(sacc, frag_load_swz<D / 8>(st, 32 * qb + l32, half + 2 * s), kf[s]);
+            mma(pacc, frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + l32, half + 2 * s),
+                vf[s]);
+          } else {
+            mma(sacc, frag_load(qr + 16 * s), kf[s]);
+            mma(pacc, frag_load(gr + 16 * s), vf[s]);
+          }
         }
         float pv[16], ds[16];
 #pragma unroll
@@ -321,7 +382,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
               Frag<T> ga, qa;
-              if constexpr (C::kBf16) {
+              if constexpr (C::kDma) {
+                ga = frag_load_tr_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + 16 * t, 32 * db);
+                qa = frag_load_tr_swz<D / 8>(st, 32 * qb + 16 * t, 32 * db);
+              } else if constexpr (C::kBf16) {
                 ga = frag_load_tr(Gs, C::NS, 32 * qb + 16 * t, 32 * db);
                 qa = frag_load_tr(Qs, C::NS, 32 * qb + 16 * t, 32 * db);
               } else {
@@ -340,9 +404,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         }
       }
     }
-    if (n + 1 < n_steps) commit(b ^ 1);
-    __syncthreads();
+    if constexpr (!C::kDma) {
+      if (n + 1 < n_steps) commit(b ^ 1);
+      __syncthreads();
+    }
   }
+  if constexpr (C::kDma) wait_vmcnt<0>();  // no load into LDS outlives the work-group
+
 
   if (kvvalid) {
     G* dkp = static_cast<G*>(p.dk) + (kvrow * hkv + hk) * D;
