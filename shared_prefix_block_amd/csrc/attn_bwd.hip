@@ -344,13 +344,34 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         f32x16 sacc = zero16(), pacc = zero16();
         const T* qr = Qs + (32 * qb + l32) * C::NS + 8 * half;
         const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
+        if constexpr (C::kDma) {
+          // Q and dO fragments read PF reduction steps ahead of their MFMAs
+          constexpr int NS = D / 16, PF = 3;
+          Frag<T> qq[PF], gq[PF];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          if constexpr (C::kDma) {
-            mma(sacc, frag_load_swz<D / 8>(st, 32 * qb + l32, half + 2 * s), kf[s]);
-            mma(pacc, frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + l32, half + 2 * s),
-                vf[s]);
-          } else {
+          for (int s = 0; s < PF - 1; ++s) {
+            qq[s] = frag_load_swz<D / 8>(st, 32 * qb + l32, half + 2 * s);
+            gq[s] = frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + l32, half + 2 * s);
+          }
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (s + PF - 1 < NS) {
+              const int sl = (s + PF - 1) % PF, c = half + 2 * (s + PF - 1);
+              qq[sl] = frag_load_swz<D / 8>(st, 32 * qb + l32, c);
+              gq[sl] = frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + l32, c);
+            }
+            mma(sacc, qq[s % PF], kf[s]);
+            mma(pacc, gq[s % PF], vf[s]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 1);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (s + PF - 1 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < D / 16; ++s) {
             mma(sacc, frag_load(qr + 16 * s), kf[s]);
             mma(pacc, frag_load(gr + 16 * s), vf[s]);
           }
@@ -374,6 +395,51 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) ds[4 * g + u] = pv[4 * g + u] * (pacc[4 * g + u] - dl[u]);
         }
+        if constexpr (C::kDma) {
+          // dV += dO^T P and dK += Q^T dS over these 32 queries (two 16-query
+          // fragments t): P and dS rounded to bf16, the (t, db) transposed reads
+          // PF products ahead of their MFMAs; then, where split_wanted, the
+          // residuals in a second pass
+          constexpr int ND = D / 32, NI = 2 * ND, PF = 3;
+          Frag<T> pf[2], sf[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            pf[t] = frag_from<T>(pv + 8 * t);
+            sf[t] = frag_from<T>(ds + 8 * t);
+          }
+          const char* gst = st + C::TILE_BYTES;
+          Frag<T> ga[PF], qa[PF];
+          auto tr_load = [&](int i, int sl) {
+            ga[sl] = frag_load_tr_swz<D / 8>(gst, 32 * qb + 16 * (i / ND), 32 * (i % ND));
+            qa[sl] = frag_load_tr_swz<D / 8>(st, 32 * qb + 16 * (i / ND), 32 * (i % ND));
+          };
+#pragma unroll
+          for (int i = 0; i < PF - 1; ++i) tr_load(i, i);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            if (i + PF - 1 < NI) tr_load(i + PF - 1, (i + PF - 1) % PF);
+            mma(adv[i % ND], ga[i % PF], pf[i / ND]);
+            mma(adk[i % ND], qa[i % PF], sf[i / ND]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 * (PF - 1), 2);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            if (i + PF - 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (split_wanted<T, MODE, true>(pv + 8 * t, ds + 8 * t)) {
+              const Frag<T> pl = frag_residual(pv + 8 * t, pf[t]);
+              const Frag<T> sl = frag_residual(ds + 8 * t, sf[t]);
+#pragma unroll
+              for (int db = 0; db < ND; ++db) {
+                mma(adv[db], frag_load_tr_swz<D / 8>(gst, 32 * qb + 16 * t, 32 * db), pl);
+                mma(adk[db], frag_load_tr_swz<D / 8>(st, 32 * qb + 16 * t, 32 * db), sl);
+              }
+            }
+          }
+        } else {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           // dV += dO^T P and dK += Q^T dS over these 16 queries: P and dS rounded to
@@ -401,6 +467,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
           products(pf, sf);
           if (split_wanted<T, MODE, true>(pv + 8 * t, ds + 8 * t))
             products(frag_residual(pv + 8 * t, pf), frag_residual(ds + 8 * t, sf));
+        }
         }
       }
     }
