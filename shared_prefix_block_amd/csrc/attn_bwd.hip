@@ -518,7 +518,12 @@ struct DqCfg {
   static constexpr int N_ELEMS = BN * NS;
   static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
   static constexpr int BUF_ELEMS = 2 * N_ELEMS + T_ELEMS;
-  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * EB + 2 * BN * 4;
+  // bf16: K | V | end[] stages filled by direct-to-LDS loads into swizzled tiles (as
+  // the forward); fp32: through registers
+  static constexpr bool kDma = kBf16;
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + 256;
+  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * BN * 4;
   static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
 };
 
@@ -581,25 +586,50 @@ void dq_kernel(BwdParams p) {
     if (left < kTileN) n_steps -= C::NSUB - int((left + C::BN - 1) / C::BN);
   }
 
+  // CSR entries (kv-tile index | kind << 30) of a 64-entry window in one register,
+  // read with readlane (see the forward kernel)
+  int wbase = 0;
+  uint32_t wreg = 0;
+  auto window_load = [&](int base) {
+    wbase = base;
+    const int e = e0 + base + lane;
+    wreg = e < e1 ? uint32_t(p.col[e]) | (uint32_t(p.kind[e]) << 30) : 0u;
+  };
+  auto entry = [&](int n) {
+    return uint32_t(__builtin_amdgcn_readlane(int(wreg), n / C::NSUB - wbase));
+  };
+  window_load(0);
+  mark_ready(*reinterpret_cast<int32_t*>(&wreg));
+
   RowStage<T, C::BN, D, C::NS, C::NT> kst, vst;
   using TStage = TransStage<T, C::BN, D, C::TS, C::NT>;
   typename std::conditional<C::kBf16, int, TStage>::type ktst;
+  DmaTile<C::BN, D, C::NT> dt;
+  const int pitch = int(ldk) * 2;
+  if constexpr (C::kDma) dt.init(pitch);
   int32_t e_reg = 0, kv_reg = 0;
 
-  auto issue = [&](int n) {
-    const int e = e0 + n / C::NSUB;
-    const int64_t kv0 = int64_t(p.col[e]) * kTileN + (n % C::NSUB) * C::BN;
+  auto issue = [&](int n, int col_n) {
+    const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
-    {  // every lane loads; a key past the end reads end = 0 and gets reach 0
-      const int r = int(threadIdx.x) & (C::BN - 1);
-      e_reg = int32_t(buf_load4(buf_rsrc(p.end + kv0, nvalid * 4), r * 4));
-      kv_reg = r < nvalid ? int32_t(kv0 + r) : 0;
+    if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | end[]
+      char* st = smem + (n & 1) * C::STAGE_BYTES;
+      dt.load(Kg + kv0 * ldk + koff, nvalid, pitch, st);
+      dt.load(Vg + kv0 * ldk + koff, nvalid, pitch, st + C::TILE_BYTES);
+      if (wave == 0 && lane < C::BN)  // keys past the end read end = 0: never visible
+        dma_load4(dma_rsrc(p.end + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
+    } else {
+      {  // every lane loads; a key past the end reads end = 0 and gets reach 0
+        const int r = int(threadIdx.x) & (C::BN - 1);
+        e_reg = int32_t(buf_load4(buf_rsrc(p.end + kv0, nvalid * 4), r * 4));
+        kv_reg = r < nvalid ? int32_t(kv0 + r) : 0;
+      }
+      kst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
+      vst.load(Vg + kv0 * ldk + koff, ldk, nvalid);
+      if constexpr (!C::kBf16) ktst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
     }
-    kst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
-    vst.load(Vg + kv0 * ldk + koff, ldk, nvalid);
-    if constexpr (!C::kBf16) ktst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
   };
-  auto commit = [&](int b) {
+  auto commit = [&](int b) {  // register path
     T* base = buf0 + b * C::BUF_ELEMS;
     kst.store(base);
     vst.store(base + C::N_ELEMS);
@@ -608,22 +638,34 @@ void dq_kernel(BwdParams p) {
   };
 
   if (n_steps > 0) {
-    issue(0);
-    commit(0);
+    issue(0, int(entry(0) & 0x3fffffffu));
+    if constexpr (!C::kDma) commit(0);
   }
-  __syncthreads();
+  if constexpr (!C::kDma) __syncthreads();
 
   for (int n = 0; n < n_steps; ++n) {
     const int b = n & 1;
-    const int e = e0 + n / C::NSUB;
-    const bool partial = tile_kind(p.kind, e) == 1;
-    const int kv0i = p.col[e] * kTileN + (n % C::NSUB) * C::BN;
-    if (n + 1 < n_steps) issue(n + 1);
+    if constexpr (C::kDma) {  // see the forward kernel
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    const uint32_t ent = entry(n);
+    const bool partial = (ent >> 30) == 1;
+    const int kv0i = int(ent & 0x3fffffffu) * kTileN + (n % C::NSUB) * C::BN;
+    if (n + 1 < n_steps) {
+      if ((n + 1) / C::NSUB - wbase >= 64) {  // next window (a vector load; rare)
+        window_load((n + 1) / C::NSUB);
+        mark_ready(*reinterpret_cast<int32_t*>(&wreg));
+      }
+      issue(n + 1, int(entry(n + 1) & 0x3fffffffu));
+    }
 
-    const T* Ks = buf0 + b * C::BUF_ELEMS;
+    const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
+    const T* Ks = buf0 + b * C::BUF_ELEMS;       // register-path buffer
     const T* Vs = Ks + C::N_ELEMS;
     const T* Kt = Ks + 2 * C::N_ELEMS;
-    const int32_t* Es = es0 + b * C::BN;
+    const int32_t* Es = C::kDma ? reinterpret_cast<const int32_t*>(st + 2 * C::TILE_BYTES)
+                                : es0 + b * C::BN;
 
     {
       const int qd = qrow_i - kv0i;
@@ -631,12 +673,39 @@ void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb) {
         f32x16 sacc = zero16(), pacc = zero16();
-        const T* kr = Ks + (32 * kb + l32) * C::NS + 8 * half;
-        const T* vr = Vs + (32 * kb + l32) * C::NS + 8 * half;
+        if constexpr (C::kDma) {
+          // K and V fragments read PF reduction steps ahead of their MFMAs
+          constexpr int NS = D / 16, PF = 3;
+          Frag<T> kq[PF], vq[PF];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          mma(sacc, frag_load(kr + 16 * s), qf[s]);
-          mma(pacc, frag_load(vr + 16 * s), gf[s]);
+          for (int s = 0; s < PF - 1; ++s) {
+            kq[s] = frag_load_swz<D / 8>(st, 32 * kb + l32, half + 2 * s);
+            vq[s] = frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * kb + l32, half + 2 * s);
+          }
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (s + PF - 1 < NS) {
+              const int sl = (s + PF - 1) % PF, cc = half + 2 * (s + PF - 1);
+              kq[sl] = frag_load_swz<D / 8>(st, 32 * kb + l32, cc);
+              vq[sl] = frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * kb + l32, cc);
+            }
+            mma(sacc, kq[s % PF], qf[s]);
+            mma(pacc, vq[s % PF], gf[s]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 1);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (s + PF - 1 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+          }
+        } else {
+          const T* kr = Ks + (32 * kb + l32) * C::NS + 8 * half;
+          const T* vr = Vs + (32 * kb + l32) * C::NS + 8 * half;
+#pragma unroll
+          for (int s = 0; s < D / 16; ++s) {
+            mma(sacc, frag_load(kr + 16 * s), qf[s]);
+            mma(pacc, frag_load(vr + 16 * s), gf[s]);
+          }
         }
         float pv[16];
 #pragma unroll
@@ -648,37 +717,83 @@ void dq_kernel(BwdParams p) {
             const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
             const int rv[4] = {ev.x, ev.y, ev.z, ev.w};
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-              pv[4 * g + u] = visible_u(qd - kvl - u, rv[u]) ? pv[4 * g + u] : 0.f;
+            for (int u = 0; u < 4; ++u) {
+              bool keep;
+              if constexpr (C::kDma)  // raw end[]: kv <= q < end
+                keep = (kvl + u <= qd) && (qrow_i < rv[u]);
+              else  // reach = end - kv
+                keep = visible_u(qd - kvl - u, rv[u]);
+              pv[4 * g + u] = keep ? pv[4 * g + u] : 0.f;
+            }
           }
         }
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) ds[kb][ii] = pv[ii] * (pacc[ii] - dl);
       }
+      if constexpr (C::kDma) {
+        // dQ^T += K^T dS^T: dS rounded, the (t, db) transposed K reads PF products
+        // ahead of their MFMAs; then, where split_wanted, the residuals
+        constexpr int ND = D / 32, NT16 = C::BN / 16, NI = NT16 * ND, PF = 3;
+        Frag<T> sf[NT16];
 #pragma unroll
-      for (int t = 0; t < C::BN / 16; ++t) {
-        // dQ^T += K^T dS^T over these 16 keys: dS rounded, then where split_wanted its
-        // residual in a second pass
-        const float* dst = &ds[t >> 1][(t & 1) * 8];
-        auto products = [&](const Frag<T>& sf) {
+        for (int t = 0; t < NT16; ++t) sf[t] = frag_from<T>(&ds[t >> 1][(t & 1) * 8]);
+        Frag<T> ka[PF];
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            Frag<T> ka;
-            if constexpr (C::kBf16)
-              ka = frag_load_tr(Ks, C::NS, 16 * t, 32 * db);
-            else
-              ka = frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half);
-            mma(adq[db], ka, sf);
+        for (int i = 0; i < PF - 1; ++i)
+          ka[i] = frag_load_tr_swz<D / 8>(st, 16 * (i / ND), 32 * (i % ND));
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if (i + PF - 1 < NI) {
+            const int j = i + PF - 1;
+            ka[j % PF] = frag_load_tr_swz<D / 8>(st, 16 * (j / ND), 32 * (j % ND));
           }
-        };
-        const Frag<T> sf = frag_from<T>(dst);
-        products(sf);
-        if (split_wanted<T, MODE, false>(nullptr, dst)) products(frag_residual(dst, sf));
+          mma(adq[i % ND], ka[i % PF], sf[i / ND]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 2);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if (i + PF - 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        }
+#pragma unroll
+        for (int t = 0; t < NT16; ++t) {
+          const float* dst = &ds[t >> 1][(t & 1) * 8];
+          if (split_wanted<T, MODE, false>(nullptr, dst)) {
+            const Frag<T> sl = frag_residual(dst, sf[t]);
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+              mma(adq[db], frag_load_tr_swz<D / 8>(st, 16 * t, 32 * db), sl);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < C::BN / 16; ++t) {
+          // dQ^T += K^T dS^T over these 16 keys: dS rounded, then where split_wanted
+          // its residual in a second pass
+          const float* dst = &ds[t >> 1][(t & 1) * 8];
+          auto products = [&](const Frag<T>& sf) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+              Frag<T> ka;
+              if constexpr (C::kBf16)
+                ka = frag_load_tr(Ks, C::NS, 16 * t, 32 * db);
+              else
+                ka = frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half);
+              mma(adq[db], ka, sf);
+            }
+          };
+          const Frag<T> sf = frag_from<T>(dst);
+          products(sf);
+          if (split_wanted<T, MODE, false>(nullptr, dst)) products(frag_residual(dst, sf));
+        }
       }
     }
-    if (n + 1 < n_steps) commit(b ^ 1);
-    __syncthreads();
+    if constexpr (!C::kDma) {
+      if (n + 1 < n_steps) commit(b ^ 1);
+      __syncthreads();
+    }
   }
+  if constexpr (C::kDma) wait_vmcnt<0>();  // no load into LDS outlives the work-group
 
   if (qvalid) {
     G* dqp = static_cast<G*>(p.dq) + (qrow * hq + h) * D;
