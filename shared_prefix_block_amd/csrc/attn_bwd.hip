@@ -250,6 +250,23 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const int pitch = int(ldq) * 2;
   if constexpr (C::kDma) dt.init(pitch);
 
+  // DMA path: a stage's tile loads are not issued in one burst (the wave would stall
+  // on the memory-request queue) but one per reduction step of the next sub-step's
+  // first S/dP product, where the MFMAs hide their issue cost.  Without a next stage
+  // the descriptors cover 0 bytes and the loads only write zeros into the idle buffer.
+  constexpr int NT_LOADS = DmaTile<C::BMS, D, C::NT>::N;  // per tile and wave
+  DmaRsrc rq{}, rg{};
+  char* st_next = smem;
+  auto dma_part = [&](int j) {
+    if constexpr (C::kDma) {
+      const int w = threadIdx.x >> 6;
+      if (j < NT_LOADS)
+        dma_load16(rq, dt.voff[j], st_next + (j * (C::NT / 64) + w) * 1024);
+      else
+        dma_load16(rg, dt.voff[j - NT_LOADS],
+                   st_next + C::TILE_BYTES + ((j - NT_LOADS) * (C::NT / 64) + w) * 1024);
+    }
+  };
   auto issue = [&](int n, int q_tile) {
     int e, h, sub;
     decode(n, e, h, sub);
@@ -258,10 +275,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const T* qp = Qg + q0 * ldq + int64_t(h) * D;
     const T* gp = Gg + q0 * ldq + int64_t(h) * D;
     const int64_t at = int64_t(h) * ntok + q0;
-    if constexpr (C::kDma) {  // straight into LDS stage n & 1: Q | dO | L2 | D
+    if constexpr (C::kDma) {  // into LDS stage n & 1: Q | dO | L2 | D
       char* st = smem + (n & 1) * C::STAGE_BYTES;
-      dt.load(qp, nvalid, pitch, st);
-      dt.load(gp, nvalid, pitch, st + C::TILE_BYTES);
+      st_next = st;
+      rq = dma_rsrc(qp, nvalid * pitch);
+      rg = dma_rsrc(gp, nvalid * pitch);
       // rows past T read L2 = D = 0; they sit in a partial tile and are masked
       if (wave == 0 && lane < C::BMS)
         dma_load4(dma_rsrc(p.L2 + at, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
@@ -301,7 +319,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     int e, h, sub;
     decode(0, e, h, sub);
     issue(0, int(entry(e) & 0x3fffffffu));
-    if constexpr (!C::kDma) commit(0);
+    if constexpr (C::kDma) {
+#pragma unroll
+      for (int j = 0; j < 2 * NT_LOADS; ++j) dma_part(j);
+    } else {
+      commit(0);
+    }
   }
   if constexpr (!C::kDma) __syncthreads();
 
@@ -326,6 +349,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         mark_ready(*reinterpret_cast<int32_t*>(&wreg));
       }
       issue(n + 1, int(entry(e1n) & 0x3fffffffu));
+    } else if constexpr (C::kDma) {
+      st_next = smem + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
+      rq = dma_rsrc(Qg, 0);
+      rg = rq;
     }
 
     const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
@@ -362,6 +389,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
             }
             mma(sacc, qq[s % PF], kf[s]);
             mma(pacc, gq[s % PF], vf[s]);
+            if (qb == 0) {  // the next stage's tile loads, spread over these steps
+#pragma unroll
+              for (int j = 0; j < 2 * NT_LOADS; ++j)
+                if ((j * NS) / (2 * NT_LOADS) == s) dma_part(j);
+            }
           }
           __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 1);
 #pragma unroll
