@@ -70,7 +70,7 @@ struct BwdParams {
 constexpr int kSplitAdaptive = 0, kSplitAll = 1;
 constexpr float kTauP = 0.125f, kTauS = 1.0f;
 
-template <typename T, int MODE, bool WITH_P>
+template <typename T, int MODE, bool WITH_P, bool WITH_S = true>
 __device__ __forceinline__ bool split_wanted(const float* p8, const float* s8) {
   if constexpr (!std::is_same<T, bf16_t>::value) {
     return false;
@@ -81,7 +81,7 @@ __device__ __forceinline__ bool split_wanted(const float* p8, const float* s8) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if constexpr (WITH_P) mp = fmaxf(mp, p8[j]);  // P >= 0
-      ms = fmaxf(ms, fabsf(s8[j]));
+      if constexpr (WITH_S) ms = fmaxf(ms, fabsf(s8[j]));
     }
     return __any(mp > kTauP || ms > kTauS);  // wave-uniform
   }
@@ -151,9 +151,14 @@ struct DkdvCfg {
   static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * 2 * BMS * 4;
 };
 
-template <typename T, typename G, int D, int MODE>
+// PART: 0 computes dK and dV together; 1 only dV, 2 only dK.  At d = 256 K, V and
+// both accumulators do not fit one wave's registers, so the pair is split into two
+// passes (dV: S and P only; dK: S, dP and dS), at the price of recomputing S.
+template <typename T, typename G, int D, int MODE, int PART>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   using C = DkdvCfg<T, D>;
+  constexpr bool kDV = PART != 2, kDK = PART != 1;
+  static_assert(PART == 0 || C::kDma, "split passes exist on the DMA path only");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   T* const buf0 = reinterpret_cast<T*>(smem);
   float* const ld0 = reinterpret_cast<float*>(smem + 2 * C::BUF_ELEMS * C::EB);  // [2][2][BMS]
@@ -183,12 +188,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       kf[s] = kvvalid ? frag_load(Kg + off + 16 * s) : frag_zero<T>();
-      vf[s] = kvvalid ? frag_load(Vg + off + 16 * s) : frag_zero<T>();
+      if constexpr (kDK) vf[s] = kvvalid ? frag_load(Vg + off + 16 * s) : frag_zero<T>();
     }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       mark_ready(kf[s]);
-      mark_ready(vf[s]);
+      if constexpr (kDK) mark_ready(vf[s]);
     }
     mark_ready(reach);
   }
@@ -375,31 +380,33 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
           // Q and dO fragments read PF reduction steps ahead of their MFMAs
           constexpr int NS = D / 16, PF = 3;
           Frag<T> qq[PF], gq[PF];
+          constexpr int RD = kDK ? 2 : 1;  // fragment reads per reduction step
 #pragma unroll
           for (int s = 0; s < PF - 1; ++s) {
             qq[s] = frag_load_swz<D / 8>(st, 32 * qb + l32, half + 2 * s);
-            gq[s] = frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + l32, half + 2 * s);
+            if constexpr (kDK)
+              gq[s] = frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + l32, half + 2 * s);
           }
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
             if (s + PF - 1 < NS) {
               const int sl = (s + PF - 1) % PF, c = half + 2 * (s + PF - 1);
               qq[sl] = frag_load_swz<D / 8>(st, 32 * qb + l32, c);
-              gq[sl] = frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + l32, c);
+              if constexpr (kDK) gq[sl] = frag_load_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + l32, c);
             }
             mma(sacc, qq[s % PF], kf[s]);
-            mma(pacc, gq[s % PF], vf[s]);
+            if constexpr (kDK) mma(pacc, gq[s % PF], vf[s]);
             if (qb == 0) {  // the next stage's tile loads, spread over these steps
 #pragma unroll
               for (int j = 0; j < 2 * NT_LOADS; ++j)
                 if ((j * NS) / (2 * NT_LOADS) == s) dma_part(j);
             }
           }
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, RD * (PF - 1), 1);
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            if (s + PF - 1 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+            if (s + PF - 1 < NS) __builtin_amdgcn_sched_group_barrier(0x100, RD, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, RD, 1);
           }
         } else {
 #pragma unroll
@@ -421,11 +428,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
           for (int ii = 0; ii < 16; ++ii)
             pv[ii] = visible_u(qd0 + 32 * qb + acc_row(ii, half), reach) ? pv[ii] : 0.f;
         }
+        if constexpr (kDK) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 dl = *reinterpret_cast<const f32x4*>(Dsh + 32 * qb + g * 8 + half * 4);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 dl = *reinterpret_cast<const f32x4*>(Dsh + 32 * qb + g * 8 + half * 4);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) ds[4 * g + u] = pv[4 * g + u] * (pacc[4 * g + u] - dl[u]);
+            for (int u = 0; u < 4; ++u) ds[4 * g + u] = pv[4 * g + u] * (pacc[4 * g + u] - dl[u]);
+          }
         }
         if constexpr (C::kDma) {
           // dV += dO^T P and dK += Q^T dS over these 32 queries (two 16-query
@@ -433,41 +442,47 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
           // PF products ahead of their MFMAs; then, where split_wanted, the
           // residuals in a second pass
           constexpr int ND = D / 32, NI = 2 * ND, PF = 3;
+          constexpr int TR = 2 * ((kDV ? 1 : 0) + (kDK ? 1 : 0));  // reads per product
+          constexpr int MF = (kDV ? 1 : 0) + (kDK ? 1 : 0);        // MFMAs per product
           Frag<T> pf[2], sf[2];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            pf[t] = frag_from<T>(pv + 8 * t);
-            sf[t] = frag_from<T>(ds + 8 * t);
+            if constexpr (kDV) pf[t] = frag_from<T>(pv + 8 * t);
+            if constexpr (kDK) sf[t] = frag_from<T>(ds + 8 * t);
           }
           const char* gst = st + C::TILE_BYTES;
           Frag<T> ga[PF], qa[PF];
           auto tr_load = [&](int i, int sl) {
-            ga[sl] = frag_load_tr_swz<D / 8>(gst, 32 * qb + 16 * (i / ND), 32 * (i % ND));
-            qa[sl] = frag_load_tr_swz<D / 8>(st, 32 * qb + 16 * (i / ND), 32 * (i % ND));
+            if constexpr (kDV)
+              ga[sl] = frag_load_tr_swz<D / 8>(gst, 32 * qb + 16 * (i / ND), 32 * (i % ND));
+            if constexpr (kDK)
+              qa[sl] = frag_load_tr_swz<D / 8>(st, 32 * qb + 16 * (i / ND), 32 * (i % ND));
           };
 #pragma unroll
           for (int i = 0; i < PF - 1; ++i) tr_load(i, i);
 #pragma unroll
           for (int i = 0; i < NI; ++i) {
             if (i + PF - 1 < NI) tr_load(i + PF - 1, (i + PF - 1) % PF);
-            mma(adv[i % ND], ga[i % PF], pf[i / ND]);
-            mma(adk[i % ND], qa[i % PF], sf[i / ND]);
+            if constexpr (kDV) mma(adv[i % ND], ga[i % PF], pf[i / ND]);
+            if constexpr (kDK) mma(adk[i % ND], qa[i % PF], sf[i / ND]);
           }
-          __builtin_amdgcn_sched_group_barrier(0x100, 4 * (PF - 1), 2);
+          __builtin_amdgcn_sched_group_barrier(0x100, TR * (PF - 1), 2);
 #pragma unroll
           for (int i = 0; i < NI; ++i) {
-            if (i + PF - 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+            if (i + PF - 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, TR, 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, MF, 2);
           }
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            if (split_wanted<T, MODE, true>(pv + 8 * t, ds + 8 * t)) {
-              const Frag<T> pl = frag_residual(pv + 8 * t, pf[t]);
-              const Frag<T> sl = frag_residual(ds + 8 * t, sf[t]);
+            if (split_wanted<T, MODE, kDV, kDK>(pv + 8 * t, ds + 8 * t)) {
 #pragma unroll
               for (int db = 0; db < ND; ++db) {
-                mma(adv[db], frag_load_tr_swz<D / 8>(gst, 32 * qb + 16 * t, 32 * db), pl);
-                mma(adk[db], frag_load_tr_swz<D / 8>(st, 32 * qb + 16 * t, 32 * db), sl);
+                if constexpr (kDV)
+                  mma(adv[db], frag_load_tr_swz<D / 8>(gst, 32 * qb + 16 * t, 32 * db),
+                      frag_residual(pv + 8 * t, pf[t]));
+                if constexpr (kDK)
+                  mma(adk[db], frag_load_tr_swz<D / 8>(st, 32 * qb + 16 * t, 32 * db),
+                      frag_residual(ds + 8 * t, sf[t]));
               }
             }
           }
@@ -520,11 +535,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * db + g * 8 + half * 4;
-        vec4_store(dkp + d, vec4_from(adk[db][4 * g] * sc, adk[db][4 * g + 1] * sc,
-                                      adk[db][4 * g + 2] * sc, adk[db][4 * g + 3] * sc,
-                                      static_cast<G*>(nullptr)));
-        vec4_store(dvp + d, vec4_from(adv[db][4 * g], adv[db][4 * g + 1], adv[db][4 * g + 2],
-                                      adv[db][4 * g + 3], static_cast<G*>(nullptr)));
+        if constexpr (kDK)
+          vec4_store(dkp + d, vec4_from(adk[db][4 * g] * sc, adk[db][4 * g + 1] * sc,
+                                        adk[db][4 * g + 2] * sc, adk[db][4 * g + 3] * sc,
+                                        static_cast<G*>(nullptr)));
+        if constexpr (kDV)
+          vec4_store(dvp + d, vec4_from(adv[db][4 * g], adv[db][4 * g + 1], adv[db][4 * g + 2],
+                                        adv[db][4 * g + 3], static_cast<G*>(nullptr)));
       }
   }
 }
@@ -888,7 +905,15 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
     p.chunk = 2;
     const int64_t per = 8 * int64_t(p.chunk);
     const int64_t grid = (p.n_work + per - 1) / per * per;
-    hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+    if constexpr (D > 128) {  // dV and dK in two passes (see dkdv_kernel)
+      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 1>), dim3(unsigned(grid)), dim3(256), 0,
+                         stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 2>), dim3(unsigned(grid)), dim3(256), 0,
+                         stream, p);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 0>), dim3(unsigned(grid)), dim3(256), 0,
+                         stream, p);
+    }
   }
   if (stages & PSA_STAGE_DQ) {
     p.n_work = map.nq * s.hq;
