@@ -77,46 +77,98 @@ hipMemPool_t pool_for(int dev) {
   return pools[dev];
 }
 
-hipError_t map_alloc(psa_tile_map* m, void** p, size_t bytes) {
-  hipMemPool_t pool = pool_for(m->device);
-  if (pool) {
-    m->pooled = true;
-    return hipMallocFromPoolAsync(p, bytes, pool, m->stream);
+// Buffers of destroyed maps are kept in a small cache and handed to later builds on
+// the same device (a buffer at least as large as asked and at most twice as large):
+// a steady stream of build / destroy pairs then does no allocation at all.  Each
+// cached buffer carries an event recorded on its last map's stream at destroy time;
+// a build that takes it makes its own stream wait on that event first.
+struct CachedBuf {
+  int dev;
+  size_t bytes;
+  void* p;
+  hipEvent_t ev;
+};
+std::mutex g_cache_mu;
+std::vector<CachedBuf> g_cache;
+constexpr size_t kCacheMaxBytes = size_t{256} << 20;
+constexpr size_t kCacheMaxCount = 16;
+
+void raw_free(int dev, void* p, hipEvent_t ev, hipStream_t s) {
+  // after the work ordered before ev, back to the pool (or the plain allocator)
+  if (ev) {
+    (void)hipStreamWaitEvent(s, ev, 0);
+    (void)hipEventDestroy(ev);
   }
-  m->pooled = false;
+  if (pool_for(dev)) (void)hipFreeAsync(p, s);
+  else (void)hipFree(p);
+}
+
+hipError_t map_alloc(psa_tile_map* m, void** p, size_t bytes, size_t* got, hipEvent_t* ev) {
+  bytes = align_up(std::max<size_t>(bytes, 1), size_t{1} << 16);
+  *ev = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    int best = -1;
+    for (size_t k = 0; k < g_cache.size(); ++k) {
+      const CachedBuf& c = g_cache[k];
+      if (c.dev == m->device && c.bytes >= bytes && c.bytes <= 2 * bytes &&
+          (best < 0 || c.bytes < g_cache[best].bytes))
+        best = int(k);
+    }
+    if (best >= 0) {
+      const CachedBuf c = g_cache[best];
+      g_cache.erase(g_cache.begin() + best);
+      *p = c.p;
+      *got = c.bytes;
+      *ev = c.ev;
+      return c.ev ? hipStreamWaitEvent(m->stream, c.ev, 0) : hipSuccess;
+    }
+  }
+  *got = bytes;
+  hipMemPool_t pool = pool_for(m->device);
+  if (pool) return hipMallocFromPoolAsync(p, bytes, pool, m->stream);
   return hipMalloc(p, bytes);
 }
 
-void map_free(const psa_tile_map* m, void* p) {
+void map_release(const psa_tile_map* m, void* p, size_t bytes, hipEvent_t ev) {
   if (!p) return;
-  if (m->pooled) (void)hipFreeAsync(p, m->stream);
-  else (void)hipFree(p);
+  if (!ev && hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    ev = nullptr;
+  }
+  if (ev && hipEventRecord(ev, m->stream) == hipSuccess) {
+    std::vector<CachedBuf> evicted;
+    {
+      std::lock_guard<std::mutex> lock(g_cache_mu);
+      g_cache.push_back({m->device, bytes, p, ev});
+      size_t total = 0;
+      for (const CachedBuf& c : g_cache) total += c.bytes;
+      while (!g_cache.empty() && (g_cache.size() > kCacheMaxCount || total > kCacheMaxBytes)) {
+        total -= g_cache.front().bytes;  // the oldest goes back to the allocator
+        evicted.push_back(g_cache.front());
+        g_cache.erase(g_cache.begin());
+      }
+    }
+    for (const CachedBuf& c : evicted) raw_free(c.dev, c.p, c.ev, m->stream);
+    return;
+  }
+  (void)hipGetLastError();
+  raw_free(m->device, p, ev, m->stream);
 }
 
 void free_map(psa_tile_map* m) {
   if (!m) return;
-  map_free(m, m->buf1);
-  map_free(m, m->buf2);
+  map_release(m, m->buf1, m->buf1_bytes, m->ev1);
+  map_release(m, m->buf2, m->buf2_bytes, m->ev2);
   delete m;
 }
 
-// Descending-length order of CSR rows / CSC columns (stable: ties keep index order).
-void length_order(const int32_t* ptr, int64_t n, int32_t* out) {
-  std::vector<int32_t> idx(n);
-  std::iota(idx.begin(), idx.end(), 0);
-  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
-    return (ptr[a + 1] - ptr[a]) > (ptr[b + 1] - ptr[b]);
-  });
-  std::copy(idx.begin(), idx.end(), out);
-}
-
 // Phase-1 allocation.  Layout: end | kinds | scratch | info (8 x int64) | row_ptr |
-// col_ptr, the last three contiguous so that one copy brings them back.
+// col_ptr.
 struct Phase1 {
   int32_t* scratch = nullptr;  // per-k-tile summaries, then reused by nothing else
   int32_t* tok_scratch = nullptr;
   int64_t* info = nullptr;     // nnz, n_full, n_partial, first layout error
-  size_t readback_bytes = 0;   // info .. end of col_ptr
 };
 
 psa_status alloc_phase1(psa_tile_map* m, Phase1* ph) {
@@ -130,7 +182,7 @@ psa_status alloc_phase1(psa_tile_map* m, Phase1* ph) {
   size_t o_rp = c.take<int32_t>(m->nq + 1);
   size_t o_cp = c.take<int32_t>(m->nk + 1);
   const size_t total = c.off;
-  hipError_t e = map_alloc(m, &m->buf1, total);
+  hipError_t e = map_alloc(m, &m->buf1, total, &m->buf1_bytes, &m->ev1);
   if (e != hipSuccess) {
     m->buf1 = nullptr;
     (void)hipGetLastError();
@@ -144,7 +196,6 @@ psa_status alloc_phase1(psa_tile_map* m, Phase1* ph) {
   ph->scratch = reinterpret_cast<int32_t*>(b + o_scr);
   ph->tok_scratch = reinterpret_cast<int32_t*>(b + o_tok);
   ph->info = reinterpret_cast<int64_t*>(b + o_info);
-  ph->readback_bytes = o_cp + size_t(m->nk + 1) * 4 - o_info;
   e = launch_map_init(m->nk, m->row_ptr, m->col_ptr, ph->info, m->stream);
   if (e != hipSuccess) return psa_hip_error(e, "tile map init launch");
   return PSA_OK;
@@ -157,19 +208,12 @@ psa_status finish_build(psa_tile_map* m, const Phase1& ph, psa_tile_map** out) {
                                  m->row_ptr, m->col_ptr, kmin, kmax, ph.info, m->stream);
   if (e != hipSuccess) return psa_hip_error(e, "tile classification launch");
 
-  // the one wait: info and both pointer arrays come back in one copy
-  std::vector<char> rb(ph.readback_bytes);
-  if ((e = hipMemcpyAsync(rb.data(), ph.info, rb.size(), hipMemcpyDeviceToHost, m->stream)) !=
+  // the one wait: the counts and the layout verdict
+  int64_t info_h[8];
+  if ((e = hipMemcpyAsync(info_h, ph.info, sizeof(info_h), hipMemcpyDeviceToHost, m->stream)) !=
           hipSuccess ||
       (e = hipStreamSynchronize(m->stream)) != hipSuccess)
     return psa_hip_error(e, "tile map readback");
-  const int64_t* info_h = reinterpret_cast<const int64_t*>(rb.data());
-  const char* rp_at = rb.data() + (reinterpret_cast<char*>(m->row_ptr) -
-                                   reinterpret_cast<char*>(ph.info));
-  const char* cp_at = rb.data() + (reinterpret_cast<char*>(m->col_ptr) -
-                                   reinterpret_cast<char*>(ph.info));
-  const int32_t* rp_h = reinterpret_cast<const int32_t*>(rp_at);
-  const int32_t* cp_h = reinterpret_cast<const int32_t*>(cp_at);
   if (info_h[3] != -1) {
     static const char* why[] = {
         "",
@@ -192,7 +236,7 @@ psa_status finish_build(psa_tile_map* m, const Phase1& ph, psa_tile_map** out) {
   size_t o_row = c.take<int32_t>(std::max<int64_t>(m->nnz, 1));
   size_t o_kc = c.take<uint8_t>(std::max<int64_t>(m->nnz, 1));
   size_t o_qo = c.take<int32_t>(std::max<int64_t>(m->nq + m->nk, 1));  // qorder | korder
-  if ((e = map_alloc(m, &m->buf2, c.off)) != hipSuccess) {
+  if ((e = map_alloc(m, &m->buf2, c.off, &m->buf2_bytes, &m->ev2)) != hipSuccess) {
     m->buf2 = nullptr;
     (void)hipGetLastError();
     return psa_set_error(PSA_ERR_ALLOC, "device allocation of the tile lists failed");
@@ -205,19 +249,9 @@ psa_status finish_build(psa_tile_map* m, const Phase1& ph, psa_tile_map** out) {
   m->qorder = reinterpret_cast<int32_t*>(b2 + o_qo);
   m->korder = m->qorder + m->nq;
 
-  if (m->nnz > 0) {
-    e = launch_fill_lists(m->nq, m->nk, m->kinds, m->row_ptr, m->col_ptr, m->col, m->kind,
-                          m->row, m->kind_csc, m->stream);
-    if (e != hipSuccess) return psa_hip_error(e, "tile list launch");
-  }
-  m->host_orders.resize(m->nq + m->nk);
-  length_order(rp_h, m->nq, m->host_orders.data());
-  length_order(cp_h, m->nk, m->host_orders.data() + m->nq);
-  if (m->nq > 0) {
-    if ((e = hipMemcpyAsync(m->qorder, m->host_orders.data(), (m->nq + m->nk) * 4,
-                            hipMemcpyHostToDevice, m->stream)) != hipSuccess)
-      return psa_hip_error(e, "tile order upload");
-  }
+  e = launch_fill_lists(m->nq, m->nk, m->kinds, m->row_ptr, m->col_ptr, m->col, m->kind,
+                        m->row, m->kind_csc, m->qorder, m->korder, m->stream);
+  if (e != hipSuccess) return psa_hip_error(e, "tile list launch");
   *out = m;
   return PSA_OK;
 }
@@ -416,15 +450,18 @@ psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
     return st;
   }
   void* d_table = nullptr;
+  size_t table_bytes = 0;
+  hipEvent_t table_ev = nullptr;
   if (n_nodes > 0) {
-    if ((e = map_alloc(m, &d_table, table.size() * sizeof(int64_t))) != hipSuccess) {
+    if ((e = map_alloc(m, &d_table, table.size() * sizeof(int64_t), &table_bytes, &table_ev)) !=
+        hipSuccess) {
       (void)hipGetLastError();
       free_map(m);
       return psa_set_error(PSA_ERR_ALLOC, "device allocation of the node table failed");
     }
     if ((e = hipMemcpyAsync(d_table, table.data(), table.size() * sizeof(int64_t),
                             hipMemcpyHostToDevice, m->stream)) != hipSuccess) {
-      map_free(m, d_table);
+      map_release(m, d_table, table_bytes, table_ev);
       free_map(m);
       return psa_hip_error(e, "node table upload");
     }
@@ -432,7 +469,7 @@ psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
   const int64_t* dt = static_cast<const int64_t*>(d_table);
   e = launch_tree_end(T, n_nodes, dt, dt ? dt + n_nodes : nullptr, start[n_nodes], m->end,
                       m->stream);
-  map_free(m, d_table);  // stream-ordered after the launch (or the plain free's wait)
+  map_release(m, d_table, table_bytes, table_ev);  // reusable once the launch is done
   if (e != hipSuccess) {
     free_map(m);
     return psa_hip_error(e, "tree expansion launch");

@@ -18,7 +18,8 @@ struct psa_tile_map {
   int64_t nnz = 0, n_full = 0, n_partial = 0;
   int device = 0;
   hipStream_t stream = nullptr;  // build stream (export waits on it; buffers freed on it)
-  bool pooled = false;           // buffers from the library's stream-ordered pool
+  size_t buf1_bytes = 0, buf2_bytes = 0;  // sizes of the two device buffers
+  hipEvent_t ev1 = nullptr, ev2 = nullptr;  // their reuse events (cached buffers)
 
   // phase-1 allocation (sized before the sync)
   void* buf1 = nullptr;
@@ -34,7 +35,6 @@ struct psa_tile_map {
   uint8_t* kind_csc = nullptr;  // [nnz] CSC kind
   int32_t* qorder = nullptr;    // [nq]  q-tiles by descending CSR row length
   int32_t* korder = nullptr;    // [nk]  kv-tiles by descending CSC column length
-  std::vector<int32_t> host_orders;  // staging of qorder/korder (lives with the map)
 };
 
 // Error helpers (api.cpp)
@@ -63,10 +63,11 @@ hipError_t launch_classify(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_
                            const int32_t* end, uint8_t* kinds, int32_t* row_ptr,
                            int32_t* col_ptr, int32_t* ktile_min_end, int32_t* ktile_max_end,
                            int64_t* info, hipStream_t stream);
+// CSR and CSC lists (ordered compaction of kinds) and the two length orders.
 hipError_t launch_fill_lists(int64_t nq, int64_t nk, const uint8_t* kinds,
                              const int32_t* row_ptr, const int32_t* col_ptr, int32_t* col,
-                             uint8_t* kind, int32_t* row, uint8_t* kind_csc,
-                             hipStream_t stream);
+                             uint8_t* kind, int32_t* row, uint8_t* kind_csc, int32_t* qorder,
+                             int32_t* korder, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // attention kernels

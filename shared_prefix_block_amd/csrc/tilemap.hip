@@ -361,44 +361,54 @@ __device__ inline int block_excl_count(bool f, int* sh_w, int* total) {
   return before + before_in_wave;
 }
 
-__global__ __launch_bounds__(kFillThreads) void k_fill_csr(int64_t nq, int64_t nk,
-                                                           const uint8_t* __restrict__ kinds,
-                                                           const int32_t* __restrict__ row_ptr,
-                                                           int32_t* col, uint8_t* kind) {
-  __shared__ int sh_w[kFillThreads / 64];
-  const int64_t i = blockIdx.x;
-  int64_t base = row_ptr[i];
-  for (int64_t j0 = 0; j0 < nk; j0 += kFillThreads) {
-    int64_t j = j0 + threadIdx.x;
-    uint8_t k = j < nk ? kinds[i * nk + j] : 0;
-    int total;
-    int pos = block_excl_count(k != 0, sh_w, &total);
-    if (k) {
-      col[base + pos] = int32_t(j);
-      kind[base + pos] = k;
-    }
-    base += total;
+// Rank of list i among n lists by descending length, ties by index (a stable sort):
+// the number of lists that come before it.  One block; O(n) work.
+__device__ inline int32_t length_rank(const int32_t* __restrict__ ptr, int64_t n, int64_t i,
+                                      int* sh_w) {
+  const int64_t li = ptr[i + 1] - ptr[i];
+  int cnt = 0;
+  for (int64_t j = threadIdx.x; j < n; j += kFillThreads) {
+    const int64_t lj = ptr[j + 1] - ptr[j];
+    cnt += (lj > li || (lj == li && j < i)) ? 1 : 0;
   }
+  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh_w[w] = cnt;
+  __syncthreads();
+  int total = 0;
+  for (int k = 0; k < kFillThreads / 64; ++k) total += sh_w[k];
+  return total;
 }
 
-__global__ __launch_bounds__(kFillThreads) void k_fill_csc(int64_t nq, int64_t nk,
-                                                           const uint8_t* __restrict__ kinds,
-                                                           const int32_t* __restrict__ col_ptr,
-                                                           int32_t* row, uint8_t* kind_csc) {
+// Blocks [0, nq): CSR row b, ordered compaction of row b of kinds, and its place in
+// qorder (q-tiles by descending list length).  Blocks [nq, nq + nk): the same for CSC
+// column b - nq and korder.
+__global__ __launch_bounds__(kFillThreads) void k_fill_lists(
+    int64_t nq, int64_t nk, const uint8_t* __restrict__ kinds,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_ptr, int32_t* col,
+    uint8_t* kind, int32_t* row, uint8_t* kind_csc, int32_t* qorder, int32_t* korder) {
   __shared__ int sh_w[kFillThreads / 64];
-  const int64_t j = blockIdx.x;
-  int64_t base = col_ptr[j];
-  for (int64_t i0 = 0; i0 < nq; i0 += kFillThreads) {
-    int64_t i = i0 + threadIdx.x;
-    uint8_t k = i < nq ? kinds[i * nk + j] : 0;
+  const bool csr = blockIdx.x < nq;
+  const int64_t i = csr ? int64_t(blockIdx.x) : int64_t(blockIdx.x) - nq;
+  const int64_t n_other = csr ? nk : nq;
+  const int32_t* ptr = csr ? row_ptr : col_ptr;
+  int32_t* idx = csr ? col : row;
+  uint8_t* kd = csr ? kind : kind_csc;
+  int64_t base = ptr[i];
+  for (int64_t j0 = 0; j0 < n_other; j0 += kFillThreads) {
+    const int64_t j = j0 + threadIdx.x;
+    const uint8_t k = j < n_other ? (csr ? kinds[i * nk + j] : kinds[j * nk + i]) : 0;
     int total;
-    int pos = block_excl_count(k != 0, sh_w, &total);
+    const int pos = block_excl_count(k != 0, sh_w, &total);
     if (k) {
-      row[base + pos] = int32_t(i);
-      kind_csc[base + pos] = k;
+      idx[base + pos] = int32_t(j);
+      kd[base + pos] = k;
     }
     base += total;
   }
+  const int32_t r = length_rank(ptr, csr ? nq : nk, i, sh_w);
+  if (threadIdx.x == 0) (csr ? qorder : korder)[r] = int32_t(i);
 }
 
 }  // namespace
@@ -456,11 +466,10 @@ hipError_t launch_classify(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_
 
 hipError_t launch_fill_lists(int64_t nq, int64_t nk, const uint8_t* kinds,
                              const int32_t* row_ptr, const int32_t* col_ptr, int32_t* col,
-                             uint8_t* kind, int32_t* row, uint8_t* kind_csc,
-                             hipStream_t stream) {
-  hipLaunchKernelGGL(k_fill_csr, dim3(unsigned(nq)), dim3(kFillThreads), 0, stream, nq, nk,
-                     kinds, row_ptr, col, kind);
-  hipLaunchKernelGGL(k_fill_csc, dim3(unsigned(nk)), dim3(kFillThreads), 0, stream, nq, nk,
-                     kinds, col_ptr, row, kind_csc);
+                             uint8_t* kind, int32_t* row, uint8_t* kind_csc, int32_t* qorder,
+                             int32_t* korder, hipStream_t stream) {
+  if (nq + nk == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_lists, dim3(unsigned(nq + nk)), dim3(kFillThreads), 0, stream, nq,
+                     nk, kinds, row_ptr, col_ptr, col, kind, row, kind_csc, qorder, korder);
   return hipGetLastError();
 }
