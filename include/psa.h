@@ -183,12 +183,16 @@ psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtyp
 
 /*
  * The backward in stages, for callers that time or overlap them (psa_bwd runs all
- * three in order), with options.  flags is the OR of a nonzero set of stages:
+ * three), with options.  flags is the OR of a nonzero set of stages:
  *   PSA_STAGE_PREPARE  D = rowsum(dO * O) and LSE in log2 units, into the workspace
  *                      (reads o, lse, dout);
  *   PSA_STAGE_DKDV     dK, dV (reads q, k, v, dout and the prepared workspace);
  *   PSA_STAGE_DQ       dQ (reads q, k, v, dout and the prepared workspace).
- * DKDV and DQ depend only on PREPARE, not on each other.  And optionally:
+ * DKDV and DQ depend only on PREPARE, not on each other.  When PREPARE and DQ are
+ * requested together (as psa_bwd does), the dQ kernel does the preparation of its own
+ * rows (it holds dO for exactly those rows) and runs first, and DKDV, if requested,
+ * runs after it; the results are those of the three stages run one by one, up to the
+ * order of the fp32 sums that form D.  And optionally:
  *   PSA_BWD_SPLIT_PDS  carry P and dS into the dV, dK and dQ products as a pair of
  *                      bf16 fragments hi + lo (about 16 significant bits instead of
  *                      8, at two MFMAs per product instead of one).  Without it P

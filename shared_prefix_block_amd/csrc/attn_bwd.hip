@@ -182,21 +182,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const T* Qg = static_cast<const T*>(p.q);
   const T* Gg = static_cast<const T*>(p.dout);
 
-  Frag<T> kf[D / 16], vf[D / 16];
-  {
-    const int64_t off = (kvrow * hkv + hk) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      kf[s] = kvvalid ? frag_load(Kg + off + 16 * s) : frag_zero<T>();
-      if constexpr (kDK) vf[s] = kvvalid ? frag_load(Vg + off + 16 * s) : frag_zero<T>();
-    }
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      mark_ready(kf[s]);
-      if constexpr (kDK) mark_ready(vf[s]);
-    }
-    mark_ready(reach);
-  }
+  Frag<T> kf[D / 16], vf[D / 16];  // loaded below, once the first tile's loads are in flight
   f32x16 adk[D / 32], adv[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -216,18 +202,20 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   }
   const int full_steps = (e1 - e0 - 1) * rep * C::NSUB;
   const int n_steps = e1 > e0 ? full_steps + rep * ns_last : 0;
-  auto decode = [&](int n, int& e, int& h, int& sub) {
-    if (n < full_steps) {
-      e = e0 + n / (rep * C::NSUB);
-      const int rem = n % (rep * C::NSUB);
-      h = hk * rep + rem / C::NSUB;
-      sub = rem % C::NSUB;
-    } else {
-      const int rem = n - full_steps;
-      e = e1 - 1;
-      h = hk * rep + rem / ns_last;
-      sub = rem % ns_last;
+  // Step cursor (CSC entry, q head, slice), advanced without divisions.
+  struct Cursor {
+    int e, h, sub;
+  };
+  auto advance = [&](Cursor u) {
+    const int ns = u.e == e1 - 1 ? ns_last : C::NSUB;
+    if (++u.sub == ns) {
+      u.sub = 0;
+      if (++u.h == (hk + 1) * rep) {
+        u.h = hk * rep;
+        ++u.e;
+      }
     }
+    return u;
   };
 
   // CSC entries (q-tile index | kind << 30) of a 64-entry window in one register,
@@ -272,9 +260,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
                    st_next + C::TILE_BYTES + ((j - NT_LOADS) * (C::NT / 64) + w) * 1024);
     }
   };
-  auto issue = [&](int n, int q_tile) {
-    int e, h, sub;
-    decode(n, e, h, sub);
+  auto issue = [&](int n, const Cursor& u, int q_tile) {
+    const int h = u.h, sub = u.sub;
     const int64_t q0 = int64_t(q_tile) * kTileM + sub * C::BMS;
     const int nvalid = ntok - q0 < C::BMS ? int(ntok - q0) : C::BMS;
     const T* qp = Qg + q0 * ldq + int64_t(h) * D;
@@ -320,16 +307,29 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     }
   };
 
+  Cursor cur{e0, hk * rep, 0};
   if (n_steps > 0) {
-    int e, h, sub;
-    decode(0, e, h, sub);
-    issue(0, int(entry(e) & 0x3fffffffu));
+    issue(0, cur, int(entry(e0) & 0x3fffffffu));
     if constexpr (C::kDma) {
 #pragma unroll
       for (int j = 0; j < 2 * NT_LOADS; ++j) dma_part(j);
     } else {
       commit(0);
     }
+  }
+  {  // K and V stay in registers; their loads overlap the first stage's
+    const int64_t off = (kvrow * hkv + hk) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kf[s] = kvvalid ? frag_load(Kg + off + 16 * s) : frag_zero<T>();
+      if constexpr (kDK) vf[s] = kvvalid ? frag_load(Vg + off + 16 * s) : frag_zero<T>();
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      mark_ready(kf[s]);
+      if constexpr (kDK) mark_ready(vf[s]);
+    }
+    mark_ready(reach);
   }
   if constexpr (!C::kDma) __syncthreads();
 
@@ -341,19 +341,16 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       wait_vmcnt<0>();
       __syncthreads();
     }
-    int e, h, sub;
-    decode(n, e, h, sub);
-    const uint32_t ent = entry(e);
+    const uint32_t ent = entry(cur.e);
     const bool partial = (ent >> 30) == 1;
-    const int q0i = int(ent & 0x3fffffffu) * kTileM + sub * C::BMS;
+    const int q0i = int(ent & 0x3fffffffu) * kTileM + cur.sub * C::BMS;
+    const Cursor nxt = advance(cur);
     if (n + 1 < n_steps) {
-      int e1n, h1n, s1n;
-      decode(n + 1, e1n, h1n, s1n);
-      if (e1n - e0 - wbase >= 64) {  // next window (a vector load; rare)
-        window_load(e1n - e0);
+      if (nxt.e - e0 - wbase >= 64) {  // next window (a vector load; rare)
+        window_load(nxt.e - e0);
         mark_ready(*reinterpret_cast<int32_t*>(&wreg));
       }
-      issue(n + 1, int(entry(e1n) & 0x3fffffffu));
+      issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu));
     } else if constexpr (C::kDma) {
       st_next = smem + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
       rq = dma_rsrc(Qg, 0);
@@ -376,6 +373,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         f32x16 sacc = zero16(), pacc = zero16();
         const T* qr = Qs + (32 * qb + l32) * C::NS + 8 * half;
         const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
+        // the rows' LSE (log2 units) and D, read before the products so that their
+        // latency passes under them
+        f32x4 l2v[4], dlv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ql = 32 * qb + g * 8 + half * 4;
+          l2v[g] = *reinterpret_cast<const f32x4*>(Ls + ql);
+          if constexpr (kDK) dlv[g] = *reinterpret_cast<const f32x4*>(Dsh + ql);
+        }
         if constexpr (C::kDma) {
           // Q and dO fragments read PF reduction steps ahead of their MFMAs
           constexpr int NS = D / 16, PF = 3;
@@ -402,6 +408,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
                 if ((j * NS) / (2 * NT_LOADS) == s) dma_part(j);
             }
           }
+          __builtin_amdgcn_sched_group_barrier(0x100, kDK ? 8 : 4, 1);  // LSE / D
           __builtin_amdgcn_sched_group_barrier(0x100, RD * (PF - 1), 1);
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
@@ -417,12 +424,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         }
         float pv[16], ds[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ql = 32 * qb + g * 8 + half * 4;
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(Ls + ql);
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) pv[4 * g + u] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + u], c, -l2[u]));
-        }
+          for (int u = 0; u < 4; ++u)
+            pv[4 * g + u] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + u], c, -l2v[g][u]));
         if (partial) {  // uniform branch; full tiles skip the mask
 #pragma unroll
           for (int ii = 0; ii < 16; ++ii)
@@ -430,11 +435,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         }
         if constexpr (kDK) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 dl = *reinterpret_cast<const f32x4*>(Dsh + 32 * qb + g * 8 + half * 4);
+          for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) ds[4 * g + u] = pv[4 * g + u] * (pacc[4 * g + u] - dl[u]);
-          }
+            for (int u = 0; u < 4; ++u) ds[4 * g + u] = pv[4 * g + u] * (pacc[4 * g + u] - dlv[g][u]);
         }
         if constexpr (C::kDma) {
           // dV += dO^T P and dK += Q^T dS over these 32 queries (two 16-query
@@ -522,9 +525,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       if (n + 1 < n_steps) commit(b ^ 1);
       __syncthreads();
     }
+    cur = nxt;
   }
   if constexpr (C::kDma) wait_vmcnt<0>();  // no load into LDS outlives the work-group
-
 
   if (kvvalid) {
     G* dkp = static_cast<G*>(p.dk) + (kvrow * hkv + hk) * D;
@@ -576,7 +579,11 @@ struct DqCfg {
   static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
 };
 
-template <typename T, typename G, int D, int MODE>
+// PRE: the kernel also does the preparation of its rows (bwd_pre_kernel's work): it
+// holds dO for exactly its (row, head) pairs, so it loads O beside it, forms D and
+// LSE in log2 units in registers and writes them to the workspace for the dK/dV
+// kernel, which then runs after it.
+template <typename T, typename G, int D, int MODE, bool PRE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, D>::WAVES_PER_EU)))
 void dq_kernel(BwdParams p) {
   using C = DqCfg<T, D>;
@@ -603,24 +610,8 @@ void dq_kernel(BwdParams p) {
   const T* Kg = static_cast<const T*>(p.k);
   const T* Vg = static_cast<const T*>(p.v);
 
-  Frag<T> qf[D / 16], gf[D / 16];
-  {
-    const int64_t off = (qrow * hq + h) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      qf[s] = qvalid ? frag_load(Qg + off + 16 * s) : frag_zero<T>();
-      gf[s] = qvalid ? frag_load(Gg + off + 16 * s) : frag_zero<T>();
-    }
-  }
-  float l2 = qvalid ? p.L2[int64_t(h) * ntok + qrow] : INFINITY;
-  float dl = qvalid ? p.Dl[int64_t(h) * ntok + qrow] : 0.f;
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    mark_ready(qf[s]);
-    mark_ready(gf[s]);
-  }
-  mark_ready(l2);
-  mark_ready(dl);
+  Frag<T> qf[D / 16], gf[D / 16];  // loaded below, once the first tile's loads are in flight
+  float l2 = INFINITY, dl = 0.f;
   f32x16 adq[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adq[db] = zero16();
@@ -689,6 +680,41 @@ void dq_kernel(BwdParams p) {
   if (n_steps > 0) {
     issue(0, int(entry(0) & 0x3fffffffu));
     if constexpr (!C::kDma) commit(0);
+  }
+  {  // Q and dO stay in registers; their loads overlap the first tile's
+    const int64_t off = (qrow * hq + h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qf[s] = qvalid ? frag_load(Qg + off + 16 * s) : frag_zero<T>();
+      gf[s] = qvalid ? frag_load(Gg + off + 16 * s) : frag_zero<T>();
+    }
+    if constexpr (PRE) {
+      // D = sum_d dO * O over the row (each lane half holds half of it) and LSE in
+      // log2 units (+inf on rows that saw no key, so their probabilities are 0)
+      const T* Og = static_cast<const T*>(p.o);
+      float lse = -INFINITY, part = 0.f;
+      if (qvalid) {
+        lse = p.lse[int64_t(h) * ntok + qrow];
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) part += frag_dot(frag_load(Og + off + 16 * s), gf[s]);
+      }
+      dl = part + __shfl_xor(part, 32);
+      l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+      if (qvalid && half == 0) {
+        p.Dl[int64_t(h) * ntok + qrow] = dl;
+        p.L2[int64_t(h) * ntok + qrow] = l2;
+      }
+    } else if (qvalid) {
+      l2 = p.L2[int64_t(h) * ntok + qrow];
+      dl = p.Dl[int64_t(h) * ntok + qrow];
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      mark_ready(qf[s]);
+      mark_ready(gf[s]);
+    }
+    mark_ready(l2);
+    mark_ready(dl);
   }
   if constexpr (!C::kDma) __syncthreads();
 
@@ -895,7 +921,21 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.c = s.scale * kLog2e;
   const int rep = s.hq / s.hkv;
 
-  if (stages & PSA_STAGE_PREPARE) {
+  // PREPARE together with DQ: the dQ kernel does the preparation of its rows and
+  // runs first; dK/dV then reads what it wrote.
+  const bool fused = (stages & PSA_STAGE_PREPARE) && (stages & PSA_STAGE_DQ);
+  auto launch_dq = [&](auto pre_t) {
+    constexpr bool PRE = decltype(pre_t)::value;
+    p.n_work = map.nq * s.hq;
+    p.chunk = rep * 2;
+    const int64_t per = 8 * int64_t(p.chunk);
+    const int64_t grid = (p.n_work + per - 1) / per * per;
+    hipLaunchKernelGGL((dq_kernel<T, G, D, MODE, PRE>), dim3(unsigned(grid)), dim3(256), 0,
+                       stream, p);
+  };
+  if (fused) {
+    launch_dq(std::true_type{});
+  } else if (stages & PSA_STAGE_PREPARE) {
     const int64_t rows = s.T * s.hq;
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(unsigned((rows + 15) / 16)), dim3(256), 0,
                        stream, p);
@@ -915,13 +955,7 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
                          stream, p);
     }
   }
-  if (stages & PSA_STAGE_DQ) {
-    p.n_work = map.nq * s.hq;
-    p.chunk = rep * 2;
-    const int64_t per = 8 * int64_t(p.chunk);
-    const int64_t grid = (p.n_work + per - 1) / per * per;
-    hipLaunchKernelGGL((dq_kernel<T, G, D, MODE>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
-  }
+  if ((stages & PSA_STAGE_DQ) && !fused) launch_dq(std::false_type{});
   return hipGetLastError();
 }
 

@@ -155,6 +155,19 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// Maximum of x over lanes l and l ^ 32 (the two halves of a wave) in VALU, without an
+// LDS round trip.  v_permlane32_swap a, b exchanges the upper half of a with the lower
+// half of b; from two copies of x it leaves (x_lo, x_lo) in a and (x_hi, x_hi) in b, and
+// their elementwise max is max(x_l, x_(l^32)) in every lane.  It is written as inline
+// assembly because the compiler's model of the intrinsic folds the two results of a
+// swap of one value into one.  The s_nop gives the two wait states a permlane needs
+// after a VALU write of its operands.
+__device__ __forceinline__ float max_halves(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
 // The mask in interval form: key kv is visible to row q iff kv <= q < end[kv], i.e.
 // (unsigned)(q - kv) < reach[kv] with reach = end - kv >= 0 (0 for a pad: never
 // visible).  One compare, used as a select (no short-circuit branch).
@@ -185,6 +198,24 @@ __device__ __forceinline__ int acc_row(int i, int half) { return (i >> 2) * 8 + 
 __device__ __forceinline__ int perm_pos(int r) {
   const int g = (r >> 2) & 3;
   return (r & ~15) + (((g & 1) << 1) | (g >> 1)) * 4 + (r & 3);
+}
+
+// Sum of the 8 elementwise products of two fragments, in fp32.
+__device__ __forceinline__ float frag_dot(const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc = fmaf(__builtin_bit_cast(float, a.v[j] << 16), __builtin_bit_cast(float, b.v[j] << 16), acc);
+    acc = fmaf(__builtin_bit_cast(float, a.v[j] & 0xffff0000u),
+               __builtin_bit_cast(float, b.v[j] & 0xffff0000u), acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_dot(const Frag<float>& a, const Frag<float>& b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = fmaf(a.lo[j], b.lo[j], fmaf(a.hi[j], b.hi[j], acc));
+  return acc;
 }
 
 // ---------------------------------------------------------------------------

@@ -103,14 +103,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
 
-  Frag<T> qf[D / 16];
-  {
-    const T* qp = Q + (qrow * hq + h) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = qvalid ? frag_load(qp + 16 * s) : frag_zero<T>();
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) mark_ready(qf[s]);
-  }
+  Frag<T> qf[D / 16];  // loaded below, once the first tile's loads are in flight
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -185,6 +178,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   if (n_steps > 0) {
     issue(0, int(entry(0) & 0x3fffffffu));
     if constexpr (!C::kDma) commit(0);
+  }
+  {  // Q stays in registers; its loads overlap the first tile's
+    const T* qp = Q + (qrow * hq + h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = qvalid ? frag_load(qp + 16 * s) : frag_zero<T>();
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) mark_ready(qf[s]);
   }
   if constexpr (!C::kDma) __syncthreads();
 
@@ -266,12 +266,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       }
       if (partial) {  // uniform branch; full tiles skip the mask
         const int qd = qrow_i - kv0i;  // q - kv for the sub-step's first key
+        // all of this lane's end[] (or reach) values first, so that their LDS reads
+        // are in flight together
+        int4 evs[C::BN / 32][4];
+#pragma unroll
+        for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            evs[kb][g] = *reinterpret_cast<const int4*>(Es + 32 * kb + g * 8 + half * 4);
 #pragma unroll
         for (int kb = 0; kb < C::BN / 32; ++kb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int kvl = 32 * kb + g * 8 + half * 4;
-            const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
+            const int4 ev = evs[kb][g];
             const int rv[4] = {ev.x, ev.y, ev.z, ev.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       for (int kb = 0; kb < C::BN / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      mx = max_halves(mx) * c;
       // raise the running max only when it grows by more than the slack
       const bool grow = mx > m + kRescaleSlack || (m == -INFINITY && mx > -INFINITY);
       if (__ballot(grow)) {  // wave-uniform branch

@@ -137,6 +137,34 @@ def test_bwd_flags_rejected():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "bf16"), (256, "bf16")])
+def test_stage_orders_agree(d, dtype):
+    """psa_bwd runs dQ with the preparation of its rows first, then dK/dV; the stages run
+    one by one (prepare, dK/dV, dQ) must give the same gradients, both at the parity bar
+    against the oracle, with pad rows and partial tiles in the layout."""
+    lay = wl.tokens_layout([(70, [40, 25, 0]), (5, [60])], pad_multiple=128)
+    hq, hkv, seed = 4, 2, 11
+    say(f"stage orders: T={lay.T} d={d} {dtype}")
+    q, k, v, do = wl.make_tensors(lay.T, hq, hkv, d, dtype, 1.0, seed)
+    tdt = DT[dtype]
+    m = psa.layout_tile_map(lay, "cuda", dtype=tdt, d=d)
+    qd, kd, vd, dod = (x.cuda() for x in (q, k, v, do))
+    o, lse = psa.fwd(m, qd, kd, vd)
+    fused = psa.bwd(m, qd, kd, vd, o, lse, dod)
+    ws = torch.empty(psa.bwd_workspace_size(m, qd, kd), dtype=torch.uint8, device="cuda")
+    outs = tuple(torch.full(x.shape, float("nan"), device="cuda") for x in (qd, kd, vd))
+    for st in (psa.STAGE_PREPARE, psa.STAGE_DKDV, psa.STAGE_DQ):
+        psa.bwd(m, qd, kd, vd, o, lse, dod, workspace=ws, stages=st, out=outs)
+    torch.cuda.synchronize()
+    _, _, dq, dk, dv = oa.backward(meta_from_layout(lay), q, k, v, do)
+    for got in (fused, outs):
+        compare("dq", got[0], dq, tdt)
+        compare("dk", got[1], dk, tdt)
+        compare("dv", got[2], dv, tdt)
+    for a, b in zip(fused, outs):  # the same sums up to the order of D's fp32 additions
+        assert torch.allclose(a, b, rtol=1e-4, atol=1e-5)
+
+
 @pytest.mark.parametrize("T", [1, 2, 31, 127, 128, 129, 300])
 def test_single_causal_sequence_ragged(T):
     """One group with no completion = plain causal attention, at ragged lengths."""
