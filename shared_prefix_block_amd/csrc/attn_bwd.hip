@@ -786,16 +786,22 @@ void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) pv[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2));
         if (partial) {  // uniform branch; full tiles skip the mask
+          // this lane's end[] (or reach) values first, their LDS reads in flight
+          // together; the two tests combined without a short circuit, so no test
+          // turns into a branch around a read
+          int4 evs[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            evs[g] = *reinterpret_cast<const int4*>(Es + 32 * kb + g * 8 + half * 4);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int kvl = 32 * kb + g * 8 + half * 4;
-            const int4 ev = *reinterpret_cast<const int4*>(Es + kvl);
-            const int rv[4] = {ev.x, ev.y, ev.z, ev.w};
+            const int rv[4] = {evs[g].x, evs[g].y, evs[g].z, evs[g].w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               bool keep;
               if constexpr (C::kDma)  // raw end[]: kv <= q < end
-                keep = (kvl + u <= qd) && (qrow_i < rv[u]);
+                keep = (kvl + u <= qd) & (qrow_i < rv[u]);
               else  // reach = end - kv
                 keep = visible_u(qd - kvl - u, rv[u]);
               pv[4 * g + u] = keep ? pv[4 * g + u] : 0.f;

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
             for (int u = 0; u < 4; ++u) {
               bool keep;
               if constexpr (C::kDma)  // raw end[]: kv <= q < end
-                keep = (kvl + u <= qd) && (qrow_i < rv[u]);
+                keep = (kvl + u <= qd) & (qrow_i < rv[u]);
               else  // reach = end - kv
                 keep = visible_u(qd - kvl - u, rv[u]);
               sv[kb][4 * g + u] = keep ? sv[kb][4 * g + u] : -INFINITY;
