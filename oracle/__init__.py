@@ -7,5 +7,6 @@ It shares no code with the HIP library and never imports it.
 * ``oracle.mask``      - the visibility rule, element by element, from the metadata
 * ``oracle.attention`` - dense masked softmax attention and its analytic gradients
 * ``oracle.tilemap``   - full / partial / empty tile classification, CSR and CSC
+* ``oracle.fold``      - the rollout fold (flat ids, labels, positions, metadata) and unfold
 """
-from . import attention, mask, tilemap  # noqa: F401
+from . import attention, fold, mask, tilemap  # noqa: F401
