@@ -172,6 +172,60 @@ def traffic_summary(pmc_dir: str, config: int, calib_mb: int, command: str) -> N
         print(path, e["bytes_per_launch"])
 
 
+def fold_bench(cfg, lay, steps: int, warmup: int) -> dict:
+    """Fold of the workload's rollout groups (random token ids) and the unfold of a
+    folded [T, hq, d] tensor back to the samples, timed with HIP events on the launch
+    stream; both are pure data movement, measured against the HBM roofline on their
+    algorithmic bytes (fold: the real tokens read once, six [T] outputs written; unfold:
+    every unfolded row read once and written once)."""
+    import numpy as np
+    import torch
+
+    from shared_prefix_block_amd import psa
+
+    dev = torch.device("cuda:0")
+    r = psa.Rollouts([p for p, _ in lay.specs], [rs for _, rs in lay.specs])
+    gen = torch.Generator("cpu").manual_seed(cfg.idx)
+    n_prompt = int(r.prompt_len.sum())
+    pt = torch.randint(0, 150000, (n_prompt,), generator=gen, dtype=torch.int32).to(dev)
+    ct = torch.randint(0, 150000, (r.fold_len - n_prompt,), generator=gen,
+                       dtype=torch.int32).to(dev)
+    src = torch.randn(lay.T, cfg.hq, cfg.d, generator=gen).to(torch.bfloat16).to(dev)
+    ws = psa.fold_workspace(r, dev)
+    dst = torch.empty((r.unfold_len, cfg.hq, cfg.d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    ms_fold = timed(lambda: psa.fold_rollouts(r, pt, ct, lay.T, workspace=ws))
+    ms_unfold = timed(lambda: psa.unfold_rows(r, src, out=dst, workspace=ws))
+    fold_bytes = 4 * r.fold_len + 21 * lay.T
+    unfold_bytes = 2 * r.unfold_len * cfg.hq * cfg.d * 2
+    gbs = unfold_bytes / (ms_unfold * 1e-3) / 1e9
+    return {"metric": "fold / unfold throughput (HBM GB/s)", "value": round(gbs, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "higher_is_better": True, "dtype": "int32 / bf16 rows", "data": "synthetic",
+            "config": {"workload": describe(cfg, lay), "T": lay.T, "T_real": lay.T_real,
+                       "unfolded_rows": r.unfold_len, "row_bytes": cfg.hq * cfg.d * 2},
+            "fold_ms": round(ms_fold, 4),
+            "fold_gbs": round(fold_bytes / (ms_fold * 1e-3) / 1e9, 1),
+            "unfold_ms": round(ms_unfold, 4),
+            "roofline": {"kernel": "k_unfold", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "algorithmic_bytes_per_launch": unfold_bytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +243,10 @@ def main():
     ap.add_argument("--traffic-summary", metavar="PMC_DIR",
                     help="no timing: write the profiles/traffic_*.json files from the two "
                          "rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) under PMC_DIR")
+    ap.add_argument("--fold", action="store_true",
+                    help="time the fold of the workload's rollout groups and the unfold of a "
+                         "folded [T, hq, d] tensor instead of the attention step (token-form "
+                         "workloads)")
     ap.add_argument("--traffic-command", default="",
                     help="with --traffic-summary: the command line the passes ran, recorded")
     args = ap.parse_args()
@@ -214,6 +272,11 @@ def main():
     torch.cuda.set_device(dev)
     cfg = wl.CONFIGS[args.config]
     lay = wl.layout_for(cfg)
+    if args.fold:
+        if lay.kind != "tokens":
+            sys.exit("--fold needs a token-form workload (rollout groups)")
+        print(json.dumps(fold_bench(cfg, lay, args.steps, args.warmup)), flush=True)
+        return
     q, k, v, do = wl.config_tensors(cfg, lay)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
     backward = cfg.passes != "fwd"

@@ -149,7 +149,9 @@ void psa_tile_map_destroy(psa_tile_map* map);
 
 /*
  * Forward: O = softmax(scale * Q K^T masked) V per q head, and LSE.
- * Device pointers: q, k, v (inputs), o, lse (outputs, fully overwritten).
+ * Device pointers: q, k, v (inputs), o, lse (outputs, fully overwritten).  lse may be
+ * NULL for a forward whose LSE is not needed (no backward follows, e.g. the extra
+ * no-grad log-prob passes of a policy-gradient step): then only O is written.
  * scale <= 0 selects 1/sqrt(d).  T must equal the map's T; the map's tile shape must
  * be psa_tile_shape(PSA_PASS_FWD, dtype, d).  Asynchronous on `stream`.
  * Errors: PSA_ERR_NULL, PSA_ERR_SHAPE, PSA_ERR_DTYPE, PSA_ERR_UNSUPPORTED,
@@ -213,6 +215,61 @@ psa_status psa_bwd_stages(const psa_tile_map* map, psa_dtype dtype, psa_dtype gr
                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
                           void* workspace, size_t workspace_bytes, int32_t flags,
                           void* stream);
+
+/*
+ * Fold of rollout groups into the flat shared-prefix layout (Automodel PR #2564 page:
+ * PR description and "Changelog", fold_shared_prefix_rollouts; the commit note on
+ * pre-shifted labels).  Group g, one prompt and the completions sampled from it, is
+ * stored once as [prompt_g | c_g0 | c_g1 | ...]; groups follow one another; positions
+ * from the folded length up to T are pad tokens.
+ *   n_groups; host tables: prompt_len[n_groups]; comp_ptr[n_groups + 1] (group g owns
+ *     completions comp_ptr[g] .. comp_ptr[g+1]-1, comp_ptr[0] = 0); comp_len[n_comp],
+ *     n_comp = comp_ptr[n_groups].  Lengths may be 0.
+ *   device inputs: prompt_tok (int32, the prompts' tokens concatenated in group order),
+ *     comp_tok (int32, the completions' tokens concatenated in completion order).
+ *   T >= the folded length (sum of all lengths).
+ *   device outputs, [T] each, fully written; NULL skips one (at least one is given):
+ *     input_ids   the flat tokens (pad_id on pads);
+ *     labels      pre-shifted next-token labels: the next flat token of the same group,
+ *                 except ignore_index on the last token of every completion, on a
+ *                 prompt's last token when the group has no completion token, and on
+ *                 pads (a prompt's last token is labelled with the first token of the
+ *                 group's first non-empty completion, its flat successor);
+ *     position_ids  a prompt's tokens 0 .. P-1; a completion's P .. P+R-1 (each
+ *                 completion continues its prompt as if alone); 0 on pads;
+ *     group, suffix, is_prefix  the token-form input of psa_build_tile_map_tokens: group
+ *                 g, suffix -1 and is_prefix 1 on prompt tokens, suffix = the global
+ *                 completion index on completion tokens, -1 / -1 / 0 on pads.
+ *   workspace: device scratch of psa_fold_workspace_size bytes (contents undefined on
+ *     entry and exit; the call uploads its segment table there, on `stream`).
+ * Asynchronous on `stream`.  Errors (nothing is launched): PSA_ERR_NULL, PSA_ERR_SHAPE (T
+ * too short or out of range), PSA_ERR_LAYOUT (negative lengths, comp_ptr not starting
+ * at 0 or decreasing), PSA_ERR_WORKSPACE, PSA_ERR_HIP.
+ */
+psa_status psa_fold_workspace_size(int64_t n_groups, int64_t n_comp, size_t* bytes);
+psa_status psa_fold_rollouts(int64_t n_groups, const int32_t* prompt_len,
+                             const int32_t* comp_ptr, const int32_t* comp_len,
+                             const int32_t* prompt_tok, const int32_t* comp_tok, int64_t T,
+                             int32_t pad_id, int32_t ignore_index, int32_t* input_ids,
+                             int32_t* labels, int32_t* position_ids, int32_t* group,
+                             int32_t* suffix, uint8_t* is_prefix, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Unfold: the rows of a folded per-token tensor (src, T rows of row_bytes bytes, the
+ * layout psa_fold_rollouts writes for the same tables) gathered into the per-sample
+ * layout, to hand per-token outputs or log-probabilities back to the samples: sample
+ * (g, i) is [prompt_g | c_gi]; samples follow in completion order; dst receives
+ * sum over completions of (P_g + R_gi) rows.  A group without completions gives no
+ * sample.  row_bytes: a positive multiple of 4 (rows move as 16-byte words when
+ * row_bytes, src and dst allow it).  Device pointers src, dst (4-byte aligned);
+ * workspace as psa_fold_rollouts.  Asynchronous on `stream`.  Errors as
+ * psa_fold_rollouts.
+ */
+psa_status psa_unfold_rows(int64_t n_groups, const int32_t* prompt_len,
+                           const int32_t* comp_ptr, const int32_t* comp_len, int64_t T,
+                           int64_t row_bytes, const void* src, void* dst, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsa.so")
 
-SOURCES = ["api.cpp", "tilemap.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["api.cpp", "tilemap.hip", "attn_fwd.hip", "attn_bwd.hip", "fold.hip"]
 ARCH = "gfx950"
 
 

@@ -528,7 +528,8 @@ psa_status psa_fwd(const psa_tile_map* map, psa_dtype dtype, int64_t T, int32_t 
   psa_status st = check_attn_args(map, dtype, T, hq, hkv, d, scale, PSA_PASS_FWD);
   if (st != PSA_OK) return st;
   if (T == 0) return PSA_OK;
-  if (!q || !k || !v || !o || !lse) return psa_set_error(PSA_ERR_NULL, "tensor pointer is NULL");
+  // lse may be NULL: a forward whose LSE nobody reads (no backward follows)
+  if (!q || !k || !v || !o) return psa_set_error(PSA_ERR_NULL, "tensor pointer is NULL");
   AttnShape s{T, hq, hkv, d, scale > 0.f ? scale : 1.0f / std::sqrt(float(d))};
   hipError_t e = launch_fwd(*map, dtype, s, q, k, v, o, lse, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return psa_hip_error(e, "forward launch");
@@ -582,6 +583,176 @@ psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtyp
                    size_t workspace_bytes, void* stream) {
   return psa_bwd_stages(map, dtype, grad_dtype, T, hq, hkv, d, scale, q, k, v, o, lse, dout,
                         dq, dk, dv, workspace, workspace_bytes, PSA_STAGE_ALL, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Fold / unfold of rollout groups (fold.hip).  The host checks the length tables and
+// builds the segment table; it goes to the caller's workspace on the stream.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct Rollouts {
+  int64_t n_groups = 0, n_comp = 0, folded = 0;
+};
+
+psa_status check_rollouts(int64_t n_groups, const int32_t* prompt_len, const int32_t* comp_ptr,
+                          const int32_t* comp_len, Rollouts* r) {
+  if (n_groups < 0) return psa_set_error(PSA_ERR_SHAPE, "negative n_groups");
+  if (n_groups > 0 && (!prompt_len || !comp_ptr))
+    return psa_set_error(PSA_ERR_NULL, "length table is NULL");
+  if (n_groups > 0 && comp_ptr[0] != 0) return psa_set_error(PSA_ERR_LAYOUT, "comp_ptr[0] != 0");
+  int64_t folded = 0;
+  for (int64_t g = 0; g < n_groups; ++g) {
+    if (prompt_len[g] < 0) return psa_set_error(PSA_ERR_LAYOUT, "negative prompt length");
+    if (comp_ptr[g + 1] < comp_ptr[g])
+      return psa_set_error(PSA_ERR_LAYOUT, "comp_ptr decreases at group " + std::to_string(g));
+    folded += prompt_len[g];
+  }
+  const int64_t n_comp = n_groups > 0 ? comp_ptr[n_groups] : 0;
+  if (n_comp > 0 && !comp_len) return psa_set_error(PSA_ERR_NULL, "comp_len is NULL");
+  for (int64_t c = 0; c < n_comp; ++c) {
+    if (comp_len[c] < 0) return psa_set_error(PSA_ERR_LAYOUT, "negative completion length");
+    folded += comp_len[c];
+  }
+  if (folded > kMaxT) return psa_set_error(PSA_ERR_SHAPE, "folded length out of range");
+  r->n_groups = n_groups;
+  r->n_comp = n_comp;
+  r->folded = folded;
+  return PSA_OK;
+}
+
+size_t fold_table_bytes(int64_t n_groups, int64_t n_comp) {
+  const size_t fold = size_t(n_groups + n_comp + 1) * sizeof(FoldSeg);
+  const size_t unfold = size_t(2 * n_comp) * sizeof(UnfoldSeg);
+  return align_up(std::max<size_t>(std::max(fold, unfold), 1), 256);
+}
+
+template <typename S>
+psa_status upload_table(const std::vector<S>& table, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  const size_t need = table.size() * sizeof(S);
+  if (!workspace || workspace_bytes < need)
+    return psa_set_error(PSA_ERR_WORKSPACE, "workspace smaller than psa_fold_workspace_size");
+  hipError_t e = hipMemcpyAsync(workspace, table.data(), need, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return psa_hip_error(e, "segment table upload");
+  return PSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+psa_status psa_fold_workspace_size(int64_t n_groups, int64_t n_comp, size_t* bytes) {
+  if (!bytes) return psa_set_error(PSA_ERR_NULL, "bytes is NULL");
+  if (n_groups < 0 || n_comp < 0) return psa_set_error(PSA_ERR_SHAPE, "negative count");
+  *bytes = fold_table_bytes(n_groups, n_comp);
+  return PSA_OK;
+}
+
+psa_status psa_fold_rollouts(int64_t n_groups, const int32_t* prompt_len, const int32_t* comp_ptr,
+                             const int32_t* comp_len, const int32_t* prompt_tok,
+                             const int32_t* comp_tok, int64_t T, int32_t pad_id,
+                             int32_t ignore_index, int32_t* input_ids, int32_t* labels,
+                             int32_t* position_ids, int32_t* group, int32_t* suffix,
+                             uint8_t* is_prefix, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Rollouts r;
+  psa_status st = check_rollouts(n_groups, prompt_len, comp_ptr, comp_len, &r);
+  if (st != PSA_OK) return st;
+  if (T < r.folded || T > kMaxT)
+    return psa_set_error(PSA_ERR_SHAPE, "T must lie in [folded length, 2^31-4096]");
+  int64_t n_prompt_tok = 0, n_comp_tok = 0;
+  for (int64_t g = 0; g < n_groups; ++g) n_prompt_tok += prompt_len[g];
+  n_comp_tok = r.folded - n_prompt_tok;
+  if ((n_prompt_tok > 0 && !prompt_tok) || (n_comp_tok > 0 && !comp_tok))
+    return psa_set_error(PSA_ERR_NULL, "token buffer is NULL");
+  if (!input_ids && !labels && !position_ids && !group && !suffix && !is_prefix)
+    return psa_set_error(PSA_ERR_NULL, "no output requested");
+
+  // segments in flat order: each group's prompt, then its completions; the pad tail
+  std::vector<FoldSeg> segs;
+  segs.reserve(size_t(n_groups + r.n_comp + 1));
+  int64_t flat = 0, psrc = 0, csrc = 0, max_len = 0;
+  for (int64_t g = 0; g < n_groups; ++g) {
+    // the label of the prompt's last token: the first token of the group's first
+    // non-empty completion (its flat successor), if any
+    int64_t first = -1, c_off = csrc;
+    for (int32_t c = comp_ptr[g]; c < comp_ptr[g + 1]; ++c) {
+      if (comp_len[c] > 0) {
+        first = c_off;
+        break;
+      }
+      c_off += comp_len[c];
+    }
+    FoldSeg p{flat, prompt_len[g], psrc, first, kFoldPrompt, int32_t(g), -1, 0};
+    segs.push_back(p);
+    flat += prompt_len[g];
+    psrc += prompt_len[g];
+    max_len = std::max<int64_t>(max_len, prompt_len[g]);
+    for (int32_t c = comp_ptr[g]; c < comp_ptr[g + 1]; ++c) {
+      FoldSeg s{flat, comp_len[c], csrc, -1, kFoldComp, int32_t(g), c, prompt_len[g]};
+      segs.push_back(s);
+      flat += comp_len[c];
+      csrc += comp_len[c];
+      max_len = std::max<int64_t>(max_len, comp_len[c]);
+    }
+  }
+  segs.push_back(FoldSeg{flat, T - flat, 0, -1, kFoldPad, -1, -1, 0});
+  max_len = std::max<int64_t>(max_len, T - flat);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = upload_table(segs, workspace, workspace_bytes, s)) != PSA_OK) return st;
+  hipError_t e = launch_fold(static_cast<const FoldSeg*>(workspace), int64_t(segs.size()),
+                             max_len, prompt_tok, comp_tok, pad_id, ignore_index, input_ids,
+                             labels, position_ids, group, suffix, is_prefix, s);
+  if (e != hipSuccess) return psa_hip_error(e, "fold launch");
+  return PSA_OK;
+}
+
+psa_status psa_unfold_rows(int64_t n_groups, const int32_t* prompt_len, const int32_t* comp_ptr,
+                           const int32_t* comp_len, int64_t T, int64_t row_bytes,
+                           const void* src, void* dst, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  Rollouts r;
+  psa_status st = check_rollouts(n_groups, prompt_len, comp_ptr, comp_len, &r);
+  if (st != PSA_OK) return st;
+  if (T < r.folded || T > kMaxT)
+    return psa_set_error(PSA_ERR_SHAPE, "T must lie in [folded length, 2^31-4096]");
+  if (row_bytes <= 0 || row_bytes % 4 != 0)
+    return psa_set_error(PSA_ERR_SHAPE, "row_bytes must be a positive multiple of 4");
+  if (r.n_comp > 0 && (!src || !dst)) return psa_set_error(PSA_ERR_NULL, "src or dst is NULL");
+
+  // per sample (g, i): its prompt rows, then its completion rows
+  std::vector<UnfoldSeg> segs;
+  segs.reserve(size_t(2 * r.n_comp));
+  int64_t flat = 0, out = 0, max_bytes = 0;
+  for (int64_t g = 0; g < n_groups; ++g) {
+    const int64_t p_start = flat;
+    int64_t c_start = flat + prompt_len[g];
+    for (int32_t c = comp_ptr[g]; c < comp_ptr[g + 1]; ++c) {
+      const int64_t pb = int64_t(prompt_len[g]) * row_bytes, cb = int64_t(comp_len[c]) * row_bytes;
+      if (pb > 0) segs.push_back(UnfoldSeg{p_start * row_bytes, out * row_bytes, pb, 0});
+      out += prompt_len[g];
+      if (cb > 0) segs.push_back(UnfoldSeg{c_start * row_bytes, out * row_bytes, cb, 0});
+      out += comp_len[c];
+      c_start += comp_len[c];
+      max_bytes = std::max(max_bytes, std::max(pb, cb));
+    }
+    flat = c_start;
+  }
+  if (segs.empty()) return PSA_OK;
+  const bool w16 = row_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+  if (!w16 && (reinterpret_cast<uintptr_t>(src) % 4 != 0 || reinterpret_cast<uintptr_t>(dst) % 4 != 0))
+    return psa_set_error(PSA_ERR_SHAPE, "src and dst must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = upload_table(segs, workspace, workspace_bytes, s)) != PSA_OK) return st;
+  hipError_t e = launch_unfold(static_cast<const UnfoldSeg*>(workspace), int64_t(segs.size()),
+                               max_bytes, src, dst, w16, s);
+  if (e != hipSuccess) return psa_hip_error(e, "unfold launch");
+  return PSA_OK;
 }
 
 }  // extern "C"

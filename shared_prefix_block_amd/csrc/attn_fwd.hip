@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
                                      acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv,
                                      static_cast<T*>(nullptr)));
       }
-    if (half == 0)
+    if (half == 0 && p.lse)  // no LSE store for a forward without gradient
       p.lse[int64_t(h) * ntok + qrow] =
           lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   }

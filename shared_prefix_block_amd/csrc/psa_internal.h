@@ -94,3 +94,27 @@ hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype grad_dt, 
                       const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       void* workspace, int stages, bool split, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// fold.hip
+// ---------------------------------------------------------------------------
+// One run of flat positions of the folded layout: a group's prompt, a completion, or
+// the pad tail.  src indexes prompt_tok (prompt) or comp_tok (completion); last_src
+// is the comp_tok index of the label of the run's last token, or -1 (masked).
+constexpr int32_t kFoldPrompt = 0, kFoldComp = 1, kFoldPad = 2;
+struct FoldSeg {
+  int64_t flat_start, len, src, last_src;
+  int32_t kind, group, suffix, pos_base;
+};
+// One contiguous byte range copied by the unfold.
+struct UnfoldSeg {
+  int64_t src_byte, dst_byte, bytes, unused;
+};
+constexpr int64_t kUnfoldChunk = 16384;  // bytes per work-group
+hipError_t launch_fold(const FoldSeg* segs, int64_t n_segs, int64_t max_len,
+                       const int32_t* prompt_tok, const int32_t* comp_tok, int32_t pad_id,
+                       int32_t ignore, int32_t* input_ids, int32_t* labels,
+                       int32_t* position_ids, int32_t* group, int32_t* suffix,
+                       uint8_t* is_prefix, hipStream_t stream);
+hipError_t launch_unfold(const UnfoldSeg* segs, int64_t n_segs, int64_t max_bytes,
+                         const void* src, void* dst, bool words16, hipStream_t stream);

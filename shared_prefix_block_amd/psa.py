@@ -31,7 +31,8 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_LAYOUT
 EXPORTS = ["psa_abi_version", "psa_status_string", "psa_last_error", "psa_tile_shape",
            "psa_build_tile_map_tokens", "psa_build_tile_map_tree", "psa_tile_map_info_get",
            "psa_tile_map_export", "psa_tile_map_destroy", "psa_fwd", "psa_bwd_workspace_size",
-           "psa_bwd", "psa_bwd_stages"]
+           "psa_bwd", "psa_bwd_stages", "psa_fold_workspace_size", "psa_fold_rollouts",
+           "psa_unfold_rows"]
 STAGE_PREPARE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 BWD_SPLIT_PDS = 16  # option bit of psa_bwd_stages: P and dS as hi + lo bf16 pairs
 
@@ -85,6 +86,10 @@ def load() -> ctypes.CDLL:
                                        P, P, P, P, P, P, P, P, SZ, P]),
             "psa_bwd_stages": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, I64, I32, I32, I32, F,
                                               P, P, P, P, P, P, P, P, P, P, SZ, I32, P]),
+            "psa_fold_workspace_size": (ctypes.c_int, [I64, I64, ctypes.POINTER(SZ)]),
+            "psa_fold_rollouts": (ctypes.c_int, [I64, P, P, P, P, P, I64, I32, I32, P, P, P, P,
+                                                 P, P, P, SZ, P]),
+            "psa_unfold_rows": (ctypes.c_int, [I64, P, P, P, I64, I64, P, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -235,14 +240,18 @@ def _check_qkv(q, k, v):
 
 def fwd(m: TileMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-        lse: Optional[torch.Tensor] = None):
-    """O [T, hq, d] (q's dtype) and LSE [hq, T] float32."""
+        lse: Optional[torch.Tensor] = None, with_lse: bool = True):
+    """O [T, hq, d] (q's dtype) and LSE [hq, T] float32.  with_lse=False: a forward
+    without gradient; no LSE is written and None is returned in its place."""
     lib = load()
     _check_qkv(q, k, v)
     T, hq, d = q.shape
     hkv = k.shape[1]
     o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty(hq, T, device=q.device, dtype=torch.float32) if lse is None else lse
+    if not with_lse:
+        lse_t = None
+    else:
+        lse_t = torch.empty(hq, T, device=q.device, dtype=torch.float32) if lse is None else lse
     with torch.cuda.device(q.device):
         _check(lib.psa_fwd(m.handle, _dtype_code(q.dtype), T, hq, hkv, d,
                            0.0 if scale is None else float(scale), _ptr(q), _ptr(k), _ptr(v),
@@ -323,3 +332,77 @@ def layout_tile_map(layout, device, dtype: torch.dtype = torch.bfloat16, d: int 
         return build_tile_map_tokens(g, s, p, block_m, block_n, dtype, d)
     return build_tile_map_tree(layout.node_lengths, layout.sample_paths, layout.T, device,
                                block_m, block_n, dtype, d)
+
+
+# ----------------------------------------------------------------------------
+# fold / unfold of rollout groups
+# ----------------------------------------------------------------------------
+class Rollouts:
+    """Host length tables of rollout groups: prompt_len[g], and per group the lengths
+    of its completions.  ``fold_len`` is the folded length (sum of all lengths)."""
+
+    def __init__(self, prompt_lens: Sequence[int], comp_lens: Sequence[Sequence[int]]):
+        if len(prompt_lens) != len(comp_lens):
+            raise ValueError("one completion list per prompt")
+        self.prompt_len = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+        self.comp_ptr = np.zeros(len(comp_lens) + 1, dtype=np.int32)
+        self.comp_ptr[1:] = np.cumsum([len(c) for c in comp_lens])
+        flat = [r for c in comp_lens for r in c]
+        self.comp_len = np.ascontiguousarray(flat if flat else [0], dtype=np.int32)
+        self.n_groups = len(prompt_lens)
+        self.n_comp = int(self.comp_ptr[-1])
+        self.fold_len = int(self.prompt_len.sum()) + int(sum(flat))
+        self.unfold_len = int(sum(self.prompt_len[g] * (self.comp_ptr[g + 1] - self.comp_ptr[g])
+                                  for g in range(self.n_groups))) + int(sum(flat))
+
+    def _tables(self):
+        np_ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        return (self.n_groups, np_ptr(self.prompt_len), np_ptr(self.comp_ptr),
+                np_ptr(self.comp_len))
+
+
+def fold_workspace(r: Rollouts, device) -> torch.Tensor:
+    lib = load()
+    b = ctypes.c_size_t(0)
+    _check(lib.psa_fold_workspace_size(r.n_groups, r.n_comp, ctypes.byref(b)))
+    return torch.empty(b.value, dtype=torch.uint8, device=device)
+
+
+def fold_rollouts(r: Rollouts, prompt_tok: torch.Tensor, comp_tok: torch.Tensor, T: int,
+                  pad_id: int = 0, ignore_index: int = -100,
+                  workspace: Optional[torch.Tensor] = None) -> dict:
+    """input_ids, labels, position_ids, group, suffix (int32 [T]) and is_prefix (uint8
+    [T]) of the folded layout; prompt_tok / comp_tok: int32 device tokens."""
+    lib = load()
+    dev = prompt_tok.device if prompt_tok.numel() else comp_tok.device
+    for t in (prompt_tok, comp_tok):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("token buffers must be contiguous int32")
+    out = {k: torch.empty(T, dtype=torch.int32, device=dev)
+           for k in ("input_ids", "labels", "position_ids", "group", "suffix")}
+    out["is_prefix"] = torch.empty(T, dtype=torch.uint8, device=dev)
+    ws = fold_workspace(r, dev) if workspace is None else workspace
+    with torch.cuda.device(dev):
+        _check(lib.psa_fold_rollouts(*r._tables(), _ptr(prompt_tok), _ptr(comp_tok), T, pad_id,
+                                     ignore_index, _ptr(out["input_ids"]), _ptr(out["labels"]),
+                                     _ptr(out["position_ids"]), _ptr(out["group"]),
+                                     _ptr(out["suffix"]), _ptr(out["is_prefix"]), _ptr(ws),
+                                     ws.numel(), _stream(dev)))
+    return out
+
+
+def unfold_rows(r: Rollouts, src: torch.Tensor, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows of a folded [T, ...] device tensor gathered per sample ([prompt_g | c_gi])."""
+    lib = load()
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    T = src.shape[0]
+    row_bytes = src[0].numel() * src.element_size() if T else 0
+    dst = torch.empty((r.unfold_len,) + tuple(src.shape[1:]), dtype=src.dtype,
+                      device=src.device) if out is None else out
+    ws = fold_workspace(r, src.device) if workspace is None else workspace
+    with torch.cuda.device(src.device):
+        _check(lib.psa_unfold_rows(*r._tables(), T, row_bytes, _ptr(src), _ptr(dst), _ptr(ws),
+                                   ws.numel(), _stream(src.device)))
+    return dst

@@ -116,3 +116,37 @@ def test_attention_argument_errors(lib):
     assert lib.psa_tile_map_info_get(None, None) == 1
     assert lib.psa_tile_map_export(None, *([None] * 8)) == 1
     lib.psa_tile_map_destroy(None)  # no-op
+
+
+def _fold_call(lib, n_groups, prompt_len, comp_ptr, comp_len, T, ws_bytes=1 << 20, outs=True):
+    arr = lambda a: (ctypes.c_int32 * len(a))(*a)  # noqa: E731
+    fake = ctypes.c_void_p(256)  # never dereferenced: every check below fails first
+    o = fake if outs else None
+    return lib.psa_fold_rollouts(n_groups, arr(prompt_len), arr(comp_ptr), arr(comp_len or [0]),
+                                 fake, fake, T, 0, -100, o, o, o, o, o, None, fake, ws_bytes, None)
+
+
+def test_fold_rejects_bad_tables(lib):
+    assert _fold_call(lib, -1, [1], [0, 1], [1], 8) == 2           # PSA_ERR_SHAPE
+    assert _fold_call(lib, 1, [2], [1, 1], [], 8) == 3             # comp_ptr[0] != 0
+    assert _fold_call(lib, 2, [2, 2], [0, 2, 1], [1, 1], 8) == 3   # decreasing comp_ptr
+    assert _fold_call(lib, 1, [-1], [0, 1], [1], 8) == 3           # negative prompt
+    assert _fold_call(lib, 1, [2], [0, 1], [-3], 8) == 3           # negative completion
+    assert _fold_call(lib, 1, [4], [0, 1], [5], 8) == 2            # T < folded length
+    assert _fold_call(lib, 1, [2], [0, 1], [1], 8, outs=False) == 1  # nothing to write
+    assert _fold_call(lib, 1, [2], [0, 1], [1], 8, ws_bytes=4) == 7  # PSA_ERR_WORKSPACE
+    assert b"workspace" in lib.psa_last_error()
+
+
+def test_unfold_rejects_bad_rows(lib):
+    arr = lambda a: (ctypes.c_int32 * len(a))(*a)  # noqa: E731
+    fake = ctypes.c_void_p(256)
+    call = lambda T, rb, ws=1 << 20: lib.psa_unfold_rows(  # noqa: E731
+        1, arr([2]), arr([0, 2]), arr([1, 1]), T, rb, fake, fake, fake, ws, None)
+    assert call(4, 6) == 2    # row_bytes not a multiple of 4
+    assert call(4, 0) == 2
+    assert call(3, 8) == 2    # T shorter than the folded length
+    assert call(4, 8, ws=8) == 7
+    b = ctypes.c_size_t(0)
+    assert lib.psa_fold_workspace_size(3, 7, ctypes.byref(b)) == 0 and b.value >= 256
+    assert lib.psa_fold_workspace_size(-1, 7, ctypes.byref(b)) == 2

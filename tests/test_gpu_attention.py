@@ -137,6 +137,25 @@ def test_bwd_flags_rejected():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (128, "bf16"), (256, "bf16")])
+def test_forward_without_lse(d, dtype):
+    """The no-grad forward (lse NULL) writes the same O as the full forward and leaves
+    the memory an LSE would go to alone."""
+    lay = wl.tokens_layout([(70, [40, 25]), (30, [50, 0])], pad_multiple=128)
+    say(f"forward without LSE: T={lay.T} d={d} {dtype}")
+    q, k, v, _ = wl.make_tensors(lay.T, 4, 2, d, dtype, 1.0, 5)
+    m = psa.layout_tile_map(lay, "cuda", dtype=DT[dtype], d=d)
+    qd, kd, vd = (x.cuda() for x in (q, k, v))
+    o1, lse1 = psa.fwd(m, qd, kd, vd)
+    guard = torch.full((4, lay.T), 7.0, device="cuda")
+    o2, lse2 = psa.fwd(m, qd, kd, vd, with_lse=False)
+    torch.cuda.synchronize()
+    assert lse2 is None
+    assert torch.equal(o1, o2)
+    assert bool((guard == 7.0).all())
+    compare("o", o2, oa.forward(meta_from_layout(lay), q, k, v)[0], DT[dtype])
+
+
 @pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "bf16"), (256, "bf16")])
 def test_stage_orders_agree(d, dtype):
     """psa_bwd runs dQ with the preparation of its rows first, then dK/dV; the stages run
