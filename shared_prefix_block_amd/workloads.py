@@ -220,6 +220,98 @@ def random_tree(rng: np.random.Generator, max_nodes: int = 8, max_len: int = 40,
 
 
 # ----------------------------------------------------------------------------
+# layouts that are not packed (interleaved runs, ids out of order, other node orders)
+# ----------------------------------------------------------------------------
+def shuffled_tokens_layout(specs: GroupSpecs, rng: np.random.Generator,
+                           prompt_first: bool = True, n_pad: int = 0,
+                           relabel: bool = True, chunk: int = 1) -> Layout:
+    """The groups of ``specs`` with their tokens interleaved at random.
+
+    Every prompt and every completion keeps its own token order, but the runs are
+    merged ``chunk`` tokens at a time (the last piece of a run may be shorter) in a
+    random order of runs (as completions generated side by side and appended in
+    turns would be): with ``prompt_first`` a completion's
+    tokens start only after its group's whole prompt (each unfolded sample keeps its
+    flat order), without it prompt tokens may follow completion tokens.  ``n_pad``
+    pad tokens go to random places; with ``relabel`` group and completion ids are
+    replaced by random distinct values in no particular order.  ``extra["pos"]``
+    gives, for every token of the packed layout, its position in this one.
+    """
+    g0, s0, p0, t_real = token_labels(specs)
+    streams = []  # (group index, is prompt, packed token indices)
+    t = 0
+    for gi, (p, rs) in enumerate(specs):
+        streams.append((gi, True, list(range(t, t + p))))
+        t += p
+        for r in rs:
+            streams.append((gi, False, list(range(t, t + r))))
+            t += r
+    prompt_left = {gi: p for gi, (p, _) in enumerate(specs)}
+    heads = [0] * len(streams)
+    order: List[int] = []
+    while len(order) < t_real:
+        ready = [k for k, (gi, isp, toks) in enumerate(streams)
+                 if heads[k] < len(toks) and (isp or not prompt_first or prompt_left[gi] == 0)]
+        k = ready[int(rng.integers(0, len(ready)))]
+        gi, isp, toks = streams[k]
+        take = min(chunk, len(toks) - heads[k])
+        order += toks[heads[k]:heads[k] + take]
+        heads[k] += take
+        if isp:
+            prompt_left[gi] -= take
+    T = t_real + n_pad
+    slots = np.sort(rng.choice(T, size=t_real, replace=False)) if T else np.zeros(0, np.int64)
+    pos = np.zeros(t_real, np.int64)
+    pos[np.asarray(order, np.int64)] = slots
+    group = np.full(T, PAD_GROUP, np.int32)
+    suffix = np.full(T, PAD_GROUP, np.int32)
+    is_prefix = np.zeros(T, np.uint8)
+    gmap = np.arange(len(specs))
+    smap_from = np.unique(s0[s0 >= 0]) if t_real else np.zeros(0, np.int32)
+    smap_to = smap_from
+    if relabel:
+        gmap = rng.choice(10**6, size=len(specs), replace=False)
+        smap_to = rng.choice(10**6, size=len(smap_from), replace=False) - 1000
+    group[pos] = gmap[g0[:t_real]]
+    sfx = s0[:t_real].copy()
+    for a, b_ in zip(smap_from, smap_to):
+        sfx[s0[:t_real] == a] = b_
+    suffix[pos] = sfx
+    is_prefix[pos] = p0[:t_real]
+    return Layout("tokens", T, t_real, group=group, suffix=suffix, is_prefix=is_prefix,
+                  specs=specs, extra={"pos": pos})
+
+
+def reorder_tree(node_lengths: Sequence[int], sample_paths: Sequence[Sequence[int]],
+                 rng: Optional[np.random.Generator] = None):
+    """The same forest with its nodes renumbered: breadth-first when ``rng`` is None,
+    else in a random order that still puts every parent before its children.  Node n
+    keeps its tokens (they move with it).  Returns (node_lengths, sample_paths)."""
+    n = len(node_lengths)
+    parent = [-1] * n
+    for path in sample_paths:
+        for a, b_ in zip(path[:-1], path[1:]):
+            parent[b_] = a
+    placed: List[int] = []
+    done = [False] * n
+    if rng is None:
+        depth = [0] * n
+        for v in range(n):  # packed order: parents come first
+            depth[v] = depth[parent[v]] + 1 if parent[v] >= 0 else 0
+        placed = sorted(range(n), key=lambda v: (depth[v], v))
+    else:
+        while len(placed) < n:
+            ready = [v for v in range(n) if not done[v] and (parent[v] < 0 or done[parent[v]])]
+            v = ready[int(rng.integers(0, len(ready)))]
+            done[v] = True
+            placed.append(v)
+    new_index = {v: i for i, v in enumerate(placed)}
+    nl = [int(node_lengths[v]) for v in placed]
+    paths = [[new_index[v] for v in path] for path in sample_paths]
+    return nl, paths
+
+
+# ----------------------------------------------------------------------------
 # tensors
 # ----------------------------------------------------------------------------
 TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}

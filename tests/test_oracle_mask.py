@@ -151,3 +151,83 @@ def test_kept_count_large_configs(idx):
     if idx == 4:
         assert closed == 1_359_003_648
     assert kept_pairs(meta_from_layout(lay), block_rows=2048) == closed
+
+
+# ---------------------------------------------------------------------------
+# layouts that are not packed: interleaved runs, ids out of order, other node orders
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(40))
+def test_interleaved_prompt_first_matches_unfolded(seed):
+    """Runs merged token by token (each prompt before its group's completions, ids
+    relabelled, pads anywhere): still plain causal attention over every unfolded
+    sample, whose tokens keep their flat order."""
+    rng = np.random.default_rng(3000 + seed)
+    specs = wl.random_group_specs(rng, max_groups=3, max_p=5, max_g=3, max_r=5)
+    lay = wl.shuffled_tokens_layout(specs, rng, prompt_first=True,
+                                    n_pad=int(rng.integers(0, 4)))
+    if lay.T == 0:
+        return
+    seqs, _ = uf.group_sequences(specs)
+    pos = lay.extra["pos"]
+    want = uf.visibility_from_sequences(lay.T, [pos[s] for s in seqs])
+    np.testing.assert_array_equal(dense_mask(meta_from_layout(lay)), want)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_interleaved_any_order_is_tree_rule_and_flat_causality(seed):
+    """Prompt tokens may follow completion tokens.  The token rule is then the tree
+    rule of the same groups (a prompt node with one child per completion, pinned
+    against the unfolded samples above) restricted to kv <= q in the new order: a
+    prompt token placed after a completion token stays hidden from it."""
+    rng = np.random.default_rng(3100 + seed)
+    specs = wl.random_group_specs(rng, max_groups=3, max_p=5, max_g=3, max_r=5)
+    lay = wl.shuffled_tokens_layout(specs, rng, prompt_first=False,
+                                    n_pad=int(rng.integers(0, 4)))
+    if lay.T == 0:
+        return
+    nl, paths = [], []
+    for p, rs in specs:
+        root = len(nl)
+        nl.append(p)
+        if not rs:
+            paths.append([root])
+        for r in rs:
+            paths.append([root, len(nl)])
+            nl.append(r)
+    packed = dense_mask(meta_from_layout(wl.tree_layout(nl, paths)))
+    pos = lay.extra["pos"]
+    want = np.zeros((lay.T, lay.T), dtype=bool)
+    want[np.ix_(pos, pos)] = packed
+    want &= np.tril(np.ones((lay.T, lay.T), dtype=bool))
+    np.testing.assert_array_equal(dense_mask(meta_from_layout(lay)), want)
+
+
+def test_interleaving_hides_later_prompt_tokens():
+    """Worked case: prompt [a b], completion [c d] laid out a c b d.  c sees a and
+    itself but not b (placed after it); d sees a, b, c and itself; b sees a, b."""
+    g = [0, 0, 0, 0]
+    s = [-1, 5, -1, 5]
+    p = [1, 0, 1, 0]
+    m = dense_mask(TokenMeta(g, s, p))
+    want = np.array([[1, 0, 0, 0],
+                     [1, 1, 0, 0],
+                     [1, 0, 1, 0],
+                     [1, 1, 1, 1]], dtype=bool)
+    np.testing.assert_array_equal(m, want)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_reordered_trees_match_unfolded(seed):
+    """Breadth-first and random parent-first node orders (subtrees no longer
+    contiguous): visibility is still causal attention over each root-to-leaf path,
+    and the kept count keeps its closed form."""
+    rng = np.random.default_rng(3200 + seed)
+    nl, paths = wl.random_tree(rng, max_nodes=7, max_len=5, max_trees=2)
+    nl, paths = wl.reorder_tree(nl, paths, None if seed % 2 else rng)
+    lay = wl.tree_layout(nl, paths, extra_pad=int(rng.integers(0, 3)))
+    if lay.T == 0:
+        return
+    meta = meta_from_layout(lay)
+    want = uf.visibility_from_sequences(lay.T, uf.tree_sequences(nl, paths))
+    np.testing.assert_array_equal(dense_mask(meta), want)
+    assert kept_pairs(meta) == uf.kept_closed_form_tree(nl, paths)
