@@ -57,7 +57,7 @@ def kept_pairs(lay) -> int:
     return sum(ln * (ln + 1) // 2 + ln * anc[n] for n, ln in enumerate(lay.node_lengths))
 
 
-def describe(cfg, lay) -> str:
+def describe(cfg, lay, layout_mode="packed", form="auto") -> str:
     if lay.kind == "tokens":
         ps = sorted({p for p, _ in lay.specs})
         layout = (f"{len(lay.specs)} groups, P={ps[0]}" if len(ps) == 1
@@ -68,6 +68,12 @@ def describe(cfg, lay) -> str:
             str(rs[0]) if len(rs) == 1 else f"[{rs[0]},{rs[-1]}]")
     else:
         layout = "8 trees: root 1024 -> 4 x 256 -> 4 x 384 leaves"
+    if layout_mode == "chunked":
+        layout += " (completions interleaved in turns of 64 tokens)"
+    elif layout_mode == "bfs":
+        layout += " (nodes in breadth-first order)"
+    if form == "nodes":
+        layout += ", node-form map"
     return (f"shared-prefix attention fwd+bwd: {layout}, T={lay.T}, "
             f"hq={cfg.hq}/hkv={cfg.hkv}, d={cfg.d}, {cfg.dtype}")
 
@@ -247,6 +253,14 @@ def main():
                     help="time the fold of the workload's rollout groups and the unfold of a "
                          "folded [T, hq, d] tensor instead of the attention step (token-form "
                          "workloads)")
+    ap.add_argument("--form", default="auto", choices=["auto", "nodes"],
+                    help="tile-map encoding: auto (the interval form for packed layouts) or "
+                         "the node form forced (the general encoding, on the same tiles)")
+    ap.add_argument("--layout", default="packed", choices=["packed", "chunked", "bfs"],
+                    help="packed (as the workload states); chunked: each group's completions "
+                         "interleaved in turns of 64 tokens after its prompt (token-form "
+                         "workloads); bfs: tree nodes in breadth-first order (tree workloads). "
+                         "Both keep the kept pairs; the map takes the node form")
     ap.add_argument("--traffic-command", default="",
                     help="with --traffic-summary: the command line the passes ran, recorded")
     args = ap.parse_args()
@@ -272,6 +286,20 @@ def main():
     torch.cuda.set_device(dev)
     cfg = wl.CONFIGS[args.config]
     lay = wl.layout_for(cfg)
+    if args.layout == "chunked":
+        if lay.kind != "tokens":
+            sys.exit("--layout chunked needs a token-form workload")
+        import numpy as np
+        lay = wl.shuffled_tokens_layout(lay.specs, np.random.default_rng(cfg.idx),
+                                        prompt_first=True, relabel=False, chunk=64,
+                                        n_pad=lay.T - lay.T_real)
+    elif args.layout == "bfs":
+        if lay.kind != "tree":
+            sys.exit("--layout bfs needs a tree workload")
+        nl, paths = wl.reorder_tree(lay.node_lengths, lay.sample_paths)
+        lay = wl.tree_layout(nl, paths, extra_pad=lay.T - lay.T_real)
+    if args.layout != "packed":
+        args.no_cpu_baseline = True  # the oracle's sample slices packed groups
     if args.fold:
         if lay.kind != "tokens":
             sys.exit("--fold needs a token-form workload (rollout groups)")
@@ -294,8 +322,9 @@ def main():
 
     def build_map():
         if lay.kind == "tokens":
-            return psa.build_tile_map_tokens(*labels, TILE, TILE)
-        return psa.build_tile_map_tree(lay.node_lengths, lay.sample_paths, lay.T, dev, TILE, TILE)
+            return psa.build_tile_map_tokens(*labels, TILE, TILE, form=args.form)
+        return psa.build_tile_map_tree(lay.node_lengths, lay.sample_paths, lay.T, dev, TILE, TILE,
+                                       form=args.form)
 
     m0 = build_map()
     ws = torch.empty(max(psa.bwd_workspace_size(m0, q, k), 1), dtype=torch.uint8, device=dev)
@@ -388,7 +417,8 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0, sigma) Q/K/V/dO; layout as the workload states)",
-        "config": {"workload": describe(cfg, lay), "T": lay.T, "T_real": lay.T_real,
+        "config": {"workload": describe(cfg, lay, args.layout, args.form), "T": lay.T,
+                   "T_real": lay.T_real, "map_form": ["interval", "nodes"][info["form"]],
                    "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": d,
                    "passes": cfg.passes, "grad_dtype": args.grad_dtype,
                    "bwd_p_ds": "hi+lo bf16" if args.split else "bf16, hi+lo where large",

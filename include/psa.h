@@ -42,13 +42,13 @@
 extern "C" {
 #endif
 
-#define PSA_ABI_VERSION 2
+#define PSA_ABI_VERSION 3
 
 typedef enum {
   PSA_OK = 0,
   PSA_ERR_NULL = 1,         /* a required pointer is NULL                              */
   PSA_ERR_SHAPE = 2,        /* T, head counts or tile sizes out of range; hq % hkv != 0 */
-  PSA_ERR_LAYOUT = 3,       /* metadata not in the packed layout the library accepts    */
+  PSA_ERR_LAYOUT = 3,       /* metadata that defines no prefix forest (see the builders) */
   PSA_ERR_DTYPE = 4,        /* unknown psa_dtype                                        */
   PSA_ERR_UNSUPPORTED = 5,  /* head_dim / dtype combination not compiled                */
   PSA_ERR_MAP_MISMATCH = 6, /* map built for another T, tile shape or device            */
@@ -73,7 +73,15 @@ typedef struct {
   int64_t nnz;         /* non-empty tiles                                         */
   int64_t n_full;      /* tiles whose every pair is kept                          */
   int64_t n_partial;   /* non-empty tiles that are not full                       */
+  int32_t form;        /* PSA_FORM_INTERVAL or PSA_FORM_NODES (mask encoding)     */
 } psa_tile_map_info;
+
+/* Mask encodings a map can carry (psa_tile_map_info.form). */
+#define PSA_FORM_INTERVAL 0 /* packed layouts: kv visible to q iff kv <= q < end[kv]    */
+#define PSA_FORM_NODES 1    /* any layout: per-token node numbers (psa_tile_map_export_nodes) */
+
+/* Build flags (the _ex builders). */
+#define PSA_MAP_NODE_FORM 1 /* build the node form even where the interval form exists */
 
 /* Library ABI version (PSA_ABI_VERSION of the build). */
 int32_t psa_abi_version(void);
@@ -95,39 +103,59 @@ psa_status psa_tile_shape(psa_pass pass, psa_dtype dtype, int32_t d, int32_t* bl
  *   group[t]     >= 0 group id, < 0 pad token;
  *   suffix[t]    completion id (ignored on prompt and pad tokens);
  *   is_prefix[t] 1 on prompt tokens, 0 on completion tokens (ignored on pads).
- * Accepted layout (reading of unsloth "prefix_grouper_kernel.py",
- * build_seg_info_multigroup, which always packs this way): each group is one
- * contiguous run; group ids increase from run to run; a group's prompt tokens come
- * before its completion tokens; each completion is one contiguous run and completion
- * ids increase within a group; pads may sit between groups or at either end.
- * Anything else returns PSA_ERR_LAYOUT (never a silently different mask).
+ * Any labelling is accepted; the mask is the rule above, token by token.  The packed
+ * layout (reading of unsloth "prefix_grouper_kernel.py", build_seg_info_multigroup,
+ * which always packs this way: each group one contiguous run, group ids increasing
+ * from run to run, a group's prompt tokens before its completion tokens, each
+ * completion one contiguous run with completion ids increasing within the group,
+ * pads between groups or at either end) gets the interval form (one int per token);
+ * every other labelling (interleaved groups or completions, prompt tokens after
+ * completion tokens, ids out of order) gets the node form (three ints per token:
+ * each token's node - its group's prompt, or one completion - numbered in
+ * depth-first order, and each node's subtree range), built by a sort of the node
+ * keys.  Both give the same mask; the node form costs one more classification pass
+ * and reads two more ints per key on partial tiles.
  * 1 <= block_m, block_n <= 1024.  T may be 0 (an empty map).
  * Work is enqueued on `stream` (a hipStream_t, NULL = default); the call waits once
  * on that stream to size the sparse lists.  The map may be used on `stream` at once;
  * on another stream, after synchronising with `stream`.
  * Ownership: *out belongs to the caller until psa_tile_map_destroy.
- * Errors: PSA_ERR_NULL, PSA_ERR_SHAPE, PSA_ERR_LAYOUT, PSA_ERR_HIP, PSA_ERR_ALLOC.
+ * Errors: PSA_ERR_NULL, PSA_ERR_SHAPE, PSA_ERR_HIP, PSA_ERR_ALLOC.
  */
 psa_status psa_build_tile_map_tokens(int64_t T, const int32_t* group, const int32_t* suffix,
                                      const uint8_t* is_prefix, int32_t block_m,
                                      int32_t block_n, void* stream, psa_tile_map** out);
+/* The same with flags (0 or PSA_MAP_NODE_FORM); PSA_ERR_VALUE for an unknown bit. */
+psa_status psa_build_tile_map_tokens_ex(int64_t T, const int32_t* group, const int32_t* suffix,
+                                        const uint8_t* is_prefix, int32_t block_m,
+                                        int32_t block_n, int32_t flags, void* stream,
+                                        psa_tile_map** out);
 
 /*
  * Build a tile map from a prefix tree (host pointers):
  *   node_lengths[n_nodes]  tokens of each node; node n owns the n-th contiguous run;
  *   path_ptr[n_paths + 1], path_nodes[path_ptr[n_paths]]  sample path s lists node
  *   indices root -> leaf in path_nodes[path_ptr[s] .. path_ptr[s+1]).
- * Accepted layout (reading of Automodel PR #2564, whose fold already emits
- * [prompt | c_0 | c_1 ...]): every node lies on a path; a node has one parent across
- * all paths; nodes are in depth-first pre-order (a parent precedes its children and
- * each subtree is one contiguous run of nodes).  Several roots pack several trees.
- * Zero-length nodes are allowed.  T >= sum(node_lengths); tokens past the sum are pads.
+ * Required (reading of Automodel PR #2564, whose fold emits a prompt before its
+ * continuations): every node lies on a path; a node has one parent across all paths;
+ * a parent comes before its children (a smaller node index), so every token a node
+ * sees sits before it.  Otherwise PSA_ERR_LAYOUT.  Nodes in depth-first pre-order
+ * (each subtree one contiguous run of nodes) get the interval form; any other order
+ * (breadth-first, interleaved branches) the node form, numbered on the host.
+ * Several roots pack several trees.  Zero-length nodes are allowed.
+ * T >= sum(node_lengths); tokens past the sum are pads.
  * Same stream, ownership and error rules as psa_build_tile_map_tokens.
  */
 psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
                                    int64_t n_paths, const int32_t* path_ptr,
                                    const int32_t* path_nodes, int64_t T, int32_t block_m,
                                    int32_t block_n, void* stream, psa_tile_map** out);
+/* The same with flags (0 or PSA_MAP_NODE_FORM); PSA_ERR_VALUE for an unknown bit. */
+psa_status psa_build_tile_map_tree_ex(int64_t n_nodes, const int32_t* node_lengths,
+                                      int64_t n_paths, const int32_t* path_ptr,
+                                      const int32_t* path_nodes, int64_t T, int32_t block_m,
+                                      int32_t block_n, int32_t flags, void* stream,
+                                      psa_tile_map** out);
 
 /* Sizes of a built map.  Errors: PSA_ERR_NULL. */
 psa_status psa_tile_map_info_get(const psa_tile_map* map, psa_tile_map_info* out);
@@ -138,11 +166,23 @@ psa_status psa_tile_map_info_get(const psa_tile_map* map, psa_tile_map_info* out
  * t <= q < end[t]), kinds[n_qtiles * n_ktiles] (row-major, 0/1/2), row_ptr[n_qtiles+1],
  * col[nnz], kind[nnz] (CSR: per q-tile its kv-tiles ascending), col_ptr[n_ktiles+1],
  * row[nnz], kind_csc[nnz] (CSC: per kv-tile its q-tiles ascending).
- * Errors: PSA_ERR_NULL, PSA_ERR_HIP.
+ * end must be NULL for a node-form map.
+ * Errors: PSA_ERR_NULL, PSA_ERR_HIP, PSA_ERR_VALUE (end of a node-form map).
  */
 psa_status psa_tile_map_export(const psa_tile_map* map, int32_t* end, uint8_t* kinds,
                                int32_t* row_ptr, int32_t* col, uint8_t* kind,
                                int32_t* col_ptr, int32_t* row, uint8_t* kind_csc);
+
+/*
+ * Copy the mask encoding as nodes to host buffers of T int32 each (NULL skipped):
+ * kv is visible to q iff kv <= q and lo[kv] <= key[q] < lo[kv] + w[kv].  For a
+ * node-form map these are its arrays (key: the token's node number from 1, 0 on a
+ * pad; [lo, lo + w): the numbers of the node's subtree, w = 0 on a pad); an
+ * interval-form map is written as key = lo = t, w = end[t] - t.  Waits for the
+ * build stream.  Errors: PSA_ERR_NULL, PSA_ERR_HIP.
+ */
+psa_status psa_tile_map_export_nodes(const psa_tile_map* map, int32_t* key, int32_t* lo,
+                                     int32_t* w);
 
 /* Free a map (NULL is a no-op).  Work that uses it must have completed. */
 void psa_tile_map_destroy(psa_tile_map* map);

@@ -12,6 +12,7 @@
 #include <new>
 #include <numeric>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "psa.h"
@@ -160,13 +161,14 @@ void free_map(psa_tile_map* m) {
   if (!m) return;
   map_release(m, m->buf1, m->buf1_bytes, m->ev1);
   map_release(m, m->buf2, m->buf2_bytes, m->ev2);
+  map_release(m, m->buf3, m->buf3_bytes, m->ev3);
   delete m;
 }
 
 // Phase-1 allocation.  Layout: end | kinds | scratch | info (8 x int64) | row_ptr |
 // col_ptr.
 struct Phase1 {
-  int32_t* scratch = nullptr;  // per-k-tile summaries, then reused by nothing else
+  int32_t* scratch = nullptr;  // per-k-tile summaries (4 x align64(nk) ints)
   int32_t* tok_scratch = nullptr;
   int64_t* info = nullptr;     // nnz, n_full, n_partial, first layout error
 };
@@ -176,7 +178,7 @@ psa_status alloc_phase1(psa_tile_map* m, Phase1* ph) {
   const int64_t nk1 = std::max<int64_t>(m->nk, 1);
   size_t o_end = c.take<int32_t>(std::max<int64_t>(m->T, 1));
   size_t o_kinds = c.take<uint8_t>(std::max<int64_t>(m->nq * m->nk, 1));
-  size_t o_scr = c.take<int32_t>(2 * align_up(nk1, 64));
+  size_t o_scr = c.take<int32_t>(4 * align_up(nk1, 64));
   size_t o_tok = c.take<int32_t>(std::max<int64_t>(tokens_scratch_ints(m->T), 1));
   size_t o_info = c.take<int64_t>(8);
   size_t o_rp = c.take<int32_t>(m->nq + 1);
@@ -201,31 +203,44 @@ psa_status alloc_phase1(psa_tile_map* m, Phase1* ph) {
   return PSA_OK;
 }
 
-psa_status finish_build(psa_tile_map* m, const Phase1& ph, psa_tile_map** out) {
-  int32_t* kmin = ph.scratch;
-  int32_t* kmax = ph.scratch + align_up(std::max<int64_t>(m->nk, 1), 64);
-  hipError_t e = launch_classify(m->T, m->bm, m->bn, m->nq, m->nk, m->end, m->kinds,
-                                 m->row_ptr, m->col_ptr, kmin, kmax, ph.info, m->stream);
+// Classification of the map's encoding (interval or node form) and the one wait: the
+// counts and the layout verdict land in info_h.
+psa_status classify_and_wait(psa_tile_map* m, const Phase1& ph, int64_t* info_h) {
+  const size_t stride = align_up(std::max<int64_t>(m->nk, 1), 64);
+  hipError_t e;
+  if (m->form == kFormNodes)
+    e = launch_classify_nodes(m->T, m->bm, m->bn, m->nq, m->nk, m->nkey, m->nlo, m->nw,
+                              m->kinds, m->row_ptr, m->col_ptr, ph.scratch, ph.info, m->stream);
+  else
+    e = launch_classify(m->T, m->bm, m->bn, m->nq, m->nk, m->end, m->kinds, m->row_ptr,
+                        m->col_ptr, ph.scratch, ph.scratch + stride, ph.info, m->stream);
   if (e != hipSuccess) return psa_hip_error(e, "tile classification launch");
-
-  // the one wait: the counts and the layout verdict
-  int64_t info_h[8];
-  if ((e = hipMemcpyAsync(info_h, ph.info, sizeof(info_h), hipMemcpyDeviceToHost, m->stream)) !=
-          hipSuccess ||
+  if ((e = hipMemcpyAsync(info_h, ph.info, 8 * sizeof(int64_t), hipMemcpyDeviceToHost,
+                          m->stream)) != hipSuccess ||
       (e = hipStreamSynchronize(m->stream)) != hipSuccess)
     return psa_hip_error(e, "tile map readback");
-  if (info_h[3] != -1) {
-    static const char* why[] = {
-        "",
-        "group ids decrease along the sequence (groups must be contiguous, ascending runs)",
-        "a group is split by pad tokens",
-        "a prompt token follows a completion token of the same group",
-        "completion ids decrease within a group (completions must be contiguous runs)"};
-    const uint64_t word = uint64_t(info_h[3]);
-    const int code = int(word & 7) >= 1 && int(word & 7) <= 4 ? int(word & 7) : 0;
-    return psa_set_error(PSA_ERR_LAYOUT, std::string("token layout rejected at position ") +
-                                             std::to_string(word >> 3) + ": " + why[code]);
+  return PSA_OK;
+}
+
+// The node-form arrays (key | lo | w) in their own buffer.
+psa_status alloc_nodes(psa_tile_map* m) {
+  const size_t arr = align_up(size_t(std::max<int64_t>(m->T, 1)) * 4, 256);
+  if (map_alloc(m, &m->buf3, 3 * arr, &m->buf3_bytes, &m->ev3) != hipSuccess) {
+    m->buf3 = nullptr;
+    (void)hipGetLastError();
+    return psa_set_error(PSA_ERR_ALLOC, "device allocation of the node arrays failed");
   }
+  char* b = static_cast<char*>(m->buf3);
+  m->nkey = reinterpret_cast<int32_t*>(b);
+  m->nlo = reinterpret_cast<int32_t*>(b + arr);
+  m->nw = reinterpret_cast<int32_t*>(b + 2 * arr);
+  m->form = kFormNodes;
+  return PSA_OK;
+}
+
+// Sparse lists from a classified map (info_h from classify_and_wait).
+psa_status finish_lists(psa_tile_map* m, const int64_t* info_h, psa_tile_map** out) {
+  hipError_t e;
   m->nnz = info_h[0];
   m->n_full = info_h[1];
   m->n_partial = info_h[2];
@@ -334,9 +349,18 @@ psa_status psa_tile_shape(psa_pass pass, psa_dtype dtype, int32_t d, int32_t* bl
 psa_status psa_build_tile_map_tokens(int64_t T, const int32_t* group, const int32_t* suffix,
                                      const uint8_t* is_prefix, int32_t block_m,
                                      int32_t block_n, void* stream, psa_tile_map** out) {
+  return psa_build_tile_map_tokens_ex(T, group, suffix, is_prefix, block_m, block_n, 0, stream,
+                                      out);
+}
+
+psa_status psa_build_tile_map_tokens_ex(int64_t T, const int32_t* group, const int32_t* suffix,
+                                        const uint8_t* is_prefix, int32_t block_m,
+                                        int32_t block_n, int32_t flags, void* stream,
+                                        psa_tile_map** out) {
   if (!out) return psa_set_error(PSA_ERR_NULL, "out is NULL");
   psa_status st = check_tiles(T, block_m, block_n);
   if (st != PSA_OK) return st;
+  if ((flags & ~PSA_MAP_NODE_FORM) != 0) return psa_set_error(PSA_ERR_VALUE, "unknown flag bit");
   if (T > 0 && (!group || !suffix || !is_prefix))
     return psa_set_error(PSA_ERR_NULL, "label pointer is NULL");
   psa_tile_map* m = new (std::nothrow) psa_tile_map();
@@ -357,13 +381,50 @@ psa_status psa_build_tile_map_tokens(int64_t T, const int32_t* group, const int3
     free_map(m);
     return st;
   }
-  e = launch_tokens_end(T, group, suffix, is_prefix, m->end, ph.tok_scratch, ph.info,
-                        m->stream);
-  if (e != hipSuccess) {
-    free_map(m);
-    return psa_hip_error(e, "label scan launch");
+  int64_t info_h[8];
+  if (!(flags & PSA_MAP_NODE_FORM)) {
+    // the interval form, when the layout is packed (the verdict comes with the counts)
+    e = launch_tokens_end(T, group, suffix, is_prefix, m->end, ph.tok_scratch, ph.info,
+                          m->stream);
+    if (e != hipSuccess) {
+      free_map(m);
+      return psa_hip_error(e, "label scan launch");
+    }
+    if ((st = classify_and_wait(m, ph, info_h)) != PSA_OK) {
+      free_map(m);
+      return st;
+    }
   }
-  st = finish_build(m, ph, out);
+  if ((flags & PSA_MAP_NODE_FORM) || info_h[3] != -1) {
+    // any other layout: the node form (numbering by a sort of the node keys)
+    void* scr = nullptr;
+    size_t scr_bytes = 0;
+    hipEvent_t scr_ev = nullptr;
+    const size_t need = tokens_nodes_scratch_bytes(T);
+    if ((st = alloc_nodes(m)) != PSA_OK) {
+      free_map(m);
+      return st;
+    }
+    if (map_alloc(m, &scr, need, &scr_bytes, &scr_ev) != hipSuccess) {
+      (void)hipGetLastError();
+      free_map(m);
+      return psa_set_error(PSA_ERR_ALLOC, "device allocation of the node sort scratch failed");
+    }
+    e = launch_map_init(m->nk, m->row_ptr, m->col_ptr, ph.info, m->stream);
+    if (e == hipSuccess)
+      e = launch_tokens_nodes(T, group, suffix, is_prefix, m->nkey, m->nlo, m->nw, scr,
+                              scr_bytes, m->stream);
+    map_release(m, scr, scr_bytes, scr_ev);  // reusable once the launches are done
+    if (e != hipSuccess) {
+      free_map(m);
+      return psa_hip_error(e, "label numbering launch");
+    }
+    if ((st = classify_and_wait(m, ph, info_h)) != PSA_OK) {
+      free_map(m);
+      return st;
+    }
+  }
+  st = finish_lists(m, info_h, out);
   if (st != PSA_OK) free_map(m);
   return st;
 }
@@ -372,16 +433,26 @@ psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
                                    int64_t n_paths, const int32_t* path_ptr,
                                    const int32_t* path_nodes, int64_t T, int32_t block_m,
                                    int32_t block_n, void* stream, psa_tile_map** out) {
+  return psa_build_tile_map_tree_ex(n_nodes, node_lengths, n_paths, path_ptr, path_nodes, T,
+                                    block_m, block_n, 0, stream, out);
+}
+
+psa_status psa_build_tile_map_tree_ex(int64_t n_nodes, const int32_t* node_lengths,
+                                      int64_t n_paths, const int32_t* path_ptr,
+                                      const int32_t* path_nodes, int64_t T, int32_t block_m,
+                                      int32_t block_n, int32_t flags, void* stream,
+                                      psa_tile_map** out) {
   if (!out) return psa_set_error(PSA_ERR_NULL, "out is NULL");
   psa_status st = check_tiles(T, block_m, block_n);
   if (st != PSA_OK) return st;
+  if ((flags & ~PSA_MAP_NODE_FORM) != 0) return psa_set_error(PSA_ERR_VALUE, "unknown flag bit");
   if (n_nodes < 0 || n_paths < 0) return psa_set_error(PSA_ERR_SHAPE, "negative count");
   if (n_nodes > 0 && (!node_lengths || !path_ptr || (!path_nodes && n_paths > 0)))
     return psa_set_error(PSA_ERR_NULL, "tree pointer is NULL");
   if (n_nodes > 0 && n_paths == 0)
     return psa_set_error(PSA_ERR_LAYOUT, "nodes given but no sample path");
 
-  // --- host validation: parents, depth-first pre-order, subtree extents ---
+  // --- host validation: parents (each before its children), subtree extents ---
   std::vector<int64_t> parent(n_nodes, -2);
   std::vector<int64_t> start(n_nodes + 1, 0);
   for (int64_t n = 0; n < n_nodes; ++n) {
@@ -407,28 +478,74 @@ psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
       prev = node;
     }
   }
-  std::vector<int64_t> stack;
   for (int64_t n = 0; n < n_nodes; ++n) {
     if (parent[n] == -2)
       return psa_set_error(PSA_ERR_LAYOUT, "node " + std::to_string(n) + " lies on no path");
-    if (parent[n] == -1) {
-      stack.clear();
-    } else {
-      while (!stack.empty() && stack.back() != parent[n]) stack.pop_back();
-      if (stack.empty())
-        return psa_set_error(PSA_ERR_LAYOUT, "nodes are not in depth-first pre-order (node " +
-                                                 std::to_string(n) + ")");
-    }
-    stack.push_back(n);
+    if (parent[n] >= n)
+      return psa_set_error(PSA_ERR_LAYOUT, "node " + std::to_string(n) +
+                                               " comes before its parent " +
+                                               std::to_string(parent[n]));
   }
-  std::vector<int64_t> sub_end(n_nodes);
-  for (int64_t n = 0; n < n_nodes; ++n) sub_end[n] = n + 1;
-  for (int64_t n = n_nodes - 1; n >= 0; --n)
-    if (parent[n] >= 0) sub_end[parent[n]] = std::max(sub_end[parent[n]], sub_end[n]);
-  std::vector<int64_t> table(2 * std::max<int64_t>(n_nodes, 1), 0);
-  for (int64_t n = 0; n < n_nodes; ++n) {
-    table[n] = start[n];
-    table[n_nodes + n] = start[sub_end[n]];
+  // depth-first pre-order (every subtree one contiguous run of nodes) has the
+  // interval form; any other order of parents before children gets the node form
+  bool dfs = true;
+  {
+    std::vector<int64_t> stack;
+    for (int64_t n = 0; n < n_nodes && dfs; ++n) {
+      if (parent[n] == -1) {
+        stack.clear();
+      } else {
+        while (!stack.empty() && stack.back() != parent[n]) stack.pop_back();
+        dfs = !stack.empty();
+      }
+      stack.push_back(n);
+    }
+  }
+  const bool nodes = !dfs || (flags & PSA_MAP_NODE_FORM);
+  std::vector<int64_t> table;
+  if (!nodes) {  // node start | token end of the node's subtree
+    std::vector<int64_t> sub_end(n_nodes);
+    for (int64_t n = 0; n < n_nodes; ++n) sub_end[n] = n + 1;
+    for (int64_t n = n_nodes - 1; n >= 0; --n)
+      if (parent[n] >= 0) sub_end[parent[n]] = std::max(sub_end[parent[n]], sub_end[n]);
+    table.assign(2 * std::max<int64_t>(n_nodes, 1), 0);
+    for (int64_t n = 0; n < n_nodes; ++n) {
+      table[n] = start[n];
+      table[n_nodes + n] = start[sub_end[n]];
+    }
+  } else {  // node start | pre-order number | subtree size (in nodes)
+    std::vector<int64_t> first_child(n_nodes, -1), next_sib(n_nodes, -1), last_child(n_nodes, -1);
+    std::vector<int64_t> roots;
+    for (int64_t n = 0; n < n_nodes; ++n) {
+      const int64_t p = parent[n];
+      if (p < 0) {
+        roots.push_back(n);
+      } else {
+        if (last_child[p] < 0) first_child[p] = n;
+        else next_sib[last_child[p]] = n;
+        last_child[p] = n;
+      }
+    }
+    table.assign(3 * std::max<int64_t>(n_nodes, 1), 0);
+    int64_t* pre = table.data() + n_nodes;
+    int64_t* size = table.data() + 2 * n_nodes;
+    int64_t counter = 0;
+    std::vector<int64_t> stack;
+    for (int64_t r : roots) {  // iterative depth-first walk, children in index order
+      stack.push_back(r);
+      while (!stack.empty()) {
+        const int64_t n = stack.back();
+        stack.pop_back();
+        pre[n] = counter++;
+        std::vector<int64_t> kids;
+        for (int64_t c = first_child[n]; c >= 0; c = next_sib[c]) kids.push_back(c);
+        for (auto it = kids.rbegin(); it != kids.rend(); ++it) stack.push_back(*it);
+      }
+    }
+    for (int64_t n = 0; n < n_nodes; ++n) size[n] = 1;
+    for (int64_t n = n_nodes - 1; n >= 0; --n)  // children come after their parent
+      if (parent[n] >= 0) size[parent[n]] += size[n];
+    for (int64_t n = 0; n < n_nodes; ++n) table[n] = start[n];
   }
 
   psa_tile_map* m = new (std::nothrow) psa_tile_map();
@@ -467,14 +584,30 @@ psa_status psa_build_tile_map_tree(int64_t n_nodes, const int32_t* node_lengths,
     }
   }
   const int64_t* dt = static_cast<const int64_t*>(d_table);
-  e = launch_tree_end(T, n_nodes, dt, dt ? dt + n_nodes : nullptr, start[n_nodes], m->end,
-                      m->stream);
+  if (nodes) {
+    if ((st = alloc_nodes(m)) != PSA_OK) {
+      map_release(m, d_table, table_bytes, table_ev);
+      free_map(m);
+      return st;
+    }
+    e = launch_tree_nodes(T, n_nodes, dt, dt ? dt + n_nodes : nullptr,
+                          dt ? dt + 2 * n_nodes : nullptr, start[n_nodes], m->nkey, m->nlo,
+                          m->nw, m->stream);
+  } else {
+    e = launch_tree_end(T, n_nodes, dt, dt ? dt + n_nodes : nullptr, start[n_nodes], m->end,
+                        m->stream);
+  }
   map_release(m, d_table, table_bytes, table_ev);  // reusable once the launch is done
   if (e != hipSuccess) {
     free_map(m);
     return psa_hip_error(e, "tree expansion launch");
   }
-  st = finish_build(m, ph, out);
+  int64_t info_h[8];
+  if ((st = classify_and_wait(m, ph, info_h)) != PSA_OK) {
+    free_map(m);
+    return st;
+  }
+  st = finish_lists(m, info_h, out);
   if (st != PSA_OK) free_map(m);
   return st;
 }
@@ -489,6 +622,7 @@ psa_status psa_tile_map_info_get(const psa_tile_map* map, psa_tile_map_info* out
   out->nnz = map->nnz;
   out->n_full = map->n_full;
   out->n_partial = map->n_partial;
+  out->form = map->form;
   return PSA_OK;
 }
 
@@ -496,6 +630,8 @@ psa_status psa_tile_map_export(const psa_tile_map* map, int32_t* end, uint8_t* k
                                int32_t* row_ptr, int32_t* col, uint8_t* kind,
                                int32_t* col_ptr, int32_t* row, uint8_t* kind_csc) {
   if (!map) return psa_set_error(PSA_ERR_NULL, "map is NULL");
+  if (end && map->form != kFormInterval && map->T > 0)
+    return psa_set_error(PSA_ERR_VALUE, "a node-form map has no end[] (export its nodes)");
   hipError_t e = hipStreamSynchronize(map->stream);
   if (e != hipSuccess) return psa_hip_error(e, "hipStreamSynchronize");
   struct Item {
@@ -516,6 +652,35 @@ psa_status psa_tile_map_export(const psa_tile_map* map, int32_t* end, uint8_t* k
     if (!it.dst || it.bytes == 0) continue;
     if ((e = hipMemcpy(it.dst, it.src, it.bytes, hipMemcpyDeviceToHost)) != hipSuccess)
       return psa_hip_error(e, "tile map export");
+  }
+  return PSA_OK;
+}
+
+psa_status psa_tile_map_export_nodes(const psa_tile_map* map, int32_t* key, int32_t* lo,
+                                     int32_t* w) {
+  if (!map) return psa_set_error(PSA_ERR_NULL, "map is NULL");
+  hipError_t e = hipStreamSynchronize(map->stream);
+  if (e != hipSuccess) return psa_hip_error(e, "hipStreamSynchronize");
+  const size_t n = size_t(map->T);
+  if (n == 0) return PSA_OK;
+  if (map->form == kFormNodes) {
+    const std::pair<int32_t*, const int32_t*> items[] = {
+        {key, map->nkey}, {lo, map->nlo}, {w, map->nw}};
+    for (const auto& it : items) {
+      if (!it.first) continue;
+      if ((e = hipMemcpy(it.first, it.second, n * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+        return psa_hip_error(e, "tile map export");
+    }
+    return PSA_OK;
+  }
+  // interval form written as nodes: key t, range [t, end[t]) (kv <= q < end[kv])
+  std::vector<int32_t> end(n);
+  if ((e = hipMemcpy(end.data(), map->end, n * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return psa_hip_error(e, "tile map export");
+  for (size_t t = 0; t < n; ++t) {
+    if (key) key[t] = int32_t(t);
+    if (lo) lo[t] = int32_t(t);
+    if (w) w[t] = end[t] - int32_t(t);
   }
   return PSA_OK;
 }

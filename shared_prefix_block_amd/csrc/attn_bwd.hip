@@ -40,7 +40,10 @@ struct BwdParams {
   void* dv;
   float* Dl;  // [hq, T]
   float* L2;  // [hq, T]
-  const int32_t* end;
+  const int32_t* end;   // interval form
+  const int32_t* nkey;  // node form
+  const int32_t* nlo;
+  const int32_t* nw;
   const int32_t* row_ptr;
   const int32_t* col;
   const uint8_t* kind;
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // transposed operands of dV^T += dO^T P and dK^T += Q^T dS come from the LDS
 // transpose read.  fp32 stages transposed copies instead.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool NODES>
 struct DkdvCfg {
   static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static constexpr int NW = 4;
@@ -143,25 +146,26 @@ struct DkdvCfg {
   static constexpr int N_ELEMS = BMS * NS;
   static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
   static constexpr int BUF_ELEMS = 2 * (N_ELEMS + T_ELEMS);
-  // bf16: Q | dO | L2 | D stages filled by direct-to-LDS loads into swizzled,
-  // unpadded tiles (as the forward's K and V); fp32: through registers.
+  // bf16: Q | dO | L2 | D (| node numbers) stages filled by direct-to-LDS loads into
+  // swizzled, unpadded tiles (as the forward's K and V); fp32: through registers.
   static constexpr bool kDma = kBf16;
+  static constexpr int LW = NODES ? 3 : 2;  // per-row words: L2, D (, key)
   static constexpr int TILE_BYTES = BMS * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * BMS * 4;
-  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * 2 * BMS * 4;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + LW * BMS * 4;
+  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * LW * BMS * 4;
 };
 
 // PART: 0 computes dK and dV together; 1 only dV, 2 only dK.  At d = 256 K, V and
 // both accumulators do not fit one wave's registers, so the pair is split into two
 // passes (dV: S and P only; dK: S, dP and dS), at the price of recomputing S.
-template <typename T, typename G, int D, int MODE, int PART>
+template <typename T, typename G, int D, int MODE, int PART, bool NODES>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
-  using C = DkdvCfg<T, D>;
+  using C = DkdvCfg<T, D, NODES>;
   constexpr bool kDV = PART != 2, kDK = PART != 1;
   static_assert(PART == 0 || C::kDma, "split passes exist on the DMA path only");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   T* const buf0 = reinterpret_cast<T*>(smem);
-  float* const ld0 = reinterpret_cast<float*>(smem + 2 * C::BUF_ELEMS * C::EB);  // [2][2][BMS]
+  float* const ld0 = reinterpret_cast<float*>(smem + 2 * C::BUF_ELEMS * C::EB);  // [2][LW][BMS]
 
   const int64_t w_id = xcd_remap(blockIdx.x, p.chunk);
   if (w_id >= p.n_work) return;
@@ -175,7 +179,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const int64_t kvrow = int64_t(kt) * C::BK + 32 * wave + l32;
   const bool kvvalid = kvrow < ntok;
   const int kvrow_i = int(kvrow);
-  int32_t reach = kvvalid ? p.end[kvrow] - kvrow_i : 0;  // rows kv .. kv+reach-1
+  // interval form: rows kv .. kv+reach-1; node form: this key's subtree range
+  int32_t reach = 0, klo = 0, kw = 0;
+  if constexpr (NODES) {
+    klo = kvvalid ? p.nlo[kvrow] : 0;
+    kw = kvvalid ? p.nw[kvrow] : 0;
+  } else {
+    reach = kvvalid ? p.end[kvrow] - kvrow_i : 0;
+  }
 
   const T* Kg = static_cast<const T*>(p.k);
   const T* Vg = static_cast<const T*>(p.v);
@@ -238,6 +249,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   using TStage = TransStage<T, C::BMS, D, C::TS, C::NT>;
   typename std::conditional<C::kBf16, int, TStage>::type qtst, gtst;
   float l2_reg = INFINITY, dl_reg = 0.f;
+  int32_t qk_reg = 0;
   bool l2_valid = false;
   DmaTile<C::BMS, D, C::NT> dt;
   const int pitch = int(ldq) * 2;
@@ -278,11 +290,16 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       if (wave == 1 && lane < C::BMS)
         dma_load4(dma_rsrc(p.Dl + at, nvalid * 4), lane * 4,
                   st + 2 * C::TILE_BYTES + C::BMS * 4);
+      if constexpr (NODES)  // rows past T read node 0: never visible
+        if (wave == 2 && lane < C::BMS)
+          dma_load4(dma_rsrc(p.nkey + q0, nvalid * 4), lane * 4,
+                    st + 2 * C::TILE_BYTES + 2 * C::BMS * 4);
     } else {
       {  // the per-row values first, loaded by every lane; rows past the end read 0
         const int rr = int(threadIdx.x) & (C::BMS - 1);
         l2_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.L2 + at, nvalid * 4), rr * 4));
         dl_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.Dl + at, nvalid * 4), rr * 4));
+        if constexpr (NODES) qk_reg = int32_t(buf_load4(buf_rsrc(p.nkey + q0, nvalid * 4), rr * 4));
         l2_valid = rr < nvalid;
       }
       qst.load(qp, ldq, nvalid);
@@ -302,8 +319,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       gtst.store(base + 2 * C::N_ELEMS + C::T_ELEMS);
     }
     if (threadIdx.x < C::BMS) {
-      ld0[(b * 2 + 0) * C::BMS + threadIdx.x] = l2_valid ? l2_reg : INFINITY;
-      ld0[(b * 2 + 1) * C::BMS + threadIdx.x] = dl_reg;
+      ld0[(b * C::LW + 0) * C::BMS + threadIdx.x] = l2_valid ? l2_reg : INFINITY;
+      ld0[(b * C::LW + 1) * C::BMS + threadIdx.x] = dl_reg;
+      if constexpr (NODES)
+        ld0[(b * C::LW + 2) * C::BMS + threadIdx.x] = __builtin_bit_cast(float, qk_reg);
     }
   };
 
@@ -329,7 +348,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       mark_ready(kf[s]);
       if constexpr (kDK) mark_ready(vf[s]);
     }
-    mark_ready(reach);
+    if constexpr (NODES) {
+      mark_ready(klo);
+      mark_ready(kw);
+    } else {
+      mark_ready(reach);
+    }
   }
   if constexpr (!C::kDma) __syncthreads();
 
@@ -363,8 +387,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const T* Qt = Qs + 2 * C::N_ELEMS;
     const T* Gt = Qt + C::T_ELEMS;
     const float* Ls = C::kDma ? reinterpret_cast<const float*>(st + 2 * C::TILE_BYTES)
-                              : ld0 + (b * 2 + 0) * C::BMS;
-    const float* Dsh = C::kDma ? Ls + C::BMS : ld0 + (b * 2 + 1) * C::BMS;
+                              : ld0 + (b * C::LW + 0) * C::BMS;
+    const float* Dsh = Ls + C::BMS;
+    const int32_t* Qk = reinterpret_cast<const int32_t*>(Ls + 2 * C::BMS);  // node form
 
     {
       const int qd0 = q0i - kvrow_i;  // q - kv at the sub-step's first row
@@ -428,7 +453,23 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int u = 0; u < 4; ++u)
             pv[4 * g + u] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + u], c, -l2v[g][u]));
-        if (partial) {  // uniform branch; full tiles skip the mask
+        if (NODES && partial) {  // uniform branch; node form
+          int4 qkv[4];  // the rows' node numbers
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            qkv[g] = *reinterpret_cast<const int4*>(Qk + 32 * qb + g * 8 + half * 4);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int kq[4] = {qkv[g].x, qkv[g].y, qkv[g].z, qkv[g].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int ii = 4 * g + u;
+              const bool keep = (qd0 + 32 * qb + acc_row(ii, half) >= 0) &
+                                (uint32_t(kq[u] - klo) < uint32_t(kw));
+              pv[ii] = keep ? pv[ii] : 0.f;
+            }
+          }
+        } else if (partial) {  // uniform branch; full tiles skip the mask
 #pragma unroll
           for (int ii = 0; ii < 16; ++ii)
             pv[ii] = visible_u(qd0 + 32 * qb + acc_row(ii, half), reach) ? pv[ii] : 0.f;
@@ -554,7 +595,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 // double-buffered LDS pipeline; Q and dO stay in registers.  bf16 takes K^T for
 // dQ^T += K^T dS^T from the LDS transpose read of the K tile; fp32 stages K^T.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool NODES>
 struct DqCfg {
   static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static constexpr int NW = 4;
@@ -570,12 +611,13 @@ struct DqCfg {
   static constexpr int N_ELEMS = BN * NS;
   static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
   static constexpr int BUF_ELEMS = 2 * N_ELEMS + T_ELEMS;
-  // bf16: K | V | end[] stages filled by direct-to-LDS loads into swizzled tiles (as
-  // the forward); fp32: through registers
+  // bf16: K | V | mask words (end[], or lo[] | w[]) stages filled by direct-to-LDS
+  // loads into swizzled tiles (as the forward); fp32: through registers
   static constexpr bool kDma = kBf16;
+  static constexpr int MW = NODES ? 2 : 1;
   static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + 256;
-  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * BN * 4;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + MW * 256;
+  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * MW * BN * 4;
   static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
 };
 
@@ -583,10 +625,10 @@ struct DqCfg {
 // holds dO for exactly its (row, head) pairs, so it loads O beside it, forms D and
 // LSE in log2 units in registers and writes them to the workspace for the dK/dV
 // kernel, which then runs after it.
-template <typename T, typename G, int D, int MODE, bool PRE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, D>::WAVES_PER_EU)))
+template <typename T, typename G, int D, int MODE, bool PRE, bool NODES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, D, NODES>::WAVES_PER_EU)))
 void dq_kernel(BwdParams p) {
-  using C = DqCfg<T, D>;
+  using C = DqCfg<T, D, NODES>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   T* const buf0 = reinterpret_cast<T*>(smem);
   int32_t* const es0 = reinterpret_cast<int32_t*>(smem + 2 * C::BUF_ELEMS * C::EB);
@@ -647,21 +689,28 @@ void dq_kernel(BwdParams p) {
   DmaTile<C::BN, D, C::NT> dt;
   const int pitch = int(ldk) * 2;
   if constexpr (C::kDma) dt.init(pitch);
-  int32_t e_reg = 0, kv_reg = 0;
+  int32_t e_reg = 0, kv_reg = 0, w_reg = 0;
+  int32_t qkey = 0;  // node form: this row's node number (0: a pad or past T)
+  const int32_t* const ev = NODES ? p.nlo : p.end;
 
   auto issue = [&](int n, int col_n) {
     const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
-    if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | end[]
+    if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | mask words
       char* st = smem + (n & 1) * C::STAGE_BYTES;
       dt.load(Kg + kv0 * ldk + koff, nvalid, pitch, st);
       dt.load(Vg + kv0 * ldk + koff, nvalid, pitch, st + C::TILE_BYTES);
-      if (wave == 0 && lane < C::BN)  // keys past the end read end = 0: never visible
-        dma_load4(dma_rsrc(p.end + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
+      if (wave == 0 && lane < C::BN)  // keys past the end read end = 0 (or w = 0): never visible
+        dma_load4(dma_rsrc(ev + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
+      if constexpr (NODES)
+        if (wave == 1 && lane < C::BN)
+          dma_load4(dma_rsrc(p.nw + kv0, nvalid * 4), lane * 4,
+                    st + 2 * C::TILE_BYTES + C::BN * 4);
     } else {
       {  // every lane loads; a key past the end reads end = 0 and gets reach 0
         const int r = int(threadIdx.x) & (C::BN - 1);
-        e_reg = int32_t(buf_load4(buf_rsrc(p.end + kv0, nvalid * 4), r * 4));
+        e_reg = int32_t(buf_load4(buf_rsrc(ev + kv0, nvalid * 4), r * 4));
+        if constexpr (NODES) w_reg = int32_t(buf_load4(buf_rsrc(p.nw + kv0, nvalid * 4), r * 4));
         kv_reg = r < nvalid ? int32_t(kv0 + r) : 0;
       }
       kst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
@@ -674,7 +723,14 @@ void dq_kernel(BwdParams p) {
     kst.store(base);
     vst.store(base + C::N_ELEMS);
     if constexpr (!C::kBf16) ktst.store(base + 2 * C::N_ELEMS);
-    if (threadIdx.x < C::BN) es0[b * C::BN + threadIdx.x] = e_reg - kv_reg;  // reach
+    if (threadIdx.x < C::BN) {
+      if constexpr (NODES) {  // lo | w
+        es0[b * 2 * C::BN + threadIdx.x] = e_reg;
+        es0[b * 2 * C::BN + C::BN + threadIdx.x] = w_reg;
+      } else {
+        es0[b * C::BN + threadIdx.x] = e_reg - kv_reg;  // reach
+      }
+    }
   };
 
   if (n_steps > 0) {
@@ -708,6 +764,7 @@ void dq_kernel(BwdParams p) {
       l2 = p.L2[int64_t(h) * ntok + qrow];
       dl = p.Dl[int64_t(h) * ntok + qrow];
     }
+    if constexpr (NODES) qkey = qvalid ? p.nkey[qrow] : 0;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       mark_ready(qf[s]);
@@ -715,6 +772,7 @@ void dq_kernel(BwdParams p) {
     }
     mark_ready(l2);
     mark_ready(dl);
+    if constexpr (NODES) mark_ready(qkey);
   }
   if constexpr (!C::kDma) __syncthreads();
 
@@ -740,7 +798,7 @@ void dq_kernel(BwdParams p) {
     const T* Vs = Ks + C::N_ELEMS;
     const T* Kt = Ks + 2 * C::N_ELEMS;
     const int32_t* Es = C::kDma ? reinterpret_cast<const int32_t*>(st + 2 * C::TILE_BYTES)
-                                : es0 + b * C::BN;
+                                : es0 + b * C::MW * C::BN;
 
     {
       const int qd = qrow_i - kv0i;
@@ -785,7 +843,25 @@ void dq_kernel(BwdParams p) {
         float pv[16];
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) pv[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2));
-        if (partial) {  // uniform branch; full tiles skip the mask
+        if (NODES && partial) {  // uniform branch; node form
+          int4 los[4], ws[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            los[g] = *reinterpret_cast<const int4*>(Es + 32 * kb + g * 8 + half * 4);
+            ws[g] = *reinterpret_cast<const int4*>(Es + C::BN + 32 * kb + g * 8 + half * 4);
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int kvl = 32 * kb + g * 8 + half * 4;
+            const int lv[4] = {los[g].x, los[g].y, los[g].z, los[g].w};
+            const int wv[4] = {ws[g].x, ws[g].y, ws[g].z, ws[g].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const bool keep = (kvl + u <= qd) & (uint32_t(qkey - lv[u]) < uint32_t(wv[u]));
+              pv[4 * g + u] = keep ? pv[4 * g + u] : 0.f;
+            }
+          }
+        } else if (partial) {  // uniform branch; full tiles skip the mask
           // this lane's end[] (or reach) values first, their LDS reads in flight
           // together; the two tests combined without a short circuit, so no test
           // turns into a branch around a read
@@ -893,7 +969,7 @@ void dq_kernel(BwdParams p) {
 
 size_t ws_align(size_t x) { return (x + 255) / 256 * 256; }
 
-template <typename T, typename G, int D, int MODE>
+template <typename T, typename G, int D, int MODE, bool NODES>
 hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void* q,
                         const void* k, const void* v, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, void* workspace,
@@ -912,6 +988,9 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.Dl = static_cast<float*>(workspace);
   p.L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + plane);
   p.end = map.end;
+  p.nkey = map.nkey;
+  p.nlo = map.nlo;
+  p.nw = map.nw;
   p.row_ptr = map.row_ptr;
   p.col = map.col;
   p.kind = map.kind;
@@ -936,8 +1015,8 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
     p.chunk = rep * 2;
     const int64_t per = 8 * int64_t(p.chunk);
     const int64_t grid = (p.n_work + per - 1) / per * per;
-    hipLaunchKernelGGL((dq_kernel<T, G, D, MODE, PRE>), dim3(unsigned(grid)), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((dq_kernel<T, G, D, MODE, PRE, NODES>), dim3(unsigned(grid)), dim3(256),
+                       0, stream, p);
   };
   if (fused) {
     launch_dq(std::true_type{});
@@ -952,13 +1031,13 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
     const int64_t per = 8 * int64_t(p.chunk);
     const int64_t grid = (p.n_work + per - 1) / per * per;
     if constexpr (D > 128) {  // dV and dK in two passes (see dkdv_kernel)
-      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 1>), dim3(unsigned(grid)), dim3(256), 0,
-                         stream, p);
-      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 2>), dim3(unsigned(grid)), dim3(256), 0,
-                         stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 1, NODES>), dim3(unsigned(grid)),
+                         dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 2, NODES>), dim3(unsigned(grid)),
+                         dim3(256), 0, stream, p);
     } else {
-      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 0>), dim3(unsigned(grid)), dim3(256), 0,
-                         stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 0, NODES>), dim3(unsigned(grid)),
+                         dim3(256), 0, stream, p);
     }
   }
   if ((stages & PSA_STAGE_DQ) && !fused) launch_dq(std::false_type{});
@@ -979,9 +1058,12 @@ hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype gdt, cons
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       void* workspace, int stages, bool split, hipStream_t stream) {
   using psa::bf16_t;
-#define PSA_BWD(T, G, D, MODE)                                                      \
-  return psa::launch_bwd_t<T, G, D, MODE>(map, s, q, k, v, o, lse, dout, dq, dk, dv, \
-                                          workspace, stages, stream)
+#define PSA_BWD(T, G, D, MODE)                                                            \
+  return map.form == kFormNodes                                                            \
+             ? psa::launch_bwd_t<T, G, D, MODE, true>(map, s, q, k, v, o, lse, dout, dq, dk, \
+                                                      dv, workspace, stages, stream)       \
+             : psa::launch_bwd_t<T, G, D, MODE, false>(map, s, q, k, v, o, lse, dout, dq, dk, \
+                                                       dv, workspace, stages, stream)
 #define PSA_BWD_BF16(G, D)                          \
   if (split) PSA_BWD(bf16_t, G, D, psa::kSplitAll); \
   PSA_BWD(bf16_t, G, D, psa::kSplitAdaptive)

@@ -8,7 +8,8 @@
 // one is computed and written to the other buffer after it, so each sub-step needs
 // one barrier and its loads overlap the math.  Per sub-step and wave:
 //   S^T = K Q^T on MFMA (Q stays in registers);
-//   the mask kv <= q < end[kv], as a select, on partial tiles only;
+//   the mask, as a select, on partial tiles only: kv <= q < end[kv] (interval form)
+//   or kv <= q with q's node in kv's subtree (node form, any layout);
 //   the online softmax in the exp2 domain (log2(e) folded into the scale); the
 //   running max is raised only when a row's max grows by more than 2^8 (the
 //   result is the same: m cancels between O and l; it only bounds P by 2^8), so
@@ -40,7 +41,10 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;
-  const int32_t* end;
+  const int32_t* end;   // interval form
+  const int32_t* nkey;  // node form
+  const int32_t* nlo;
+  const int32_t* nw;
   const int32_t* row_ptr;
   const int32_t* col;
   const uint8_t* kind;
@@ -54,7 +58,7 @@ struct FwdParams {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays below 2^8
 
-template <typename T, int D>
+template <typename T, int D, bool NODES>
 struct FwdCfg {
   static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static constexpr int NW = 4;
@@ -70,17 +74,19 @@ struct FwdCfg {
   static constexpr int V_ELEMS = kBf16 ? BN * VS : D * VS;
   static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
   // bf16 tiles come in by direct-to-LDS loads into swizzled, unpadded tiles (two
-  // stages of K | V | end[]); fp32 tiles go through registers into padded tiles.
+  // stages of K | V | mask words); fp32 tiles go through registers into padded tiles.
+  // Mask words per key: end[] (interval form) or lo[] | w[] (node form).
   static constexpr bool kDma = kBf16;
+  static constexpr int MW = NODES ? 2 : 1;
   static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + BN * 4;
-  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * BN * 4;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + MW * BN * 4;
+  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * MW * BN * 4;
   static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D>::WAVES_PER_EU))) void fwd_kernel(FwdParams p) {
-  using C = FwdCfg<T, D>;
+template <typename T, int D, bool NODES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D, NODES>::WAVES_PER_EU))) void fwd_kernel(FwdParams p) {
+  using C = FwdCfg<T, D, NODES>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   T* const buf0 = reinterpret_cast<T*>(smem);
   int32_t* const es0 = reinterpret_cast<int32_t*>(smem + 2 * C::BUF_ELEMS * C::EB);
@@ -146,23 +152,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   DmaTile<C::BN, D, C::NT> dt;
   const int pitch = int(ldk) * 2;
   if constexpr (C::kDma) dt.init(pitch);
-  int32_t e_reg = 0, kv_reg = 0;
+  int32_t e_reg = 0, kv_reg = 0, w_reg = 0;
+  int32_t qkey = 0;  // node form: this row's node number (0: a pad or past T)
+  const int32_t* const ev = NODES ? p.nlo : p.end;
 
   auto issue = [&](int n, int col_n) {  // global reads of sub-step n
     const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
-    if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | end[]
+    if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | mask words
       static_assert(C::BN == 64, "one end[] value per lane");
       char* st = smem + (n & 1) * C::STAGE_BYTES;
       dt.load(K + kv0 * ldk + koff, nvalid, pitch, st);
       dt.load(V + kv0 * ldk + koff, nvalid, pitch, st + C::TILE_BYTES);
-      if (wave == 0)  // keys past the end read end = 0: never visible
-        dma_load4(dma_rsrc(p.end + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
+      if (wave == 0)  // keys past the end read end = 0 (or w = 0): never visible
+        dma_load4(dma_rsrc(ev + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
+      if constexpr (NODES)
+        if (wave == 1)
+          dma_load4(dma_rsrc(p.nw + kv0, nvalid * 4), lane * 4,
+                    st + 2 * C::TILE_BYTES + C::BN * 4);
     } else {  // into registers; commit() stores them
-      // end[] first: the loads retire in order, so waiting for it at commit does not
-      // wait for the K/V reads issued after it
+      // mask words first: the loads retire in order, so waiting for them at commit
+      // does not wait for the K/V reads issued after them
       const int r = int(threadIdx.x) & (C::BN - 1);
-      e_reg = int32_t(buf_load4(buf_rsrc(p.end + kv0, nvalid * 4), r * 4));
+      e_reg = int32_t(buf_load4(buf_rsrc(ev + kv0, nvalid * 4), r * 4));
+      if constexpr (NODES) w_reg = int32_t(buf_load4(buf_rsrc(p.nw + kv0, nvalid * 4), r * 4));
       kv_reg = r < nvalid ? int32_t(kv0 + r) : 0;
       kst.load(K + kv0 * ldk + koff, ldk, nvalid);
       vst.load(V + kv0 * ldk + koff, ldk, nvalid);
@@ -172,7 +185,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     T* kb = buf0 + b * C::BUF_ELEMS;
     kst.store(kb);
     vst.store(kb + C::K_ELEMS);
-    if (threadIdx.x < C::BN) es0[b * C::BN + threadIdx.x] = e_reg - kv_reg;  // reach
+    if (threadIdx.x < C::BN) {
+      if constexpr (NODES) {  // lo | w
+        es0[b * 2 * C::BN + threadIdx.x] = e_reg;
+        es0[b * 2 * C::BN + C::BN + threadIdx.x] = w_reg;
+      } else {
+        es0[b * C::BN + threadIdx.x] = e_reg - kv_reg;  // reach
+      }
+    }
   };
 
   if (n_steps > 0) {
@@ -183,8 +203,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     const T* qp = Q + (qrow * hq + h) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = qvalid ? frag_load(qp + 16 * s) : frag_zero<T>();
+    if constexpr (NODES) qkey = qvalid ? p.nkey[qrow] : 0;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) mark_ready(qf[s]);
+    if constexpr (NODES) mark_ready(qkey);
   }
   if constexpr (!C::kDma) __syncthreads();
 
@@ -211,7 +233,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     const T* Ks = buf0 + b * C::BUF_ELEMS;       // register-path buffer
     const T* Vs = Ks + C::K_ELEMS;
     const int32_t* Es = C::kDma ? reinterpret_cast<const int32_t*>(st + 2 * C::TILE_BYTES)
-                                : es0 + b * C::BN;
+                                : es0 + b * C::MW * C::BN;
 
     {
       // S^T = K Q^T for BN keys x 32 queries (this wave)
@@ -264,7 +286,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
 #pragma unroll
           for (int i = 0; i < 16; ++i) sv[kb][i] = acc_s[kb][i];
       }
-      if (partial) {  // uniform branch; full tiles skip the mask
+      if (NODES && partial) {  // uniform branch; node form
+        const int qd = qrow_i - kv0i;
+#pragma unroll
+        for (int kb = 0; kb < C::BN / 32; ++kb) {
+          int4 los[4], ws[4];  // this lane's keys' lo and w, read together
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            los[g] = *reinterpret_cast<const int4*>(Es + 32 * kb + g * 8 + half * 4);
+            ws[g] = *reinterpret_cast<const int4*>(Es + C::BN + 32 * kb + g * 8 + half * 4);
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int kvl = 32 * kb + g * 8 + half * 4;
+            const int lv[4] = {los[g].x, los[g].y, los[g].z, los[g].w};
+            const int wv[4] = {ws[g].x, ws[g].y, ws[g].z, ws[g].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const bool keep = (kvl + u <= qd) & (uint32_t(qkey - lv[u]) < uint32_t(wv[u]));
+              sv[kb][4 * g + u] = keep ? sv[kb][4 * g + u] : -INFINITY;
+            }
+          }
+        }
+      } else if (partial) {  // uniform branch; full tiles skip the mask
         const int qd = qrow_i - kv0i;  // q - kv for the sub-step's first key
         // all of this lane's end[] (or reach) values first, so that their LDS reads
         // are in flight together
@@ -375,6 +419,9 @@ hipError_t launch_fwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.o = o;
   p.lse = lse;
   p.end = map.end;
+  p.nkey = map.nkey;
+  p.nlo = map.nlo;
+  p.nw = map.nw;
   p.row_ptr = map.row_ptr;
   p.col = map.col;
   p.kind = map.kind;
@@ -388,7 +435,10 @@ hipError_t launch_fwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.chunk = rep * 2;
   const int64_t per = 8 * int64_t(p.chunk);
   const int64_t grid = (p.n_work + per - 1) / per * per;
-  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+  if (map.form == kFormNodes)
+    hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, false>), dim3(unsigned(grid)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

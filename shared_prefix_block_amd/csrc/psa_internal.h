@@ -9,17 +9,33 @@
 
 #include "psa.h"
 
-// The tile map: per-token interval ends plus the full/partial/empty classification
-// of every (q-tile, kv-tile) pair, as a dense kinds matrix and as CSR / CSC lists.
+// The tile map: the per-token mask encoding plus the full/partial/empty
+// classification of every (q-tile, kv-tile) pair, as a dense kinds matrix and as
+// CSR / CSC lists.
+//
+// Two encodings of keep(q, kv):
+//  - interval form (packed layouts): kv <= q < end[kv];
+//  - node form (any layout): kv <= q and lo[kv] <= key[q] < lo[kv] + w[kv], where
+//    key[t] is the pre-order number (from 1) of t's node in the prefix forest and
+//    [lo, lo + w) the pre-order numbers of the node's subtree; pads have key 0 and
+//    w 0, so they see nothing and are seen by nothing.
+constexpr int32_t kFormInterval = 0, kFormNodes = 1;
 struct psa_tile_map {
   int64_t T = 0;
   int32_t bm = 0, bn = 0;
   int64_t nq = 0, nk = 0;
   int64_t nnz = 0, n_full = 0, n_partial = 0;
+  int32_t form = kFormInterval;
   int device = 0;
   hipStream_t stream = nullptr;  // build stream (export waits on it; buffers freed on it)
-  size_t buf1_bytes = 0, buf2_bytes = 0;  // sizes of the two device buffers
-  hipEvent_t ev1 = nullptr, ev2 = nullptr;  // their reuse events (cached buffers)
+  size_t buf1_bytes = 0, buf2_bytes = 0, buf3_bytes = 0;  // sizes of the device buffers
+  hipEvent_t ev1 = nullptr, ev2 = nullptr, ev3 = nullptr;  // their reuse events
+
+  // node form (buf3): key | lo | w, T int32 each
+  void* buf3 = nullptr;
+  int32_t* nkey = nullptr;
+  int32_t* nlo = nullptr;
+  int32_t* nw = nullptr;
 
   // phase-1 allocation (sized before the sync)
   void* buf1 = nullptr;
@@ -57,12 +73,29 @@ hipError_t launch_tokens_end(int64_t T, const int32_t* group, const int32_t* suf
 hipError_t launch_tree_end(int64_t T, int64_t n_nodes, const int64_t* node_start,
                            const int64_t* node_subtree_end, int64_t t_real, int32_t* end,
                            hipStream_t stream);
+// Node form from labels: key / lo / w per token (see psa_tile_map).  Nodes are the
+// groups' prompts and completions, numbered in the order of (group id, prompt first,
+// then completion ids).  scratch: tokens_nodes_scratch_bytes(T) bytes.
+size_t tokens_nodes_scratch_bytes(int64_t T);
+hipError_t launch_tokens_nodes(int64_t T, const int32_t* group, const int32_t* suffix,
+                               const uint8_t* is_prefix, int32_t* key, int32_t* lo,
+                               int32_t* w, void* scratch, size_t scratch_bytes,
+                               hipStream_t stream);
+// Node form from a per-node table (node token start, pre-order number, subtree size).
+hipError_t launch_tree_nodes(int64_t T, int64_t n_nodes, const int64_t* node_start,
+                             const int64_t* node_pre, const int64_t* node_size, int64_t t_real,
+                             int32_t* key, int32_t* lo, int32_t* w, hipStream_t stream);
 // Classification + counts + pointer scans (after launch_map_init).  info (device,
 // 8 x int64) receives nnz, n_full, n_partial.
 hipError_t launch_classify(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk,
                            const int32_t* end, uint8_t* kinds, int32_t* row_ptr,
                            int32_t* col_ptr, int32_t* ktile_min_end, int32_t* ktile_max_end,
                            int64_t* info, hipStream_t stream);
+// The same from the node form.  ksum: 4 * align64(nk) ints of scratch.
+hipError_t launch_classify_nodes(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk,
+                                 const int32_t* key, const int32_t* lo, const int32_t* w,
+                                 uint8_t* kinds, int32_t* row_ptr, int32_t* col_ptr,
+                                 int32_t* ksum, int64_t* info, hipStream_t stream);
 // CSR and CSC lists (ordered compaction of kinds) and the two length orders.
 hipError_t launch_fill_lists(int64_t nq, int64_t nk, const uint8_t* kinds,
                              const int32_t* row_ptr, const int32_t* col_ptr, int32_t* col,

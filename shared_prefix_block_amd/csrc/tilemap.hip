@@ -15,7 +15,16 @@
 // never computed), then lays the non-empty tiles out as CSR (per q-tile) and CSC
 // (per kv-tile) lists in ascending order.  Everything is integer work with scans or
 // integer atomics whose sums do not depend on order, so the map is deterministic.
+//
+// Layouts that are not packed this way (groups or completions interleaved, a prompt
+// token after a completion token, group or completion ids out of order, a prefix tree
+// whose subtrees are not contiguous) have no interval form; they get the node form
+// instead (psa_tile_map): every token carries the pre-order number of its node in the
+// prefix forest (a group's prompt is the parent of its completions), every key the
+// pre-order range of its node's subtree, and keep(q, kv) is kv <= q with q's node in
+// kv's subtree, which is the same rule written on nodes.
 #include <hip/hip_runtime.h>
+#include <hipcub/hipcub.hpp>
 
 #include <climits>
 #include <cstdint>
@@ -216,6 +225,95 @@ __global__ void k_tree_end(int64_t T, int64_t n_nodes, const int64_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Step 1c: labels -> node form.  A node is (group, prompt) or (group, completion s);
+// its sort key is group * 2^33 + (0 for the prompt, 1 + s as unsigned 32-bit for a
+// completion), so a group's nodes are one contiguous run of sorted keys with the
+// prompt first.  The node number is the rank among the distinct keys, plus 1; a
+// prompt's subtree is every node of its group, a completion's is itself.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kPadComposite = ~0ull;  // above every real key: sorts last
+
+__device__ inline uint64_t node_composite(int32_t g, int32_t s, uint8_t pf) {
+  return (uint64_t(uint32_t(g)) << 33) | (pf ? 0ull : uint64_t(uint32_t(s)) + 1ull);
+}
+
+__global__ void k_node_composite(int64_t T, const int32_t* __restrict__ group,
+                                 const int32_t* __restrict__ suffix,
+                                 const uint8_t* __restrict__ is_prefix,
+                                 uint64_t* __restrict__ comp) {
+  for (int64_t t = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; t < T;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    const int32_t g = group[t];
+    comp[t] = g < 0 ? kPadComposite : node_composite(g, suffix[t], is_prefix[t]);
+  }
+}
+
+// first index in uniq[0, n) whose value is > x (x < x_limit is not assumed)
+__device__ inline int64_t upper_index(const uint64_t* __restrict__ uniq, int64_t n, uint64_t x) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (uniq[mid] <= x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void k_node_number(int64_t T, const int32_t* __restrict__ group,
+                              const uint8_t* __restrict__ is_prefix,
+                              const uint64_t* __restrict__ comp,
+                              const uint64_t* __restrict__ uniq,
+                              const int64_t* __restrict__ n_uniq, int32_t* __restrict__ key,
+                              int32_t* __restrict__ lo, int32_t* __restrict__ w) {
+  const int64_t n = *n_uniq;
+  for (int64_t t = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; t < T;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    const uint64_t c = comp[t];
+    if (c == kPadComposite) {
+      key[t] = 0;
+      lo[t] = 0;
+      w[t] = 0;
+      continue;
+    }
+    const int64_t r = upper_index(uniq, n, c) - 1;  // rank of c itself
+    int64_t width = 1;
+    if (is_prefix[t]) {  // every key of the group: up to group * 2^33 + (2^33 - 1)
+      const uint64_t last = (uint64_t(uint32_t(group[t])) << 33) | ((1ull << 33) - 1);
+      width = upper_index(uniq, n, last) - r;
+    }
+    key[t] = int32_t(r + 1);
+    lo[t] = int32_t(r + 1);
+    w[t] = int32_t(width);
+  }
+}
+
+// Step 1d: per-node table -> node form (the tree's pre-order numbering is the host's).
+__global__ void k_tree_nodes(int64_t T, int64_t n_nodes, const int64_t* __restrict__ node_start,
+                             const int64_t* __restrict__ pre, const int64_t* __restrict__ size,
+                             int64_t t_real, int32_t* __restrict__ key, int32_t* __restrict__ lo,
+                             int32_t* __restrict__ w) {
+  for (int64_t t = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; t < T;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    if (t >= t_real) {
+      key[t] = 0;
+      lo[t] = 0;
+      w[t] = 0;
+      continue;
+    }
+    int64_t a = 0, b = n_nodes;  // first node with node_start > t; the one before owns t
+    while (a < b) {
+      const int64_t mid = (a + b) >> 1;
+      if (node_start[mid] <= t) a = mid + 1;
+      else b = mid;
+    }
+    const int64_t node = a - 1;
+    key[t] = int32_t(pre[node] + 1);
+    lo[t] = int32_t(pre[node] + 1);
+    w[t] = int32_t(size[node]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Step 2: classification
 // ---------------------------------------------------------------------------
 // info[0..2] = nnz, n_full, n_partial; info[3] = first layout error (all ones: none).
@@ -300,6 +398,151 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_rows(
     red[0][w] = cnt;
     red[1][w] = nfull;
     red[2][w] = npart;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, b = 0, c = 0;
+    for (int k = 0; k < kClassifyThreads / 64; ++k) {
+      a += red[0][k];
+      b += red[1][k];
+      c += red[2][k];
+    }
+    row_ptr[i + 1] = a;
+    atomicAdd(reinterpret_cast<unsigned long long*>(&info[1]), (unsigned long long)b);
+    atomicAdd(reinterpret_cast<unsigned long long*>(&info[2]), (unsigned long long)c);
+  }
+}
+
+// Node form.  One wave per kv-tile: over its keys with w > 0, the smallest lo and the
+// largest lo + w (INT_MAX / 0 if none); and, for the full test, the largest lo and
+// the smallest lo + w over all its columns, or INT_MAX / 0 if a column is a pad or
+// lies past T (such a tile is never full).
+__global__ __launch_bounds__(64) void k_ktile_summary_nodes(int64_t T, int32_t bn, int64_t nk,
+                                                            const int32_t* __restrict__ lo,
+                                                            const int32_t* __restrict__ w,
+                                                            int32_t* ksum, int64_t stride) {
+  const int64_t j = blockIdx.x;
+  if (j >= nk) return;
+  const int64_t k0 = j * bn;
+  const int64_t k1 = k0 + bn < T ? k0 + bn : T;
+  int mn = INT_MAX, mx = 0, flo = 0, fhi = INT_MAX;
+  bool all = k0 + bn <= T;
+  for (int64_t kv = k0 + threadIdx.x; kv < k1; kv += 64) {
+    const int a = lo[kv], n = w[kv];
+    if (n > 0) {
+      mn = a < mn ? a : mn;
+      mx = a + n > mx ? a + n : mx;
+      flo = a > flo ? a : flo;
+      fhi = a + n < fhi ? a + n : fhi;
+    } else {
+      all = false;
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int a = __shfl_xor(mn, off), b = __shfl_xor(mx, off);
+    const int c = __shfl_xor(flo, off), d = __shfl_xor(fhi, off);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+    flo = c > flo ? c : flo;
+    fhi = d < fhi ? d : fhi;
+  }
+  all = __all(all);
+  if (threadIdx.x == 0) {
+    ksum[j] = mn;
+    ksum[stride + j] = mx;
+    ksum[2 * stride + j] = all ? flo : INT_MAX;
+    ksum[3 * stride + j] = all ? fhi : 0;
+  }
+}
+
+// One block per q-tile, its keys in LDS; each wave takes every fourth kv-tile.  A
+// tile is empty when it lies wholly after the q-tile (kv > q everywhere) or when the
+// keys' subtree ranges miss the q-tile's key range; full when it lies wholly at or
+// before the q-tile and every range holds every key; otherwise the wave searches it
+// exactly, one column per lane, for a kept pair.
+__global__ __launch_bounds__(kClassifyThreads) void k_classify_nodes_rows(
+    int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk, const int32_t* __restrict__ key,
+    const int32_t* __restrict__ lo, const int32_t* __restrict__ w,
+    const int32_t* __restrict__ ksum, int64_t stride, uint8_t* kinds, int32_t* row_ptr,
+    int32_t* col_ptr, int64_t* info) {
+  __shared__ int32_t qk[1024];
+  __shared__ int red[3][kClassifyThreads / 64];
+  const int64_t i = blockIdx.x;
+  const int64_t q0 = i * bm;
+  const int64_t q_last = (q0 + bm < T ? q0 + bm : T) - 1;
+  const bool rows_in = q0 + bm <= T;
+  const int nrow = int(q_last - q0 + 1);
+  int kmin = INT_MAX, kmax = 0;  // over real rows (key > 0)
+  bool all_real = rows_in;
+  for (int r = threadIdx.x; r < nrow; r += kClassifyThreads) {
+    const int k = key[q0 + r];
+    qk[r] = k;
+    if (k > 0) {
+      kmin = k < kmin ? k : kmin;
+      kmax = k > kmax ? k : kmax;
+    } else {
+      all_real = false;
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int a = __shfl_xor(kmin, off), b = __shfl_xor(kmax, off);
+    kmin = a < kmin ? a : kmin;
+    kmax = b > kmax ? b : kmax;
+  }
+  all_real = __all(all_real);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[0][wv] = kmin;
+    red[1][wv] = kmax;
+    red[2][wv] = all_real ? 1 : 0;
+  }
+  __syncthreads();
+  for (int k = 0; k < kClassifyThreads / 64; ++k) {
+    kmin = red[0][k] < kmin ? red[0][k] : kmin;
+    kmax = red[1][k] > kmax ? red[1][k] : kmax;
+    all_real = all_real && red[2][k];
+  }
+  __syncthreads();
+
+  int cnt = 0, nfull = 0, npart = 0;  // lane 0 of each wave counts its tiles
+  for (int64_t j = wv; j < nk; j += kClassifyThreads / 64) {
+    const int64_t k0 = j * bn;
+    const int64_t k_last = (k0 + bn < T ? k0 + bn : T) - 1;
+    const int mn = ksum[j], mx = ksum[stride + j];
+    uint8_t kind = 0;
+    if (k0 <= q_last && kmax > 0 && mn != INT_MAX && mx > kmin && mn <= kmax) {
+      if (all_real && k0 + bn <= T && k_last <= q0 && ksum[2 * stride + j] <= kmin &&
+          kmax < ksum[3 * stride + j]) {
+        kind = 2;
+      } else {
+        bool found = false;
+        for (int64_t kv = k0 + lane; kv <= k_last && !found; kv += 64) {
+          const int a = lo[kv], n = w[kv];
+          if (n <= 0) continue;
+          for (int64_t r = (kv > q0 ? kv : q0) - q0; r < nrow; ++r) {
+            if (uint32_t(qk[r] - a) < uint32_t(n)) {
+              found = true;
+              break;
+            }
+          }
+        }
+        kind = __any(found) ? 1 : 0;
+      }
+    }
+    if (lane == 0) {
+      kinds[i * nk + j] = kind;
+      if (kind) {
+        ++cnt;
+        if (kind == 2) ++nfull;
+        else ++npart;
+        atomicAdd(&col_ptr[j + 1], 1);
+      }
+    }
+  }
+  if (lane == 0) {
+    red[0][wv] = cnt;
+    red[1][wv] = nfull;
+    red[2][wv] = npart;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -458,6 +701,78 @@ hipError_t launch_classify(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_
   if (nq > 0) {
     hipLaunchKernelGGL(k_classify_rows, dim3(unsigned(nq)), dim3(kClassifyThreads), 0, stream, T,
                        bm, bn, nq, nk, end, kmin, kmax, kinds, row_ptr, col_ptr, info);
+  }
+  hipLaunchKernelGGL(k_scan_ptrs, dim3(1), dim3(kScanThreads), 0, stream, nq, nk, row_ptr,
+                     col_ptr, info);
+  return hipGetLastError();
+}
+
+size_t tokens_nodes_scratch_bytes(int64_t T) {
+  const size_t n = size_t(T > 0 ? T : 1);
+  size_t sort_b = 0, uniq_b = 0;
+  uint64_t* none = nullptr;
+  int64_t* cnt = nullptr;
+  (void)hipcub::DeviceRadixSort::SortKeys(nullptr, sort_b, none, none, int64_t(n), 0, 64);
+  (void)hipcub::DeviceSelect::Unique(nullptr, uniq_b, none, none, cnt, int64_t(n));
+  const size_t arr = (n * 8 + 255) / 256 * 256;
+  return 3 * arr + 256 + (sort_b > uniq_b ? sort_b : uniq_b);
+}
+
+hipError_t launch_tokens_nodes(int64_t T, const int32_t* group, const int32_t* suffix,
+                               const uint8_t* is_prefix, int32_t* key, int32_t* lo,
+                               int32_t* w, void* scratch, size_t scratch_bytes,
+                               hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const size_t arr = (size_t(T) * 8 + 255) / 256 * 256;
+  char* base = static_cast<char*>(scratch);
+  uint64_t* comp = reinterpret_cast<uint64_t*>(base);
+  uint64_t* sorted = reinterpret_cast<uint64_t*>(base + arr);
+  uint64_t* uniq = reinterpret_cast<uint64_t*>(base + 2 * arr);
+  int64_t* n_uniq = reinterpret_cast<int64_t*>(base + 3 * arr);
+  void* tmp = base + 3 * arr + 256;
+  if (scratch_bytes < 3 * arr + 256) return hipErrorInvalidValue;
+  size_t tmp_bytes = scratch_bytes - (3 * arr + 256);
+  int64_t blocks = (T + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_node_composite, dim3(unsigned(blocks)), dim3(256), 0, stream, T, group,
+                     suffix, is_prefix, comp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  size_t b = tmp_bytes;
+  e = hipcub::DeviceRadixSort::SortKeys(tmp, b, comp, sorted, T, 0, 64, stream);
+  if (e != hipSuccess) return e;
+  b = tmp_bytes;
+  e = hipcub::DeviceSelect::Unique(tmp, b, sorted, uniq, n_uniq, T, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_node_number, dim3(unsigned(blocks)), dim3(256), 0, stream, T, group,
+                     is_prefix, comp, uniq, n_uniq, key, lo, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_nodes(int64_t T, int64_t n_nodes, const int64_t* node_start,
+                             const int64_t* node_pre, const int64_t* node_size, int64_t t_real,
+                             int32_t* key, int32_t* lo, int32_t* w, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  int64_t blocks = (T + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_tree_nodes, dim3(unsigned(blocks)), dim3(256), 0, stream, T, n_nodes,
+                     node_start, node_pre, node_size, t_real, key, lo, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_classify_nodes(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk,
+                                 const int32_t* key, const int32_t* lo, const int32_t* w,
+                                 uint8_t* kinds, int32_t* row_ptr, int32_t* col_ptr,
+                                 int32_t* ksum, int64_t* info, hipStream_t stream) {
+  const int64_t stride = (nk + 63) / 64 * 64;
+  if (nk > 0) {
+    hipLaunchKernelGGL(k_ktile_summary_nodes, dim3(unsigned(nk)), dim3(64), 0, stream, T, bn,
+                       nk, lo, w, ksum, stride);
+  }
+  if (nq > 0) {
+    hipLaunchKernelGGL(k_classify_nodes_rows, dim3(unsigned(nq)), dim3(kClassifyThreads), 0,
+                       stream, T, bm, bn, nq, nk, key, lo, w, ksum, stride, kinds, row_ptr,
+                       col_ptr, info);
   }
   hipLaunchKernelGGL(k_scan_ptrs, dim3(1), dim3(kScanThreads), 0, stream, nq, nk, row_ptr,
                      col_ptr, info);

@@ -32,7 +32,10 @@ EXPORTS = ["psa_abi_version", "psa_status_string", "psa_last_error", "psa_tile_s
            "psa_build_tile_map_tokens", "psa_build_tile_map_tree", "psa_tile_map_info_get",
            "psa_tile_map_export", "psa_tile_map_destroy", "psa_fwd", "psa_bwd_workspace_size",
            "psa_bwd", "psa_bwd_stages", "psa_fold_workspace_size", "psa_fold_rollouts",
-           "psa_unfold_rows"]
+           "psa_unfold_rows", "psa_build_tile_map_tokens_ex", "psa_build_tile_map_tree_ex",
+           "psa_tile_map_export_nodes"]
+FORM_INTERVAL, FORM_NODES = 0, 1  # mask encodings of a map (info["form"])
+MAP_NODE_FORM = 1  # build flag: the node form even where the interval form exists
 STAGE_PREPARE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 BWD_SPLIT_PDS = 16  # option bit of psa_bwd_stages: P and dS as hi + lo bf16 pairs
 
@@ -48,7 +51,7 @@ class TileMapInfo(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
                 ("n_qtiles", ctypes.c_int64), ("n_ktiles", ctypes.c_int64),
                 ("nnz", ctypes.c_int64), ("n_full", ctypes.c_int64),
-                ("n_partial", ctypes.c_int64)]
+                ("n_partial", ctypes.c_int64), ("form", ctypes.c_int32)]
 
 
 def lib_path() -> str:
@@ -76,6 +79,10 @@ def load() -> ctypes.CDLL:
                                               ctypes.POINTER(I32), ctypes.POINTER(I32)]),
             "psa_build_tile_map_tokens": (ctypes.c_int, [I64, P, P, P, I32, I32, P, PP]),
             "psa_build_tile_map_tree": (ctypes.c_int, [I64, P, I64, P, P, I64, I32, I32, P, PP]),
+            "psa_build_tile_map_tokens_ex": (ctypes.c_int, [I64, P, P, P, I32, I32, I32, P, PP]),
+            "psa_build_tile_map_tree_ex": (ctypes.c_int, [I64, P, I64, P, P, I64, I32, I32, I32,
+                                                          P, PP]),
+            "psa_tile_map_export_nodes": (ctypes.c_int, [P, P, P, P]),
             "psa_tile_map_info_get": (ctypes.c_int, [P, ctypes.POINTER(TileMapInfo)]),
             "psa_tile_map_export": (ctypes.c_int, [P, P, P, P, P, P, P, P, P]),
             "psa_tile_map_destroy": (None, [P]),
@@ -162,10 +169,13 @@ class TileMap:
             pass
 
     def export(self) -> dict:
-        """end, kinds [nq, nk], CSR and CSC as numpy arrays."""
+        """kinds [nq, nk], CSR and CSC as numpy arrays, and the mask encoding: end (an
+        interval-form map) and key, lo, w (either form; see export_nodes)."""
         i = self.info
         T, nq, nk, nnz = i["T"], i["n_qtiles"], i["n_ktiles"], i["nnz"]
-        out = {"end": np.zeros(T, np.int32), "kinds": np.zeros(nq * nk, np.uint8),
+        interval = i["form"] == FORM_INTERVAL
+        out = {"end": np.zeros(T if interval else 0, np.int32),
+               "kinds": np.zeros(nq * nk, np.uint8),
                "row_ptr": np.zeros(nq + 1, np.int32), "col": np.zeros(nnz, np.int32),
                "kind": np.zeros(nnz, np.uint8), "col_ptr": np.zeros(nk + 1, np.int32),
                "row": np.zeros(nnz, np.int32), "kind_csc": np.zeros(nnz, np.uint8)}
@@ -173,13 +183,29 @@ class TileMap:
                 for a in out.values()]
         _check(load().psa_tile_map_export(self.handle, *args))
         out["kinds"] = out["kinds"].reshape(nq, nk)
+        if not interval:
+            del out["end"]
+        out.update(self.export_nodes())
+        return out
+
+    def export_nodes(self) -> dict:
+        """key, lo, w [T] int32: kv visible to q iff kv <= q and lo[kv] <= key[q] <
+        lo[kv] + w[kv] (an interval-form map as key = lo = t, w = end - t)."""
+        T = self.info["T"]
+        out = {n: np.zeros(T, np.int32) for n in ("key", "lo", "w")}
+        args = [ctypes.c_void_p(a.ctypes.data) if a.size else ctypes.c_void_p(0)
+                for a in out.values()]
+        _check(load().psa_tile_map_export_nodes(self.handle, *args))
         return out
 
 
 def build_tile_map_tokens(group: torch.Tensor, suffix: torch.Tensor, is_prefix: torch.Tensor,
                           block_m: Optional[int] = None, block_n: Optional[int] = None,
-                          dtype: torch.dtype = torch.bfloat16, d: int = 128) -> TileMap:
-    """Tile map from per-token labels (device tensors: int32, int32, uint8)."""
+                          dtype: torch.dtype = torch.bfloat16, d: int = 128,
+                          form: str = "auto") -> TileMap:
+    """Tile map from per-token labels (device tensors: int32, int32, uint8).  form
+    "auto": the interval form for packed layouts, else the node form; "nodes": always
+    the node form."""
     lib = load()
     if block_m is None or block_n is None:
         block_m, block_n = tile_shape(PASS_FWD, dtype, d)
@@ -192,16 +218,24 @@ def build_tile_map_tokens(group: torch.Tensor, suffix: torch.Tensor, is_prefix: 
     dev = group.device
     out = ctypes.c_void_p()
     with torch.cuda.device(dev):
-        _check(lib.psa_build_tile_map_tokens(T, _ptr(group), _ptr(suffix), _ptr(is_prefix),
-                                             block_m, block_n, _stream(dev), ctypes.byref(out)))
+        _check(lib.psa_build_tile_map_tokens_ex(T, _ptr(group), _ptr(suffix), _ptr(is_prefix),
+                                                block_m, block_n, _form_flags(form),
+                                                _stream(dev), ctypes.byref(out)))
     return TileMap(out.value, dev)
+
+
+def _form_flags(form: str) -> int:
+    if form not in ("auto", "nodes"):
+        raise ValueError('form must be "auto" or "nodes"')
+    return MAP_NODE_FORM if form == "nodes" else 0
 
 
 def build_tile_map_tree(node_lengths: Sequence[int], sample_paths: Sequence[Sequence[int]],
                         T: Optional[int] = None, device=None, block_m: Optional[int] = None,
                         block_n: Optional[int] = None, dtype: torch.dtype = torch.bfloat16,
-                        d: int = 128) -> TileMap:
-    """Tile map from a prefix tree given on the host."""
+                        d: int = 128, form: str = "auto") -> TileMap:
+    """Tile map from a prefix tree given on the host (form as build_tile_map_tokens:
+    "auto" takes the interval form for depth-first node orders)."""
     lib = load()
     if block_m is None or block_n is None:
         block_m, block_n = tile_shape(PASS_FWD, dtype, d)
@@ -220,9 +254,10 @@ def build_tile_map_tree(node_lengths: Sequence[int], sample_paths: Sequence[Sequ
         return ctypes.c_void_p(a.ctypes.data if a.size else 0)
 
     with torch.cuda.device(dev):
-        _check(lib.psa_build_tile_map_tree(len(nl), addr(nl), len(sample_paths), addr(ptr),
-                                           addr(nodes), int(T), block_m, block_n, _stream(dev),
-                                           ctypes.byref(out)))
+        _check(lib.psa_build_tile_map_tree_ex(len(nl), addr(nl), len(sample_paths), addr(ptr),
+                                              addr(nodes), int(T), block_m, block_n,
+                                              _form_flags(form), _stream(dev),
+                                              ctypes.byref(out)))
     return TileMap(out.value, dev)
 
 
@@ -323,15 +358,16 @@ class PrefixAttention(torch.autograd.Function):
 
 
 def layout_tile_map(layout, device, dtype: torch.dtype = torch.bfloat16, d: int = 128,
-                    block_m: Optional[int] = None, block_n: Optional[int] = None) -> TileMap:
+                    block_m: Optional[int] = None, block_n: Optional[int] = None,
+                    form: str = "auto") -> TileMap:
     """Tile map of a workloads.Layout (token labels are copied to the device)."""
     if layout.kind == "tokens":
         g = torch.as_tensor(layout.group, dtype=torch.int32).to(device)
         s = torch.as_tensor(layout.suffix, dtype=torch.int32).to(device)
         p = torch.as_tensor(layout.is_prefix, dtype=torch.uint8).to(device)
-        return build_tile_map_tokens(g, s, p, block_m, block_n, dtype, d)
+        return build_tile_map_tokens(g, s, p, block_m, block_n, dtype, d, form)
     return build_tile_map_tree(layout.node_lengths, layout.sample_paths, layout.T, device,
-                               block_m, block_n, dtype, d)
+                               block_m, block_n, dtype, d, form)
 
 
 # ----------------------------------------------------------------------------

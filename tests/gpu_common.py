@@ -50,7 +50,11 @@ def compare(name, got, want, dtype, mask=None, out_round=0.0):
         diff = np.maximum(diff - out_round * (np.abs(w[fin_w]) + TOL[dtype]["max_abs"]), 0.0)
     max_abs = float(diff.max())
     tol = TOL[dtype]
-    assert max_abs <= tol["max_abs"], f"{name}: max-abs {max_abs:.3e} > {tol['max_abs']}"
+    if max_abs > tol["max_abs"]:
+        at = int(np.argmax(diff))
+        where = np.unravel_index(np.flatnonzero(fin_w)[at], w.shape) if mask is None else at
+        raise AssertionError(f"{name}: max-abs {max_abs:.3e} > {tol['max_abs']} at {where}: "
+                             f"got {g[fin_w][at]:.9g}, want {w[fin_w][at]:.9g}")
     if tol["mean_rel"] is not None:
         assert mean_rel <= tol["mean_rel"], f"{name}: mean-rel {mean_rel:.3e} > {tol['mean_rel']}"
     return max_abs, mean_rel

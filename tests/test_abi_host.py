@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.psa_abi_version() == 2
+    assert lib.psa_abi_version() == 3
     for code, name in psa.STATUS.items():
         s = lib.psa_status_string(code).decode()
         assert s and s != "unknown status", name
@@ -78,14 +78,30 @@ def _tree(lib, nl, paths, T=None, bm=128, bn=128):
     ([4, 4, 4], [[0, 1]], "lies on no path"),
     ([4, 4], [[0, 5]], "out of range"),
     ([4, -1], [[0, 1]], "negative node length"),
-    ([4, 4, 4, 4], [[0, 2], [0, 1, 3]], "pre-order"),  # 3 is a child of 1 but follows 2
-    ([4, 4], [[1, 0]], "pre-order"),  # a child before its parent
+    ([4, 4], [[1, 0]], "comes before its parent"),
+    ([4, 4, 4], [[0, 2, 1]], "comes before its parent"),  # 1's parent is 2
     ([4], [[]], "empty"),
 ])
 def test_tree_layout_rejected_on_host(lib, nl, paths, why):
     st, msg = _tree(lib, nl, paths)
     assert st == 3, (st, msg)
     assert why in msg
+
+
+def test_builder_flags_rejected(lib):
+    """Only PSA_MAP_NODE_FORM is a known build flag (checked before any device work)."""
+    import numpy as np
+    out = ctypes.c_void_p()
+    assert lib.psa_build_tile_map_tokens_ex(16, None, None, None, 128, 128, 2, None,
+                                            ctypes.byref(out)) == 10
+    nl = np.asarray([4], np.int32)
+    ptr = np.asarray([0, 1], np.int32)
+    nodes = np.asarray([0], np.int32)
+    assert lib.psa_build_tile_map_tree_ex(1, ctypes.c_void_p(nl.ctypes.data), 1,
+                                          ctypes.c_void_p(ptr.ctypes.data),
+                                          ctypes.c_void_p(nodes.ctypes.data), 4, 128, 128, 4,
+                                          None, ctypes.byref(out)) == 10
+    assert b"flag" in lib.psa_last_error()
 
 
 def test_tree_shape_errors(lib):
@@ -115,6 +131,7 @@ def test_attention_argument_errors(lib):
     assert lib.psa_bwd(None, 1, 0, 16, 2, 2, 128, 0.0, *([None] * 9), None, 0, None) == 1
     assert lib.psa_tile_map_info_get(None, None) == 1
     assert lib.psa_tile_map_export(None, *([None] * 8)) == 1
+    assert lib.psa_tile_map_export_nodes(None, None, None, None) == 1
     lib.psa_tile_map_destroy(None)  # no-op
 
 

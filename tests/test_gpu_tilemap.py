@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from oracle import tilemap as ot
-from oracle.mask import dense_mask, meta_from_layout
+from oracle.mask import TokenMeta, dense_mask, meta_from_layout
 from shared_prefix_block_amd import psa
 from shared_prefix_block_amd import workloads as wl
 from tests.gpu_common import need_gpu, say
@@ -114,28 +114,31 @@ def _labels(group, suffix, is_prefix):
             torch.tensor(is_prefix, dtype=torch.uint8, device=dev))
 
 
-@pytest.mark.parametrize("group,suffix,is_prefix,pos,why", [
-    ([1, 1, 0, 0], [-1, -1, -1, -1], [1, 1, 1, 1], 2, "group ids decrease"),
-    ([0, 0, -1, 0], [-1, 3, -1, 3], [1, 0, 0, 0], 3, "split by pad"),
-    ([0, 0, 0, 0], [-1, 4, -1, 4], [1, 0, 1, 0], 2, "prompt token follows"),
-    ([0, 0, 0, 0, 0], [-1, 2, 1, 2, 2], [1, 0, 0, 0, 0], 2, "completion ids decrease"),
-    ([0, 0, 0, 0, 0], [-1, 2, 3, 2, 2], [1, 0, 0, 0, 0], 3, "completion ids decrease"),
+@pytest.mark.parametrize("group,suffix,is_prefix", [
+    ([1, 1, 0, 0], [-1, -1, -1, -1], [1, 1, 1, 1]),            # group ids decrease
+    ([0, 0, -1, 0], [-1, 3, -1, 3], [1, 0, 0, 0]),             # a group split by a pad
+    ([0, 0, 0, 0], [-1, 4, -1, 4], [1, 0, 1, 0]),              # prompt after completion
+    ([0, 0, 0, 0, 0], [-1, 2, 1, 2, 2], [1, 0, 0, 0, 0]),      # completion ids decrease
+    ([0, 0, 0, 0, 0], [-1, 2, 3, 2, 2], [1, 0, 0, 0, 0]),      # a completion split
 ])
-def test_token_layout_rejected(group, suffix, is_prefix, pos, why):
+def test_unpacked_token_layouts_take_node_form(group, suffix, is_prefix):
+    """Labellings the interval form cannot hold get the node form, and the same mask
+    as the oracle's rule token by token."""
     g, s, p = _labels(group, suffix, is_prefix)
-    with pytest.raises(psa.PsaError) as ei:
-        psa.build_tile_map_tokens(g, s, p, 128, 128)
-    assert ei.value.name == "PSA_ERR_LAYOUT"
-    assert why in str(ei.value) and f"position {pos}" in str(ei.value)
+    m = psa.build_tile_map_tokens(g, s, p, 2, 3)
+    assert m.info["form"] == psa.FORM_NODES
+    meta = TokenMeta(group, suffix, is_prefix)
+    _assert_same_map(m.export(), ot.tile_map(meta, 2, 3), m.info)
 
 
-def test_long_token_layout_rejected_late():
-    """An error far into a long sequence (past several scan chunks) is still found."""
+def test_long_unpacked_layout_found_late():
+    """A break of the packed layout far into a long sequence (past several scan chunks)
+    is still found, and the node form takes over."""
     lay = wl.tokens_layout([(3000, [2000] * 4), (100, [50, 60])])
     s = lay.suffix.copy()
     s[-60:-30] = 10**6  # breaks the last completion into two runs with a smaller id after
     g, sf, p = _labels(lay.group, s, lay.is_prefix)
-    with pytest.raises(psa.PsaError) as ei:
-        psa.build_tile_map_tokens(g, sf, p, 128, 128)
-    assert ei.value.name == "PSA_ERR_LAYOUT"
-    assert f"position {lay.T - 30}" in str(ei.value)
+    m = psa.build_tile_map_tokens(g, sf, p, 128, 128)
+    assert m.info["form"] == psa.FORM_NODES
+    meta = TokenMeta(lay.group, s, lay.is_prefix)
+    _assert_same_map(m.export(), ot.tile_map(meta, 128, 128), m.info)
