@@ -8,5 +8,6 @@ It shares no code with the HIP library and never imports it.
 * ``oracle.attention`` - dense masked softmax attention and its analytic gradients
 * ``oracle.tilemap``   - full / partial / empty tile classification, CSR and CSC
 * ``oracle.fold``      - the rollout fold (flat ids, labels, positions, metadata) and unfold
+* ``oracle.draft``     - the packed-document draft mask of block-diffusion drafters
 """
-from . import attention, fold, mask, tilemap  # noqa: F401
+from . import attention, draft, fold, mask, tilemap  # noqa: F401
