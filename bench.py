@@ -45,6 +45,16 @@ def kernel_source_hash() -> str:
 
 def kept_pairs(lay) -> int:
     """Exact number of kept (q, kv) pairs of a packed layout (per q head)."""
+    if lay.kind == "draft":  # per kept block: its document's context before the anchor
+        import numpy as np  # and its own block (all of it, or causally)
+        x = lay.extra
+        bs, doc, total = x["block_size"], x["ctx_doc"], 0
+        pos = np.arange(len(doc))
+        for a, dd, kp in zip(x["anchors"], x["anchor_doc"], x["keep"]):
+            if kp:
+                total += bs * int(((pos < a) & (doc == dd)).sum())
+                total += bs * (bs + 1) // 2 if x["causal"] else bs * bs
+        return total
     if lay.kind == "tokens":
         return sum(p * (p + 1) // 2 + sum(r * p + r * (r + 1) // 2 for r in rs)
                    for p, rs in lay.specs)
@@ -58,6 +68,13 @@ def kept_pairs(lay) -> int:
 
 
 def describe(cfg, lay, layout_mode="packed", form="auto") -> str:
+    if lay.kind == "draft":
+        x = lay.extra
+        n_docs = len(set(int(d) for d in x["ctx_doc"]))
+        return (f"draft blocks over packed documents fwd+bwd: {n_docs} documents, context "
+                f"{x['ctx_len']}, {len(x['anchors'])} blocks of {x['block_size']} "
+                f"({'causal' if x['causal'] else 'bidirectional'}), T={lay.T}, "
+                f"hq={cfg.hq}/hkv={cfg.hkv}, d={cfg.d}, {cfg.dtype}")
     if lay.kind == "tokens":
         ps = sorted({p for p, _ in lay.specs})
         layout = (f"{len(lay.specs)} groups, P={ps[0]}" if len(ps) == 1
@@ -298,7 +315,7 @@ def main():
             sys.exit("--layout bfs needs a tree workload")
         nl, paths = wl.reorder_tree(lay.node_lengths, lay.sample_paths)
         lay = wl.tree_layout(nl, paths, extra_pad=lay.T - lay.T_real)
-    if args.layout != "packed":
+    if args.layout != "packed" or lay.kind == "draft":
         args.no_cpu_baseline = True  # the oracle's sample slices packed groups
     if args.fold:
         if lay.kind != "tokens":
@@ -321,6 +338,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def build_map():
+        if lay.kind == "draft":
+            return psa.layout_tile_map(lay, dev, block_m=TILE, block_n=TILE)
         if lay.kind == "tokens":
             return psa.build_tile_map_tokens(*labels, TILE, TILE, form=args.form)
         return psa.build_tile_map_tree(lay.node_lengths, lay.sample_paths, lay.T, dev, TILE, TILE,

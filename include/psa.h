@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PSA_ABI_VERSION 3
+#define PSA_ABI_VERSION 4
 
 typedef enum {
   PSA_OK = 0,
@@ -74,6 +74,7 @@ typedef struct {
   int64_t n_full;      /* tiles whose every pair is kept                          */
   int64_t n_partial;   /* non-empty tiles that are not full                       */
   int32_t form;        /* PSA_FORM_INTERVAL or PSA_FORM_NODES (mask encoding)     */
+  int32_t causal;      /* 1: kv <= q is part of the mask; 0: a bidirectional draft map */
 } psa_tile_map_info;
 
 /* Mask encodings a map can carry (psa_tile_map_info.form). */
@@ -82,6 +83,8 @@ typedef struct {
 
 /* Build flags (the _ex builders). */
 #define PSA_MAP_NODE_FORM 1 /* build the node form even where the interval form exists */
+/* Flag of psa_build_tile_map_draft. */
+#define PSA_DRAFT_CAUSAL 1 /* draft blocks attend causally within the block */
 
 /* Library ABI version (PSA_ABI_VERSION of the build). */
 int32_t psa_abi_version(void);
@@ -157,6 +160,34 @@ psa_status psa_build_tile_map_tree_ex(int64_t n_nodes, const int32_t* node_lengt
                                       int32_t block_n, int32_t flags, void* stream,
                                       psa_tile_map** out);
 
+/*
+ * Build a tile map for the packed-document draft mask of block-diffusion drafters
+ * (Automodel PR #3023, PR description and the review comment listing the mask
+ * builder's arguments; Model-Optimizer PR #2757, the commit note on the generation
+ * mask).  The flat layout is the context, positions [0, ctx_len), then n_blocks
+ * blocks of block_size draft tokens (block b's token j at ctx_len + b * block_size
+ * + j), then pads up to T.  The queries that matter are the draft tokens: a draft
+ * token of block b sees the context positions c < anchors[b] whose ctx_doc[c] equals
+ * anchor_doc[b], and its own block's tokens (all of them; with PSA_DRAFT_CAUSAL only
+ * those at or before itself).  A block with keep[b] == 0 sees nothing and is seen by
+ * nothing; context rows and pads see nothing (O = 0, LSE = -inf).  The caller passes
+ * Q, K, V for all T positions (context query rows are ignored).
+ * Device pointers: anchors[n_blocks] int32 in [0, ctx_len] (else PSA_ERR_LAYOUT),
+ * keep[n_blocks] uint8 (NULL: every block kept), ctx_doc[ctx_len] and
+ * anchor_doc[n_blocks] int32 document ids (both NULL: one document; ignored when
+ * there is no context or no block).  Needs
+ * T >= ctx_len + n_blocks * block_size and (ctx_len + 1) * n_blocks <= 2^32.
+ * The map takes the node form with causal = 0 unless PSA_DRAFT_CAUSAL is set.
+ * Same stream and ownership rules as psa_build_tile_map_tokens.
+ * Errors: PSA_ERR_NULL, PSA_ERR_SHAPE, PSA_ERR_LAYOUT, PSA_ERR_VALUE, PSA_ERR_HIP,
+ * PSA_ERR_ALLOC.
+ */
+psa_status psa_build_tile_map_draft(int64_t ctx_len, int32_t block_size, int64_t n_blocks,
+                                    const int32_t* anchors, const uint8_t* keep,
+                                    const int32_t* ctx_doc, const int32_t* anchor_doc,
+                                    int32_t flags, int64_t T, int32_t block_m, int32_t block_n,
+                                    void* stream, psa_tile_map** out);
+
 /* Sizes of a built map.  Errors: PSA_ERR_NULL. */
 psa_status psa_tile_map_info_get(const psa_tile_map* map, psa_tile_map_info* out);
 
@@ -175,7 +206,8 @@ psa_status psa_tile_map_export(const psa_tile_map* map, int32_t* end, uint8_t* k
 
 /*
  * Copy the mask encoding as nodes to host buffers of T int32 each (NULL skipped):
- * kv is visible to q iff kv <= q and lo[kv] <= key[q] < lo[kv] + w[kv].  For a
+ * kv is visible to q iff kv <= q (only when the map is causal) and
+ * lo[kv] <= key[q] < lo[kv] + w[kv].  For a
  * node-form map these are its arrays (key: the token's node number from 1, 0 on a
  * pad; [lo, lo + w): the numbers of the node's subtree, w = 0 on a pad); an
  * interval-form map is written as key = lo = t, w = end[t] - t.  Waits for the

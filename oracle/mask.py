@@ -157,8 +157,13 @@ class TreeMeta:
         return out
 
 
-def meta_from_layout(layout) -> "TokenMeta | TreeMeta":
+def meta_from_layout(layout):
     """Build the oracle's metadata object from a workloads.Layout (plain arrays only)."""
+    if layout.kind == "draft":
+        from .draft import DraftMeta
+        x = layout.extra
+        return DraftMeta(x["ctx_len"], x["block_size"], x["anchors"], x["keep"], x["ctx_doc"],
+                         x["anchor_doc"], x["causal"], layout.T)
     if layout.kind == "tokens":
         return TokenMeta(layout.group, layout.suffix, layout.is_prefix)
     return TreeMeta(layout.node_lengths, layout.sample_paths, layout.T)

@@ -210,7 +210,8 @@ psa_status classify_and_wait(psa_tile_map* m, const Phase1& ph, int64_t* info_h)
   hipError_t e;
   if (m->form == kFormNodes)
     e = launch_classify_nodes(m->T, m->bm, m->bn, m->nq, m->nk, m->nkey, m->nlo, m->nw,
-                              m->kinds, m->row_ptr, m->col_ptr, ph.scratch, ph.info, m->stream);
+                              m->causal, m->kinds, m->row_ptr, m->col_ptr, ph.scratch, ph.info,
+                              m->stream);
   else
     e = launch_classify(m->T, m->bm, m->bn, m->nq, m->nk, m->end, m->kinds, m->row_ptr,
                         m->col_ptr, ph.scratch, ph.scratch + stride, ph.info, m->stream);
@@ -612,6 +613,75 @@ psa_status psa_build_tile_map_tree_ex(int64_t n_nodes, const int32_t* node_lengt
   return st;
 }
 
+psa_status psa_build_tile_map_draft(int64_t ctx_len, int32_t block_size, int64_t n_blocks,
+                                    const int32_t* anchors, const uint8_t* keep,
+                                    const int32_t* ctx_doc, const int32_t* anchor_doc,
+                                    int32_t flags, int64_t T, int32_t block_m, int32_t block_n,
+                                    void* stream, psa_tile_map** out) {
+  if (!out) return psa_set_error(PSA_ERR_NULL, "out is NULL");
+  psa_status st = check_tiles(T, block_m, block_n);
+  if (st != PSA_OK) return st;
+  if ((flags & ~PSA_DRAFT_CAUSAL) != 0) return psa_set_error(PSA_ERR_VALUE, "unknown flag bit");
+  if (ctx_len < 0 || n_blocks < 0 || block_size < 1)
+    return psa_set_error(PSA_ERR_SHAPE, "need ctx_len >= 0, n_blocks >= 0, block_size >= 1");
+  if (n_blocks > (int64_t{1} << 31) || ctx_len + n_blocks * int64_t(block_size) > T)
+    return psa_set_error(PSA_ERR_SHAPE, "T is shorter than ctx_len + n_blocks * block_size");
+  if ((ctx_len + 1) * n_blocks > (int64_t{1} << 32))
+    return psa_set_error(PSA_ERR_SHAPE, "(ctx_len + 1) * n_blocks must not exceed 2^32");
+  if (n_blocks > 0 && !anchors) return psa_set_error(PSA_ERR_NULL, "anchors is NULL");
+  if (ctx_len > 0 && n_blocks > 0 && (ctx_doc == nullptr) != (anchor_doc == nullptr))
+    return psa_set_error(PSA_ERR_NULL, "ctx_doc and anchor_doc are given together or not at all");
+  if (ctx_len == 0 || n_blocks == 0) ctx_doc = anchor_doc = nullptr;  // nothing to compare
+  psa_tile_map* m = new (std::nothrow) psa_tile_map();
+  if (!m) return psa_set_error(PSA_ERR_ALLOC, "host allocation failed");
+  m->T = T;
+  m->bm = block_m;
+  m->bn = block_n;
+  m->nq = (T + block_m - 1) / block_m;
+  m->nk = (T + block_n - 1) / block_n;
+  m->causal = (flags & PSA_DRAFT_CAUSAL) ? 1 : 0;
+  m->stream = static_cast<hipStream_t>(stream);
+  hipError_t e = hipGetDevice(&m->device);
+  if (e != hipSuccess) {
+    free_map(m);
+    return psa_hip_error(e, "hipGetDevice");
+  }
+  Phase1 ph;
+  if ((st = alloc_phase1(m, &ph)) != PSA_OK || (st = alloc_nodes(m)) != PSA_OK) {
+    free_map(m);
+    return st;
+  }
+  void* scr = nullptr;
+  size_t scr_bytes = 0;
+  hipEvent_t scr_ev = nullptr;
+  if (map_alloc(m, &scr, draft_scratch_bytes(n_blocks), &scr_bytes, &scr_ev) != hipSuccess) {
+    (void)hipGetLastError();
+    free_map(m);
+    return psa_set_error(PSA_ERR_ALLOC, "device allocation of the block sort scratch failed");
+  }
+  e = launch_draft_nodes(T, ctx_len, block_size, n_blocks, anchors, keep, ctx_doc, anchor_doc,
+                         m->nkey, m->nlo, m->nw, scr, scr_bytes, ph.info, m->stream);
+  map_release(m, scr, scr_bytes, scr_ev);  // reusable once the launches are done
+  if (e != hipSuccess) {
+    free_map(m);
+    return psa_hip_error(e, "draft numbering launch");
+  }
+  int64_t info_h[8];
+  if ((st = classify_and_wait(m, ph, info_h)) != PSA_OK) {
+    free_map(m);
+    return st;
+  }
+  if (info_h[3] != -1) {
+    free_map(m);
+    return psa_set_error(PSA_ERR_LAYOUT, "anchor of block " +
+                                             std::to_string(uint64_t(info_h[3]) >> 3) +
+                                             " lies outside [0, ctx_len]");
+  }
+  st = finish_lists(m, info_h, out);
+  if (st != PSA_OK) free_map(m);
+  return st;
+}
+
 psa_status psa_tile_map_info_get(const psa_tile_map* map, psa_tile_map_info* out) {
   if (!map || !out) return psa_set_error(PSA_ERR_NULL, "map or out is NULL");
   out->T = map->T;
@@ -623,6 +693,7 @@ psa_status psa_tile_map_info_get(const psa_tile_map* map, psa_tile_map_info* out
   out->n_full = map->n_full;
   out->n_partial = map->n_partial;
   out->form = map->form;
+  out->causal = map->causal;
   return PSA_OK;
 }
 

@@ -44,6 +44,7 @@ struct BwdParams {
   const int32_t* nkey;  // node form
   const int32_t* nlo;
   const int32_t* nw;
+  int32_t causal;  // node form: 0 drops the kv <= q conjunct
   const int32_t* row_ptr;
   const int32_t* col;
   const uint8_t* kind;
@@ -454,6 +455,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
           for (int u = 0; u < 4; ++u)
             pv[4 * g + u] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + u], c, -l2v[g][u]));
         if (NODES && partial) {  // uniform branch; node form
+          const bool nc = p.causal == 0;
           int4 qkv[4];  // the rows' node numbers
 #pragma unroll
           for (int g = 0; g < 4; ++g)
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int ii = 4 * g + u;
-              const bool keep = (qd0 + 32 * qb + acc_row(ii, half) >= 0) &
+              const bool keep = ((qd0 + 32 * qb + acc_row(ii, half) >= 0) | nc) &
                                 (uint32_t(kq[u] - klo) < uint32_t(kw));
               pv[ii] = keep ? pv[ii] : 0.f;
             }
@@ -844,6 +846,7 @@ void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) pv[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[ii], c, -l2));
         if (NODES && partial) {  // uniform branch; node form
+          const bool nc = p.causal == 0;
           int4 los[4], ws[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -857,7 +860,8 @@ void dq_kernel(BwdParams p) {
             const int wv[4] = {ws[g].x, ws[g].y, ws[g].z, ws[g].w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const bool keep = (kvl + u <= qd) & (uint32_t(qkey - lv[u]) < uint32_t(wv[u]));
+              const bool keep =
+                  ((kvl + u <= qd) | nc) & (uint32_t(qkey - lv[u]) < uint32_t(wv[u]));
               pv[4 * g + u] = keep ? pv[4 * g + u] : 0.f;
             }
           }
@@ -991,6 +995,7 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.nkey = map.nkey;
   p.nlo = map.nlo;
   p.nw = map.nw;
+  p.causal = map.causal;
   p.row_ptr = map.row_ptr;
   p.col = map.col;
   p.kind = map.kind;

@@ -45,6 +45,7 @@ struct FwdParams {
   const int32_t* nkey;  // node form
   const int32_t* nlo;
   const int32_t* nw;
+  int32_t causal;  // node form: 0 drops the kv <= q conjunct
   const int32_t* row_ptr;
   const int32_t* col;
   const uint8_t* kind;
@@ -288,6 +289,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       }
       if (NODES && partial) {  // uniform branch; node form
         const int qd = qrow_i - kv0i;
+        const bool nc = p.causal == 0;
 #pragma unroll
         for (int kb = 0; kb < C::BN / 32; ++kb) {
           int4 los[4], ws[4];  // this lane's keys' lo and w, read together
@@ -303,7 +305,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
             const int wv[4] = {ws[g].x, ws[g].y, ws[g].z, ws[g].w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const bool keep = (kvl + u <= qd) & (uint32_t(qkey - lv[u]) < uint32_t(wv[u]));
+              const bool keep =
+                  ((kvl + u <= qd) | nc) & (uint32_t(qkey - lv[u]) < uint32_t(wv[u]));
               sv[kb][4 * g + u] = keep ? sv[kb][4 * g + u] : -INFINITY;
             }
           }
@@ -422,6 +425,7 @@ hipError_t launch_fwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.nkey = map.nkey;
   p.nlo = map.nlo;
   p.nw = map.nw;
+  p.causal = map.causal;
   p.row_ptr = map.row_ptr;
   p.col = map.col;
   p.kind = map.kind;

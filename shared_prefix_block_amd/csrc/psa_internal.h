@@ -19,6 +19,8 @@
 //    key[t] is the pre-order number (from 1) of t's node in the prefix forest and
 //    [lo, lo + w) the pre-order numbers of the node's subtree; pads have key 0 and
 //    w 0, so they see nothing and are seen by nothing.
+// A map that is not causal (draft blocks attending both ways) drops kv <= q: the
+// ranges alone decide, and they already keep context keys before their queries.
 constexpr int32_t kFormInterval = 0, kFormNodes = 1;
 struct psa_tile_map {
   int64_t T = 0;
@@ -26,6 +28,7 @@ struct psa_tile_map {
   int64_t nq = 0, nk = 0;
   int64_t nnz = 0, n_full = 0, n_partial = 0;
   int32_t form = kFormInterval;
+  int32_t causal = 1;  // 0: node form without the kv <= q conjunct
   int device = 0;
   hipStream_t stream = nullptr;  // build stream (export waits on it; buffers freed on it)
   size_t buf1_bytes = 0, buf2_bytes = 0, buf3_bytes = 0;  // sizes of the device buffers
@@ -91,11 +94,24 @@ hipError_t launch_classify(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_
                            const int32_t* end, uint8_t* kinds, int32_t* row_ptr,
                            int32_t* col_ptr, int32_t* ktile_min_end, int32_t* ktile_max_end,
                            int64_t* info, hipStream_t stream);
-// The same from the node form.  ksum: 4 * align64(nk) ints of scratch.
+// Node form of a packed-document draft layout (context [0, S), then n_blocks blocks
+// of bs draft tokens): a block's number orders it by (document, anchor, index); a
+// context key's range holds the kept blocks of its document anchored after it; a
+// draft key's range is its own block.  anchors out of [0, S] set info[3] to
+// block * 8 + 5.  scratch: draft_scratch_bytes(n_blocks) bytes.
+size_t draft_scratch_bytes(int64_t n_blocks);
+hipError_t launch_draft_nodes(int64_t T, int64_t S, int32_t bs, int64_t n_blocks,
+                              const int32_t* anchors, const uint8_t* keep,
+                              const int32_t* ctx_doc, const int32_t* anchor_doc, int32_t* key,
+                              int32_t* lo, int32_t* w, void* scratch, size_t scratch_bytes,
+                              int64_t* info, hipStream_t stream);
+// The same from the node form.  ksum: 4 * align64(nk) ints of scratch.  causal = 0
+// drops the kv <= q conjunct.
 hipError_t launch_classify_nodes(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk,
                                  const int32_t* key, const int32_t* lo, const int32_t* w,
-                                 uint8_t* kinds, int32_t* row_ptr, int32_t* col_ptr,
-                                 int32_t* ksum, int64_t* info, hipStream_t stream);
+                                 int32_t causal, uint8_t* kinds, int32_t* row_ptr,
+                                 int32_t* col_ptr, int32_t* ksum, int64_t* info,
+                                 hipStream_t stream);
 // CSR and CSC lists (ordered compaction of kinds) and the two length orders.
 hipError_t launch_fill_lists(int64_t nq, int64_t nk, const uint8_t* kinds,
                              const int32_t* row_ptr, const int32_t* col_ptr, int32_t* col,

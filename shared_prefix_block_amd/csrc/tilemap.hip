@@ -413,6 +413,74 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_rows(
   }
 }
 
+// Step 1e: draft layout -> node form.  Block b's sort key is
+// order(anchor document) * 2^32 + a_b * n_blocks + b (the host checks that the low
+// word fits), or all ones for a block not kept; its number is its rank, from 1.
+__device__ inline uint64_t doc_order(int32_t d) { return uint64_t(uint32_t(d) ^ 0x80000000u); }
+
+__global__ void k_draft_composite(int64_t S, int64_t n, const int32_t* __restrict__ anchors,
+                                  const uint8_t* __restrict__ keep,
+                                  const int32_t* __restrict__ anchor_doc,
+                                  uint64_t* __restrict__ comp, int32_t* __restrict__ idx,
+                                  unsigned long long* err) {
+  for (int64_t b = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; b < n;
+       b += int64_t(gridDim.x) * blockDim.x) {
+    const int32_t a = anchors[b];
+    idx[b] = int32_t(b);
+    if (a < 0 || a > S) {
+      atomicMin(err, (unsigned long long)b * 8 + 5);
+      comp[b] = kPadComposite;
+      continue;
+    }
+    const bool live = keep ? keep[b] != 0 : true;
+    const uint64_t d = anchor_doc ? doc_order(anchor_doc[b]) : doc_order(0);
+    comp[b] = live ? (d << 32) | (uint64_t(a) * uint64_t(n) + uint64_t(b)) : kPadComposite;
+  }
+}
+
+__global__ void k_draft_rank(int64_t n, const uint64_t* __restrict__ sorted,
+                             const int32_t* __restrict__ order, int32_t* __restrict__ rank) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    rank[order[i]] = sorted[i] == kPadComposite ? 0 : int32_t(i + 1);
+}
+
+// first index in sorted[0, n) whose value is >= x
+__device__ inline int64_t lower_index(const uint64_t* __restrict__ v, int64_t n, uint64_t x) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (v[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void k_draft_tokens(int64_t T, int64_t S, int32_t bs, int64_t n,
+                               const int32_t* __restrict__ ctx_doc,
+                               const uint64_t* __restrict__ sorted,
+                               const int32_t* __restrict__ rank, int32_t* __restrict__ key,
+                               int32_t* __restrict__ lo, int32_t* __restrict__ w) {
+  for (int64_t t = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; t < T;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    int32_t k = 0, a = 0, width = 0;
+    if (t < S) {  // a context key: the kept blocks of its document anchored after it
+      const uint64_t d = (ctx_doc ? doc_order(ctx_doc[t]) : doc_order(0)) << 32;
+      const int64_t first = lower_index(sorted, n, d | (uint64_t(t + 1) * uint64_t(n)));
+      const int64_t past = upper_index(sorted, n, d | 0xffffffffull);
+      a = int32_t(first + 1);
+      width = int32_t(past - first);
+    } else if (t < S + int64_t(bs) * n) {  // a draft token: its own block
+      k = rank[(t - S) / bs];
+      a = k;
+      width = k > 0 ? 1 : 0;
+    }
+    key[t] = k;
+    lo[t] = a;
+    w[t] = width;
+  }
+}
+
 // Node form.  One wave per kv-tile: over its keys with w > 0, the smallest lo and the
 // largest lo + w (INT_MAX / 0 if none); and, for the full test, the largest lo and
 // the smallest lo + w over all its columns, or INT_MAX / 0 if a column is a pad or
@@ -456,13 +524,13 @@ __global__ __launch_bounds__(64) void k_ktile_summary_nodes(int64_t T, int32_t b
 }
 
 // One block per q-tile, its keys in LDS; each wave takes every fourth kv-tile.  A
-// tile is empty when it lies wholly after the q-tile (kv > q everywhere) or when the
-// keys' subtree ranges miss the q-tile's key range; full when it lies wholly at or
-// before the q-tile and every range holds every key; otherwise the wave searches it
-// exactly, one column per lane, for a kept pair.
+// tile is empty when it lies wholly after the q-tile (kv > q everywhere; causal maps
+// only) or when the keys' subtree ranges miss the q-tile's key range; full when it
+// lies wholly at or before the q-tile (causal maps) and every range holds every key;
+// otherwise the wave searches it exactly, one column per lane, for a kept pair.
 __global__ __launch_bounds__(kClassifyThreads) void k_classify_nodes_rows(
     int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk, const int32_t* __restrict__ key,
-    const int32_t* __restrict__ lo, const int32_t* __restrict__ w,
+    const int32_t* __restrict__ lo, const int32_t* __restrict__ w, int32_t causal,
     const int32_t* __restrict__ ksum, int64_t stride, uint8_t* kinds, int32_t* row_ptr,
     int32_t* col_ptr, int64_t* info) {
   __shared__ int32_t qk[1024];
@@ -510,8 +578,8 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_nodes_rows(
     const int64_t k_last = (k0 + bn < T ? k0 + bn : T) - 1;
     const int mn = ksum[j], mx = ksum[stride + j];
     uint8_t kind = 0;
-    if (k0 <= q_last && kmax > 0 && mn != INT_MAX && mx > kmin && mn <= kmax) {
-      if (all_real && k0 + bn <= T && k_last <= q0 && ksum[2 * stride + j] <= kmin &&
+    if ((k0 <= q_last || !causal) && kmax > 0 && mn != INT_MAX && mx > kmin && mn <= kmax) {
+      if (all_real && k0 + bn <= T && (k_last <= q0 || !causal) && ksum[2 * stride + j] <= kmin &&
           kmax < ksum[3 * stride + j]) {
         kind = 2;
       } else {
@@ -519,7 +587,7 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_nodes_rows(
         for (int64_t kv = k0 + lane; kv <= k_last && !found; kv += 64) {
           const int a = lo[kv], n = w[kv];
           if (n <= 0) continue;
-          for (int64_t r = (kv > q0 ? kv : q0) - q0; r < nrow; ++r) {
+          for (int64_t r = causal && kv > q0 ? kv - q0 : 0; r < nrow; ++r) {
             if (uint32_t(qk[r] - a) < uint32_t(n)) {
               found = true;
               break;
@@ -760,10 +828,60 @@ hipError_t launch_tree_nodes(int64_t T, int64_t n_nodes, const int64_t* node_sta
   return hipGetLastError();
 }
 
+size_t draft_scratch_bytes(int64_t n_blocks) {
+  const size_t n = size_t(n_blocks > 0 ? n_blocks : 1);
+  size_t sort_b = 0;
+  uint64_t* none = nullptr;
+  int32_t* ni = nullptr;
+  (void)hipcub::DeviceRadixSort::SortPairs(nullptr, sort_b, none, none, ni, ni, int64_t(n), 0,
+                                           64);
+  const size_t a8 = (n * 8 + 255) / 256 * 256, a4 = (n * 4 + 255) / 256 * 256;
+  return 2 * a8 + 3 * a4 + sort_b;
+}
+
+hipError_t launch_draft_nodes(int64_t T, int64_t S, int32_t bs, int64_t n_blocks,
+                              const int32_t* anchors, const uint8_t* keep,
+                              const int32_t* ctx_doc, const int32_t* anchor_doc, int32_t* key,
+                              int32_t* lo, int32_t* w, void* scratch, size_t scratch_bytes,
+                              int64_t* info, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const size_t n = size_t(n_blocks > 0 ? n_blocks : 1);
+  const size_t a8 = (n * 8 + 255) / 256 * 256, a4 = (n * 4 + 255) / 256 * 256;
+  if (scratch_bytes < 2 * a8 + 3 * a4) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(scratch);
+  uint64_t* comp = reinterpret_cast<uint64_t*>(base);
+  uint64_t* sorted = reinterpret_cast<uint64_t*>(base + a8);
+  int32_t* idx = reinterpret_cast<int32_t*>(base + 2 * a8);
+  int32_t* order = reinterpret_cast<int32_t*>(base + 2 * a8 + a4);
+  int32_t* rank = reinterpret_cast<int32_t*>(base + 2 * a8 + 2 * a4);
+  void* tmp = base + 2 * a8 + 3 * a4;
+  size_t tmp_bytes = scratch_bytes - (2 * a8 + 3 * a4);
+  hipError_t e = hipSuccess;
+  if (n_blocks > 0) {
+    const int64_t blocks = (n_blocks + 255) / 256 < 4096 ? (n_blocks + 255) / 256 : 4096;
+    unsigned long long* err = reinterpret_cast<unsigned long long*>(info + 3);
+    hipLaunchKernelGGL(k_draft_composite, dim3(unsigned(blocks)), dim3(256), 0, stream, S,
+                       n_blocks, anchors, keep, anchor_doc, comp, idx, err);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = hipcub::DeviceRadixSort::SortPairs(tmp, tmp_bytes, comp, sorted, idx, order, n_blocks,
+                                           0, 64, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_draft_rank, dim3(unsigned(blocks)), dim3(256), 0, stream, n_blocks,
+                       sorted, order, rank);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  int64_t tb = (T + 255) / 256;
+  if (tb > 4096) tb = 4096;
+  hipLaunchKernelGGL(k_draft_tokens, dim3(unsigned(tb)), dim3(256), 0, stream, T, S, bs,
+                     n_blocks, ctx_doc, sorted, rank, key, lo, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_classify_nodes(int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk,
                                  const int32_t* key, const int32_t* lo, const int32_t* w,
-                                 uint8_t* kinds, int32_t* row_ptr, int32_t* col_ptr,
-                                 int32_t* ksum, int64_t* info, hipStream_t stream) {
+                                 int32_t causal, uint8_t* kinds, int32_t* row_ptr,
+                                 int32_t* col_ptr, int32_t* ksum, int64_t* info,
+                                 hipStream_t stream) {
   const int64_t stride = (nk + 63) / 64 * 64;
   if (nk > 0) {
     hipLaunchKernelGGL(k_ktile_summary_nodes, dim3(unsigned(nk)), dim3(64), 0, stream, T, bn,
@@ -771,8 +889,8 @@ hipError_t launch_classify_nodes(int64_t T, int32_t bm, int32_t bn, int64_t nq, 
   }
   if (nq > 0) {
     hipLaunchKernelGGL(k_classify_nodes_rows, dim3(unsigned(nq)), dim3(kClassifyThreads), 0,
-                       stream, T, bm, bn, nq, nk, key, lo, w, ksum, stride, kinds, row_ptr,
-                       col_ptr, info);
+                       stream, T, bm, bn, nq, nk, key, lo, w, causal, ksum, stride, kinds,
+                       row_ptr, col_ptr, info);
   }
   hipLaunchKernelGGL(k_scan_ptrs, dim3(1), dim3(kScanThreads), 0, stream, nq, nk, row_ptr,
                      col_ptr, info);

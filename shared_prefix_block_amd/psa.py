@@ -33,9 +33,10 @@ EXPORTS = ["psa_abi_version", "psa_status_string", "psa_last_error", "psa_tile_s
            "psa_tile_map_export", "psa_tile_map_destroy", "psa_fwd", "psa_bwd_workspace_size",
            "psa_bwd", "psa_bwd_stages", "psa_fold_workspace_size", "psa_fold_rollouts",
            "psa_unfold_rows", "psa_build_tile_map_tokens_ex", "psa_build_tile_map_tree_ex",
-           "psa_tile_map_export_nodes"]
+           "psa_tile_map_export_nodes", "psa_build_tile_map_draft"]
 FORM_INTERVAL, FORM_NODES = 0, 1  # mask encodings of a map (info["form"])
 MAP_NODE_FORM = 1  # build flag: the node form even where the interval form exists
+DRAFT_CAUSAL = 1  # flag of psa_build_tile_map_draft: causal attention inside a block
 STAGE_PREPARE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 BWD_SPLIT_PDS = 16  # option bit of psa_bwd_stages: P and dS as hi + lo bf16 pairs
 
@@ -51,7 +52,8 @@ class TileMapInfo(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
                 ("n_qtiles", ctypes.c_int64), ("n_ktiles", ctypes.c_int64),
                 ("nnz", ctypes.c_int64), ("n_full", ctypes.c_int64),
-                ("n_partial", ctypes.c_int64), ("form", ctypes.c_int32)]
+                ("n_partial", ctypes.c_int64), ("form", ctypes.c_int32),
+                ("causal", ctypes.c_int32)]
 
 
 def lib_path() -> str:
@@ -83,6 +85,8 @@ def load() -> ctypes.CDLL:
             "psa_build_tile_map_tree_ex": (ctypes.c_int, [I64, P, I64, P, P, I64, I32, I32, I32,
                                                           P, PP]),
             "psa_tile_map_export_nodes": (ctypes.c_int, [P, P, P, P]),
+            "psa_build_tile_map_draft": (ctypes.c_int, [I64, I32, I64, P, P, P, P, I32, I64, I32,
+                                                        I32, P, PP]),
             "psa_tile_map_info_get": (ctypes.c_int, [P, ctypes.POINTER(TileMapInfo)]),
             "psa_tile_map_export": (ctypes.c_int, [P, P, P, P, P, P, P, P, P]),
             "psa_tile_map_destroy": (None, [P]),
@@ -261,6 +265,37 @@ def build_tile_map_tree(node_lengths: Sequence[int], sample_paths: Sequence[Sequ
     return TileMap(out.value, dev)
 
 
+def build_tile_map_draft(ctx_len: int, block_size: int, anchors: torch.Tensor,
+                         keep: Optional[torch.Tensor] = None,
+                         ctx_doc: Optional[torch.Tensor] = None,
+                         anchor_doc: Optional[torch.Tensor] = None, causal: bool = False,
+                         T: Optional[int] = None, block_m: Optional[int] = None,
+                         block_n: Optional[int] = None, dtype: torch.dtype = torch.bfloat16,
+                         d: int = 128) -> TileMap:
+    """Tile map of the packed-document draft mask (device tensors: anchors int32 [N],
+    keep uint8 [N] or None, ctx_doc int32 [ctx_len] and anchor_doc int32 [N], or both
+    None).  Positions: the context, then N blocks of block_size draft tokens, then pads
+    up to T."""
+    lib = load()
+    if block_m is None or block_n is None:
+        block_m, block_n = tile_shape(PASS_FWD, dtype, d)
+    for t, dt in ((anchors, torch.int32), (keep, torch.uint8), (ctx_doc, torch.int32),
+                  (anchor_doc, torch.int32)):
+        if t is not None and (t.dtype != dt or not t.is_cuda or not t.is_contiguous()):
+            raise TypeError("draft arrays must be contiguous device tensors (int32 / uint8)")
+    n = anchors.numel()
+    if T is None:
+        T = ctx_len + n * block_size
+    dev = anchors.device
+    out = ctypes.c_void_p()
+    with torch.cuda.device(dev):
+        _check(lib.psa_build_tile_map_draft(int(ctx_len), int(block_size), n, _ptr(anchors),
+                                            _ptr(keep), _ptr(ctx_doc), _ptr(anchor_doc),
+                                            DRAFT_CAUSAL if causal else 0, int(T), block_m,
+                                            block_n, _stream(dev), ctypes.byref(out)))
+    return TileMap(out.value, dev)
+
+
 def _check_qkv(q, k, v):
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [T, heads, d]")
@@ -361,6 +396,15 @@ def layout_tile_map(layout, device, dtype: torch.dtype = torch.bfloat16, d: int 
                     block_m: Optional[int] = None, block_n: Optional[int] = None,
                     form: str = "auto") -> TileMap:
     """Tile map of a workloads.Layout (token labels are copied to the device)."""
+    if layout.kind == "draft":
+        x = layout.extra
+        dv = lambda a, dt: torch.as_tensor(a, dtype=dt).to(device)  # noqa: E731
+        docs = x["ctx_len"] > 0  # an empty context has no documents to compare
+        return build_tile_map_draft(x["ctx_len"], x["block_size"], dv(x["anchors"], torch.int32),
+                                    dv(x["keep"], torch.uint8),
+                                    dv(x["ctx_doc"], torch.int32) if docs else None,
+                                    dv(x["anchor_doc"], torch.int32) if docs else None,
+                                    x["causal"], layout.T, block_m, block_n, dtype, d)
     if layout.kind == "tokens":
         g = torch.as_tensor(layout.group, dtype=torch.int32).to(device)
         s = torch.as_tensor(layout.suffix, dtype=torch.int32).to(device)

@@ -13,6 +13,10 @@ is ``group`` (int32, negative for a pad token), ``suffix`` (int32, -1 on prefix
 tokens, globally increasing over the suffixes) and ``is_prefix`` (uint8).  Pad
 tokens are appended at the end up to the requested multiple.
 
+Draft layouts (``draft_layout``) are the second mask workload: a block-diffusion
+drafter's context of packed documents followed by blocks of draft tokens anchored in
+it (Automodel PR #3023 page, PR description).
+
 Prefix trees follow the Automodel PR #2564 page ("Changelog": ``node_lengths`` and
 ``sample_paths`` carried on the batch): nodes are listed in depth-first pre-order,
 node ``n`` owns the n-th contiguous run of ``node_lengths`` tokens, and each sample
@@ -37,7 +41,7 @@ class Config:
 
     idx: int
     name: str
-    kind: str  # "tokens" or "tree"
+    kind: str  # "tokens", "tree" or "draft"
     hq: int
     hkv: int
     d: int
@@ -60,6 +64,10 @@ CONFIGS = {
               note="2 groups, P=16384, G=64 x R=512 (T=98304), 8/8 heads, N(0, 0.5)"),
     5: Config(5, "8trees_1024_4x256_4x384", "tree", 16, 8, 256, "bf16", 1.0, "fwd+bwd",
               note="8 trees: root 1024 -> 4 x 256 -> 4 x 384 leaves (T=65536), GQA 16/8, d=256"),
+    # the second mask workload: a block-diffusion drafter's packed-document batch
+    6: Config(6, "draft_4doc_4096_bs16", "draft", 16, 4, 128, "bf16", 1.0, "fwd+bwd",
+              note="draft blocks: 4 packed documents of 4096 context tokens, 512 blocks of "
+                   "16 per document (T=49152), bidirectional blocks, GQA 16/4, d=128"),
 }
 
 
@@ -152,6 +160,9 @@ class Layout:
 
 
 def layout_for(cfg: Config, seed: Optional[int] = None) -> Layout:
+    if cfg.kind == "draft":
+        rng = np.random.default_rng(cfg.idx if seed is None else seed)
+        return draft_layout([4096] * 4, 16, 512, rng)
     if cfg.kind == "tree":
         nl, sp = tree_spec()
         t = int(sum(nl))
@@ -309,6 +320,43 @@ def reorder_tree(node_lengths: Sequence[int], sample_paths: Sequence[Sequence[in
     nl = [int(node_lengths[v]) for v in placed]
     paths = [[new_index[v] for v in path] for path in sample_paths]
     return nl, paths
+
+
+# ----------------------------------------------------------------------------
+# draft blocks of a block-diffusion drafter over packed documents
+# ----------------------------------------------------------------------------
+def draft_layout(doc_lens: Sequence[int], block_size: int, blocks_per_doc,
+                 rng: np.random.Generator, causal: bool = False, keep_frac: float = 1.0,
+                 extra_pad: int = 0, doc_ids: Optional[Sequence[int]] = None) -> Layout:
+    """Context = the documents packed in order; per document, ``blocks_per_doc`` anchors
+    drawn uniformly where a whole block stays inside the document (anchor + block_size
+    - 1 within it, as the Automodel PR #3023 page samples them; a shorter document gets
+    none), sorted; blocks follow the context in that order.  ``keep_frac`` of the blocks
+    are kept (the rest masked out).  ``extra`` holds the draft-mask arguments."""
+    n_docs = len(doc_lens)
+    per = ([int(blocks_per_doc)] * n_docs if np.isscalar(blocks_per_doc)
+           else [int(x) for x in blocks_per_doc])
+    ids = list(range(n_docs)) if doc_ids is None else [int(x) for x in doc_ids]
+    ctx_doc = np.concatenate([np.full(n, i, np.int32) for i, n in zip(ids, doc_lens)] +
+                             [np.zeros(0, np.int32)])
+    anchors, adoc = [], []
+    start = 0
+    for i, n, k in zip(ids, doc_lens, per):
+        hi = n - (block_size - 1)  # anchors 0 .. n - block_size: the block ends in the document
+        if hi > 0 and k > 0:
+            anchors += sorted(start + int(a) for a in rng.integers(0, hi, size=k))
+            adoc += [i] * k
+        start += n
+    S = int(sum(doc_lens))
+    N = len(anchors)
+    keep = (rng.random(N) < keep_frac).astype(np.uint8) if keep_frac < 1.0 else \
+        np.ones(N, np.uint8)
+    t_real = S + N * block_size
+    return Layout("draft", t_real + extra_pad, t_real,
+                  extra={"ctx_len": S, "block_size": int(block_size),
+                         "anchors": np.asarray(anchors, np.int32), "keep": keep,
+                         "ctx_doc": ctx_doc, "anchor_doc": np.asarray(adoc, np.int32),
+                         "causal": bool(causal)})
 
 
 # ----------------------------------------------------------------------------

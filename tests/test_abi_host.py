@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.psa_abi_version() == 3
+    assert lib.psa_abi_version() == 4
     for code, name in psa.STATUS.items():
         s = lib.psa_status_string(code).decode()
         assert s and s != "unknown status", name
@@ -102,6 +102,23 @@ def test_builder_flags_rejected(lib):
                                           ctypes.c_void_p(nodes.ctypes.data), 4, 128, 128, 4,
                                           None, ctypes.byref(out)) == 10
     assert b"flag" in lib.psa_last_error()
+
+
+def test_draft_builder_argument_errors(lib):
+    """Checked on the host before any device work."""
+    out = ctypes.c_void_p()
+    fake = ctypes.c_void_p(256)  # never dereferenced: every check below fails first
+    call = lambda S, bs, n, anchors=fake, cdoc=None, adoc=None, flags=0, T=None: \
+        lib.psa_build_tile_map_draft(S, bs, n, anchors, None, cdoc, adoc, flags,
+                                     S + n * bs if T is None else T, 128, 128, None,
+                                     ctypes.byref(out))  # noqa: E731
+    assert call(8, 4, 2, flags=2) == 10                  # unknown flag
+    assert call(8, 0, 2) == 2                            # block_size < 1
+    assert call(8, 4, 2, T=15) == 2                      # T too short
+    assert call(1 << 20, 1, 1 << 13) == 2                # (S + 1) * N above 2^32
+    assert call(8, 4, 2, anchors=None) == 1              # anchors missing
+    assert call(8, 4, 2, cdoc=fake) == 1                 # documents given by halves
+    assert call(8, 4, 2, adoc=fake) == 1
 
 
 def test_tree_shape_errors(lib):
