@@ -157,14 +157,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   int32_t qkey = 0;  // node form: this row's node number (0: a pad or past T)
   const int32_t* const ev = NODES ? p.nlo : p.end;
 
+  // DMA path: a stage's K and V tile loads are not issued in one burst (the wave
+  // would stall on the memory-request queue) but one per reduction step of the
+  // current sub-step's S product, where the MFMAs hide their issue cost.  Without a
+  // next sub-step the descriptors cover 0 bytes and the loads only write zeros into
+  // the idle buffer.
+  constexpr int NL = DmaTile<C::BN, D, C::NT>::N;  // loads per tile and wave
+  DmaRsrc rk{}, rvv{};
+  char* st_next = smem;
+  auto dma_part = [&](int j) {
+    if constexpr (C::kDma) {
+      const int w = threadIdx.x >> 6;
+      if (j < NL)
+        dma_load16(rk, dt.voff[j], st_next + (j * (C::NT / 64) + w) * 1024);
+      else
+        dma_load16(rvv, dt.voff[j - NL],
+                   st_next + C::TILE_BYTES + ((j - NL) * (C::NT / 64) + w) * 1024);
+    }
+  };
+
   auto issue = [&](int n, int col_n) {  // global reads of sub-step n
     const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
     if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | mask words
       static_assert(C::BN == 64, "one end[] value per lane");
       char* st = smem + (n & 1) * C::STAGE_BYTES;
-      dt.load(K + kv0 * ldk + koff, nvalid, pitch, st);
-      dt.load(V + kv0 * ldk + koff, nvalid, pitch, st + C::TILE_BYTES);
+      st_next = st;
+      rk = dma_rsrc(K + kv0 * ldk + koff, nvalid * pitch);
+      rvv = dma_rsrc(V + kv0 * ldk + koff, nvalid * pitch);
       if (wave == 0)  // keys past the end read end = 0 (or w = 0): never visible
         dma_load4(dma_rsrc(ev + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
       if constexpr (NODES)
@@ -198,7 +218,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
 
   if (n_steps > 0) {
     issue(0, int(entry(0) & 0x3fffffffu));
-    if constexpr (!C::kDma) commit(0);
+    if constexpr (C::kDma) {
+#pragma unroll
+      for (int j = 0; j < 2 * NL; ++j) dma_part(j);
+    } else {
+      commit(0);
+    }
   }
   {  // Q stays in registers; its loads overlap the first tile's
     const T* qp = Q + (qrow * hq + h) * D + 8 * half;
@@ -228,6 +253,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
         mark_ready(*reinterpret_cast<int32_t*>(&wreg));
       }
       issue(n + 1, int(entry(n + 1) & 0x3fffffffu));
+    } else if constexpr (C::kDma) {
+      st_next = smem + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
+      rk = dma_rsrc(K, 0);
+      rvv = rk;
     }
 
     const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
@@ -266,6 +295,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
             }
 #pragma unroll
             for (int kb = 0; kb < NK; ++kb) mma(acc_s[kb], kq[s % PF][kb], qf[s]);
+            // the next stage's tile loads, spread over these steps
+#pragma unroll
+            for (int j = 0; j < 2 * NL; ++j)
+              if ((j * NS) / (2 * NL) == s) dma_part(j);
           }
           // keep that order: the first PF-1 steps' reads, then per step the reads
           // PF-1 steps ahead followed by this step's MFMAs
