@@ -401,19 +401,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       l += rs;
 
       // O^T += V^T P^T, 16 keys per step
+      if constexpr (C::kDma && D > 128) {
+        // P fragments first; the (t, db) transposed V reads PF products ahead of
+        // their MFMAs, so that LDS latency overlaps the MFMAs in flight (at d = 128
+        // the compiler's own order of the reads is faster, at d = 256 this one)
+        constexpr int NT16 = C::BN / 16, ND = D / 32, NI = NT16 * ND, PF = 3;
+        Frag<T> pfr[NT16];
 #pragma unroll
-      for (int t = 0; t < C::BN / 16; ++t) {
-        const Frag<T> pf = frag_from<T>(&sv[t >> 1][(t & 1) * 8]);
+        for (int t = 0; t < NT16; ++t) pfr[t] = frag_from<T>(&sv[t >> 1][(t & 1) * 8]);
+        const char* vst = st + C::TILE_BYTES;
+        Frag<T> va[PF];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          Frag<T> va;
-          if constexpr (C::kDma)
-            va = frag_load_tr_swz<D / 8>(st + C::TILE_BYTES, 16 * t, 32 * db);
-          else if constexpr (C::kBf16)
-            va = frag_load_tr(Vs, C::VS, 16 * t, 32 * db);
-          else
-            va = frag_load(Vs + (32 * db + l32) * C::VS + 16 * t + 8 * half);
-          mma(acc[db], va, pf);
+        for (int i = 0; i < PF - 1; ++i)
+          va[i] = frag_load_tr_swz<D / 8>(vst, 16 * (i / ND), 32 * (i % ND));
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if (i + PF - 1 < NI) {
+            const int j = i + PF - 1;
+            va[j % PF] = frag_load_tr_swz<D / 8>(vst, 16 * (j / ND), 32 * (j % ND));
+          }
+          mma(acc[i % ND], va[i % PF], pfr[i / ND]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 3);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if (i + PF - 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < C::BN / 16; ++t) {
+          const Frag<T> pf = frag_from<T>(&sv[t >> 1][(t & 1) * 8]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            Frag<T> va;
+            if constexpr (C::kDma)
+              va = frag_load_tr_swz<D / 8>(st + C::TILE_BYTES, 16 * t, 32 * db);
+            else if constexpr (C::kBf16)
+              va = frag_load_tr(Vs, C::VS, 16 * t, 32 * db);
+            else
+              va = frag_load(Vs + (32 * db + l32) * C::VS + 16 * t + 8 * half);
+            mma(acc[db], va, pf);
+          }
         }
       }
     }
