@@ -646,6 +646,7 @@ void dq_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t qrow = int64_t(qt) * C::BM + 32 * wave + l32;
+  const int wave_last = qt * C::BM + 32 * wave + 31;  // this wave's last row
   const bool qvalid = qrow < ntok;
   const int qrow_i = int(qrow);
 
@@ -802,7 +803,9 @@ void dq_kernel(BwdParams p) {
     const int32_t* Es = C::kDma ? reinterpret_cast<const int32_t*>(st + 2 * C::TILE_BYTES)
                                 : es0 + b * C::MW * C::BN;
 
-    {
+    // keys of a partial tile all after this wave's rows: no kept pair (kv <= q is
+    // part of every causal mask), nothing to add to dQ
+    if (!(partial && p.causal && kv0i > wave_last)) {
       const int qd = qrow_i - kv0i;
       float ds[C::BN / 32][16];
 #pragma unroll

@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t qrow = int64_t(qt) * C::BM + 32 * wave + l32;
+  const int wave_last = qt * C::BM + 32 * wave + 31;  // this wave's last row
   const bool qvalid = qrow < ntok;
   const int qrow_i = int(qrow);
 
@@ -265,7 +266,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     const int32_t* Es = C::kDma ? reinterpret_cast<const int32_t*>(st + 2 * C::TILE_BYTES)
                                 : es0 + b * C::MW * C::BN;
 
-    {
+    // a partial tile's sub-step whose keys all come after this wave's rows holds no
+    // kept pair (kv <= q is part of every causal mask): the wave skips its products
+    // and softmax update (both would leave its state as it is); the next stage's tile
+    // loads still go out
+    if (partial && p.causal && kv0i > wave_last) {
+      if constexpr (C::kDma) {
+#pragma unroll
+        for (int j = 0; j < 2 * NL; ++j) dma_part(j);
+      }
+    } else {
       // S^T = K Q^T for BN keys x 32 queries (this wave)
       // (the BN/32 accumulation chains are interleaved so that consecutive MFMAs do
       // not wait on each other's results)
