@@ -1,6 +1,6 @@
 """Benchmark of the shared-prefix attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 
 One step = one pass of the whole path over one batch of synthetic input: build the
 tile map from the per-token labels (label scan -> interval ends -> classification ->
@@ -143,9 +143,9 @@ KERNEL_STAGE = {"fwd_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bw
 TRAFFIC_PASSES = ("FETCH_SIZE", "WRITE_SIZE")
 
 
-def traffic_summary(pmc_dir: str, config: int, calib_mb: int, command: str) -> None:
+def traffic_summary(pmc_dir: str, workload: str, calib_mb: int, command: str) -> None:
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, each
-    with --calib-mb) into profiles/traffic_<stage>_config<N>.json, one per attention
+    with --calib-mb) into profiles/traffic_<stage>_<workload>.json, one per attention
     kernel: the counters (KiB per dispatch) scaled so that the reference negation over
     calib_mb MiB reads and writes exactly calib_mb MiB."""
     import csv
@@ -189,7 +189,7 @@ def traffic_summary(pmc_dir: str, config: int, calib_mb: int, command: str) -> N
         e["bytes_per_launch"] = int(sum(e[c + "_KiB"] * e[c + "_scale"] * 1024 for c in TRAFFIC_PASSES))
         e["kernel_source_hash"] = src_hash
         e["command"] = command
-        path = os.path.join(ROOT, "profiles", f"traffic_{stage}_config{config}.json")
+        path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
         with open(path, "w") as fh:
             json.dump(e, fh, indent=1)
         print(path, e["bytes_per_launch"])
@@ -254,7 +254,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--split", action="store_true",
@@ -282,7 +282,9 @@ def main():
                     help="with --traffic-summary: the command line the passes ran, recorded")
     args = ap.parse_args()
     if args.traffic_summary:
-        traffic_summary(args.traffic_summary, args.config, args.calib_mb or 512,
+        from shared_prefix_block_amd import workloads as wl
+        traffic_summary(args.traffic_summary, wl.WORKLOADS[args.workload].name,
+                        args.calib_mb or 512,
                         args.traffic_command)
         return
 
@@ -301,7 +303,7 @@ def main():
     psa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = wl.CONFIGS[args.config]
+    cfg = wl.WORKLOADS[args.workload]
     lay = wl.layout_for(cfg)
     if args.layout == "chunked":
         if lay.kind != "tokens":
@@ -322,7 +324,7 @@ def main():
             sys.exit("--fold needs a token-form workload (rollout groups)")
         print(json.dumps(fold_bench(cfg, lay, args.steps, args.warmup)), flush=True)
         return
-    q, k, v, do = wl.config_tensors(cfg, lay)
+    q, k, v, do = wl.workload_tensors(cfg, lay)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
     backward = cfg.passes != "fwd"
     do = do.to(dev) if backward else None
@@ -416,7 +418,7 @@ def main():
     dom = max(cand, key=cand.get)
     achieved = kept * hq * algo[dom] / (avg[dom] * 1e-3) / 1e12
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_config{cfg.idx}.json")
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_{cfg.name}.json")
     if os.path.exists(tpath):
         with open(tpath) as fh:
             t = json.load(fh)

@@ -36,7 +36,7 @@ GroupSpecs = List[Tuple[int, List[int]]]
 
 
 @dataclass(frozen=True)
-class Config:
+class Workload:
     """One synthetic workload: layout, head counts, head dim, dtype, passes."""
 
     idx: int
@@ -52,20 +52,20 @@ class Config:
     note: str = ""
 
 
-CONFIGS = {
-    1: Config(1, "1grp_P64_G4_R32", "tokens", 2, 2, 64, "fp32", 1.0, "fwd",
+WORKLOADS = {
+    1: Workload(1, "1grp_P64_G4_R32", "tokens", 2, 2, 64, "fp32", 1.0, "fwd",
               note="1 group, P=64, G=4 x R=32 (T=192), fp32, forward only"),
-    2: Config(2, "8grp_P512_G8_R256", "tokens", 32, 8, 128, "bf16", 1.0, "fwd+bwd",
+    2: Workload(2, "8grp_P512_G8_R256", "tokens", 32, 8, 128, "bf16", 1.0, "fwd+bwd",
               note="8 groups, P=512, G=8 x R=256 (T=20480), GQA 32/8, d=128, bf16"),
-    3: Config(3, "16grp_varlen", "tokens", 16, 4, 128, "bf16", 1.0, "fwd+bwd",
+    3: Workload(3, "16grp_varlen", "tokens", 16, 4, 128, "bf16", 1.0, "fwd+bwd",
               pad_multiple=128,
               note="16 groups, P~U[128,2048], G=16, R~U[64,1024], padded to x128, GQA 16/4"),
-    4: Config(4, "2grp_P16384_G64_R512", "tokens", 8, 8, 128, "bf16", 0.5, "fwd+bwd",
+    4: Workload(4, "2grp_P16384_G64_R512", "tokens", 8, 8, 128, "bf16", 0.5, "fwd+bwd",
               note="2 groups, P=16384, G=64 x R=512 (T=98304), 8/8 heads, N(0, 0.5)"),
-    5: Config(5, "8trees_1024_4x256_4x384", "tree", 16, 8, 256, "bf16", 1.0, "fwd+bwd",
+    5: Workload(5, "8trees_1024_4x256_4x384", "tree", 16, 8, 256, "bf16", 1.0, "fwd+bwd",
               note="8 trees: root 1024 -> 4 x 256 -> 4 x 384 leaves (T=65536), GQA 16/8, d=256"),
     # the second mask workload: a block-diffusion drafter's packed-document batch
-    6: Config(6, "draft_4doc_4096_bs16", "draft", 16, 4, 128, "bf16", 1.0, "fwd+bwd",
+    6: Workload(6, "draft_4doc_4096_bs16", "draft", 16, 4, 128, "bf16", 1.0, "fwd+bwd",
               note="draft blocks: 4 packed documents of 4096 context tokens, 512 blocks of "
                    "16 per document (T=49152), bidirectional blocks, GQA 16/4, d=128"),
 }
@@ -74,8 +74,8 @@ CONFIGS = {
 # ----------------------------------------------------------------------------
 # layouts
 # ----------------------------------------------------------------------------
-def group_specs(cfg: Config, seed: Optional[int] = None) -> GroupSpecs:
-    """(P_g, [R_g0, R_g1, ...]) for every group of a token-form config."""
+def group_specs(cfg: Workload, seed: Optional[int] = None) -> GroupSpecs:
+    """(P_g, [R_g0, R_g1, ...]) for every group of a token-form workload."""
     if cfg.idx == 1:
         return [(64, [32] * 4)]
     if cfg.idx == 2:
@@ -90,7 +90,7 @@ def group_specs(cfg: Config, seed: Optional[int] = None) -> GroupSpecs:
         return specs
     if cfg.idx == 4:
         return [(16384, [512] * 64) for _ in range(2)]
-    raise ValueError(f"config {cfg.idx} is not token-form")
+    raise ValueError(f"workload {cfg.idx} is not token-form")
 
 
 def tree_spec(n_trees: int = 8, root: int = 1024, n_branch: int = 4, branch: int = 256,
@@ -159,7 +159,7 @@ class Layout:
     extra: dict = field(default_factory=dict)
 
 
-def layout_for(cfg: Config, seed: Optional[int] = None) -> Layout:
+def layout_for(cfg: Workload, seed: Optional[int] = None) -> Layout:
     if cfg.kind == "draft":
         rng = np.random.default_rng(cfg.idx if seed is None else seed)
         return draft_layout([4096] * 4, 16, 512, rng)
@@ -378,7 +378,7 @@ def make_tensors(T: int, hq: int, hkv: int, d: int, dtype: str, sigma: float = 1
     return q, k, v, do
 
 
-def config_tensors(cfg: Config, layout: Layout, seed: Optional[int] = None):
+def workload_tensors(cfg: Workload, layout: Layout, seed: Optional[int] = None):
     return make_tensors(layout.T, cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.sigma,
                         cfg.idx if seed is None else seed,
                         with_grad_out=(cfg.passes != "fwd"))

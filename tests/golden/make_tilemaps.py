@@ -16,7 +16,7 @@ from oracle.tilemap import tile_counts, tile_kinds  # noqa: E402
 from shared_prefix_block_amd import workloads as wl  # noqa: E402
 
 for idx in (3, 4):
-    lay = wl.layout_for(wl.CONFIGS[idx])
+    lay = wl.layout_for(wl.WORKLOADS[idx])
     counts = tile_counts(meta_from_layout(lay), 128, 128, block_rows=2048)
     kinds = tile_kinds(counts, 128, 128)
     path = os.path.join(HERE, f"tilemap_cfg{idx}_128x128.npz")

@@ -242,11 +242,11 @@ def _boundaries(lay):
 
 @pytest.mark.parametrize("idx,split", [(1, False), (2, False), (3, False), (4, False),
                                        (5, False), (2, True), (4, True)])
-def test_config_parity_sampled(idx, split):
-    cfg = wl.CONFIGS[idx]
+def test_workload_parity_sampled(idx, split):
+    cfg = wl.WORKLOADS[idx]
     lay = wl.layout_for(cfg)
     backward = cfg.passes != "fwd"
-    say(f"config {idx}: T={lay.T} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d} {cfg.dtype} "
+    say(f"workload {idx}: T={lay.T} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d} {cfg.dtype} "
         f"split={split}")
     (q, k, v, do), got = _run(lay, cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.idx, cfg.sigma,
                               backward, split=split)
@@ -296,7 +296,7 @@ def test_config_parity_sampled(idx, split):
 def test_zero_query_closed_form(idx):
     """Q = 0 pins the kernel's mask row by row without the oracle: every visible score is
     0, so LSE = ln(#visible keys) and O = the mean of the visible V rows."""
-    cfg = wl.CONFIGS[idx]
+    cfg = wl.WORKLOADS[idx]
     lay = wl.layout_for(cfg)
     _, k, v, _ = wl.make_tensors(lay.T, cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.sigma, idx,
                                  with_grad_out=False)

@@ -108,11 +108,11 @@ def test_draft_generation_block(causal):
 def test_draft_workload_sampled():
     """The draft workload at full size (4 packed documents of 4096 context tokens, 512
     blocks of 16 each, bidirectional): sampled rows and keys vs the oracle."""
-    cfg = wl.CONFIGS[6]
+    cfg = wl.WORKLOADS[6]
     lay = wl.layout_for(cfg)
     tdt = DT[cfg.dtype]
     say(f"draft workload: T={lay.T} hq={cfg.hq} hkv={cfg.hkv} d={cfg.d}")
-    q, k, v, do = wl.config_tensors(cfg, lay)
+    q, k, v, do = wl.workload_tensors(cfg, lay)
     m = psa.layout_tile_map(lay, "cuda", dtype=tdt, d=cfg.d)
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     o, lse = psa.fwd(m, qd, kd, vd)

@@ -74,7 +74,7 @@ def test_fold_degenerate():
 def test_fold_workload_layouts(idx):
     """The workloads' rollout shapes, random token ids: the fold matches the oracle, and
     its attention metadata is the layout the attention tests and the bench use."""
-    cfg = wl.CONFIGS[idx]
+    cfg = wl.WORKLOADS[idx]
     specs = wl.group_specs(cfg)
     rng = np.random.default_rng(idx)
     prompts = [rng.integers(0, 150000, p).astype(np.int32) for p, _ in specs]

@@ -162,12 +162,12 @@ def test_general_full_size_sampled(which):
     token with prompt tokens anywhere), and the 8 trees in breadth-first node order."""
     rng = np.random.default_rng(77)
     if which == "tree":
-        cfg = wl.CONFIGS[5]
+        cfg = wl.WORKLOADS[5]
         nl, paths = wl.tree_spec()
         nl, paths = wl.reorder_tree(nl, paths)
         lay = wl.tree_layout(nl, paths)
     else:
-        cfg = wl.CONFIGS[2]
+        cfg = wl.WORKLOADS[2]
         specs = wl.group_specs(cfg)
         lay = wl.shuffled_tokens_layout(specs, rng, prompt_first=(which == "chunked"),
                                         chunk=64 if which == "chunked" else 1)

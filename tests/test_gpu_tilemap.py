@@ -64,30 +64,30 @@ def test_tilemap_fuzz_bit_exact(seed):
 
 @pytest.mark.parametrize("idx", [1, 2, 5])
 @pytest.mark.parametrize("bm,bn", [(128, 128), (128, 64), (64, 64)])
-def test_tilemap_configs(idx, bm, bn):
-    lay = wl.layout_for(wl.CONFIGS[idx])
-    say(f"tilemap config {idx} T={lay.T} tile={bm}x{bn}")
+def test_tilemap_workloads(idx, bm, bn):
+    lay = wl.layout_for(wl.WORKLOADS[idx])
+    say(f"tilemap workload {idx} T={lay.T} tile={bm}x{bn}")
     m = _gpu_map(lay, bm, bn)
     _assert_same_map(m.export(), ot.tile_map(meta_from_layout(lay), bm, bn), m.info)
 
 
 @pytest.mark.parametrize("idx", [3, 4])
-def test_tilemap_large_configs_golden(idx):
+def test_tilemap_large_workloads_golden(idx):
     g = np.load(os.path.join(GOLDEN, f"tilemap_cfg{idx}_128x128.npz"))
-    lay = wl.layout_for(wl.CONFIGS[idx])
+    lay = wl.layout_for(wl.WORKLOADS[idx])
     assert int(g["T"]) == lay.T
     kinds = g["kinds"]
     want = {"kinds": kinds, "n_full": int((kinds == 2).sum()),
             "n_partial": int((kinds == 1).sum())}
     want["row_ptr"], want["col"], want["kind"] = ot.csr(kinds)
     want["col_ptr"], want["row"], want["kind_csc"] = ot.csc(kinds)
-    say(f"tilemap config {idx} T={lay.T} (golden)")
+    say(f"tilemap workload {idx} T={lay.T} (golden)")
     m = _gpu_map(lay, 128, 128)
     _assert_same_map(m.export(), want, m.info)
 
 
 def test_tilemap_deterministic():
-    lay = wl.layout_for(wl.CONFIGS[3])
+    lay = wl.layout_for(wl.WORKLOADS[3])
     a = _gpu_map(lay, 128, 128).export()
     b = _gpu_map(lay, 128, 128).export()
     for k in a:

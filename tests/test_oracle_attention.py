@@ -146,8 +146,8 @@ def test_folded_equals_unfolded_trees(seed):
     _folded_vs_unfolded(lay, seqs, owner, 4, 2, 8, seed)
 
 
-def test_folded_equals_unfolded_config1():
-    cfg = wl.CONFIGS[1]
+def test_folded_equals_unfolded_1grp_P64():
+    cfg = wl.WORKLOADS[1]
     lay = wl.layout_for(cfg)
     seqs, _ = uf.group_sequences(lay.specs)
     owner = np.full(lay.T, -1)
@@ -181,7 +181,7 @@ def test_zero_query_closed_form(seed):
 
 
 def test_constant_values_give_constant_output():
-    lay = wl.layout_for(wl.CONFIGS[1])
+    lay = wl.layout_for(wl.WORKLOADS[1])
     meta = meta_from_layout(lay)
     q, k, _, _ = _rand(lay.T, 2, 2, 64, 5)
     c = torch.linspace(-1, 1, 64, dtype=torch.float64)

@@ -130,8 +130,8 @@ def test_kept_count_closed_form_random(seed):
 
 
 @pytest.mark.parametrize("idx,expected", [(1, 12_384), (2, 11_544_576), (5, 86_016_000)])
-def test_kept_count_configs(idx, expected):
-    cfg = wl.CONFIGS[idx]
+def test_kept_count_workloads(idx, expected):
+    cfg = wl.WORKLOADS[idx]
     lay = wl.layout_for(cfg)
     meta = meta_from_layout(lay)
     if lay.kind == "tokens":
@@ -144,8 +144,8 @@ def test_kept_count_configs(idx, expected):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("idx", [3, 4])
-def test_kept_count_large_configs(idx):
-    cfg = wl.CONFIGS[idx]
+def test_kept_count_large_workloads(idx):
+    cfg = wl.WORKLOADS[idx]
     lay = wl.layout_for(cfg)
     closed = uf.kept_closed_form_groups(lay.specs)
     if idx == 4:

@@ -71,8 +71,8 @@ def _check_sparse(m):
 
 @pytest.mark.parametrize("idx", [1, 2, 5])
 @pytest.mark.parametrize("bm,bn", [(128, 128), (128, 64), (64, 64)])
-def test_config_tile_maps_sum_to_closed_form(idx, bm, bn):
-    cfg = wl.CONFIGS[idx]
+def test_workload_tile_maps_sum_to_closed_form(idx, bm, bn):
+    cfg = wl.WORKLOADS[idx]
     lay = wl.layout_for(cfg)
     m = ot.tile_map(meta_from_layout(lay), bm, bn)
     if lay.kind == "tokens":
@@ -83,11 +83,11 @@ def test_config_tile_maps_sum_to_closed_form(idx, bm, bn):
     _check_sparse(m)
 
 
-def test_config_tile_kind_totals_128():
-    """Full / partial / empty tile totals at 128 x 128 for configs 1, 2 and 5."""
+def test_workload_tile_kind_totals_128():
+    """Full / partial / empty tile totals at 128 x 128 for workloads 1, 2 and 5."""
     want = {1: (0, 3, 1), 2: (624, 160, 24_816), 5: (4_992, 512, 256_640)}
     for idx, (full, part, empty) in want.items():
-        lay = wl.layout_for(wl.CONFIGS[idx])
+        lay = wl.layout_for(wl.WORKLOADS[idx])
         m = ot.tile_map(meta_from_layout(lay), 128, 128)
         k = m["kinds"]
         assert (int((k == 2).sum()), int((k == 1).sum()), int((k == 0).sum())) == \
