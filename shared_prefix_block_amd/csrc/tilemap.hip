@@ -523,18 +523,22 @@ __global__ __launch_bounds__(64) void k_ktile_summary_nodes(int64_t T, int32_t b
   }
 }
 
-// One block per q-tile, its keys in LDS; each wave takes every fourth kv-tile.  A
-// tile is empty when it lies wholly after the q-tile (kv > q everywhere; causal maps
-// only) or when the keys' subtree ranges miss the q-tile's key range; full when it
-// lies wholly at or before the q-tile (causal maps) and every range holds every key;
-// otherwise the wave searches it exactly, one column per lane, for a kept pair.
+// One block per q-tile, its keys in LDS as runs of equal node numbers (number, last
+// row); each wave takes every fourth kv-tile.  A tile is empty when it lies wholly
+// after the q-tile (kv > q everywhere; causal maps only) or when the keys' subtree
+// ranges miss the q-tile's key range; full when it lies wholly at or before the
+// q-tile (causal maps) and every range holds every key; otherwise the wave searches
+// it exactly, one column per lane: a key is seen by some row iff a run's number lies
+// in its range (and, causal, the run ends at or after the key).
 __global__ __launch_bounds__(kClassifyThreads) void k_classify_nodes_rows(
     int64_t T, int32_t bm, int32_t bn, int64_t nq, int64_t nk, const int32_t* __restrict__ key,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ w, int32_t causal,
     const int32_t* __restrict__ ksum, int64_t stride, uint8_t* kinds, int32_t* row_ptr,
     int32_t* col_ptr, int64_t* info) {
   __shared__ int32_t qk[1024];
+  __shared__ int32_t runk[1024], runl[1024];  // run number, run's last row (absolute)
   __shared__ int red[3][kClassifyThreads / 64];
+  __shared__ int n_runs;
   const int64_t i = blockIdx.x;
   const int64_t q0 = i * bm;
   const int64_t q_last = (q0 + bm < T ? q0 + bm : T) - 1;
@@ -570,7 +574,25 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_nodes_rows(
     kmax = red[1][k] > kmax ? red[1][k] : kmax;
     all_real = all_real && red[2][k];
   }
+  if (wv == 0) {  // run-length encoding of the rows' node numbers, 64 rows at a time
+    int count = 0;
+    for (int base = 0; base < nrow; base += 64) {
+      const int r = base + lane;
+      const bool start = r < nrow && (r == 0 || qk[r] != qk[r - 1]);
+      const unsigned long long m = __ballot(start);
+      const int at = count + __popcll(m & ((1ull << lane) - 1)) - 1;  // run of row r
+      if (start) runk[at + 1] = qk[r];
+      count += __popcll(m);
+      // the row before a run start ends the previous run
+      if (start && r > 0) runl[at] = int(q0) + r - 1;
+    }
+    if (lane == 0) {
+      if (count > 0) runl[count - 1] = int(q0) + nrow - 1;
+      n_runs = count;
+    }
+  }
   __syncthreads();
+  const int m_runs = n_runs;
 
   int cnt = 0, nfull = 0, npart = 0;  // lane 0 of each wave counts its tiles
   for (int64_t j = wv; j < nk; j += kClassifyThreads / 64) {
@@ -587,8 +609,8 @@ __global__ __launch_bounds__(kClassifyThreads) void k_classify_nodes_rows(
         for (int64_t kv = k0 + lane; kv <= k_last && !found; kv += 64) {
           const int a = lo[kv], n = w[kv];
           if (n <= 0) continue;
-          for (int64_t r = causal && kv > q0 ? kv - q0 : 0; r < nrow; ++r) {
-            if (uint32_t(qk[r] - a) < uint32_t(n)) {
+          for (int e = 0; e < m_runs; ++e) {
+            if (uint32_t(runk[e] - a) < uint32_t(n) && (!causal || runl[e] >= kv)) {
               found = true;
               break;
             }
