@@ -29,7 +29,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOP/s (unmasked tiles) fwd+bwd, % bf16 MFMA peak; tokens/s"
-PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3, "fp8": 5033.2}  # MI355X dense MFMA
+# e4m3 forward: S = Q K^T on the fp8 MFMA, P V on the bf16 one (2d FLOPs each per
+# kept pair): the peak of that mix is 4d over the time both halves take at their peaks
+PEAK_FP8_FWD = 4.0 / (2.0 / PEAK_TFLOPS["fp8"] + 2.0 / PEAK_TFLOPS["bf16"])
 HBM_PEAK_GBS = 8000.0
 TILE = 128
 KERNEL_SOURCES = ["attn_common.h", "attn_fwd.hip", "attn_bwd.hip"]
@@ -278,6 +281,9 @@ def main():
                          "interleaved in turns of 64 tokens after its prompt (token-form "
                          "workloads); bfs: tree nodes in breadth-first order (tree workloads). "
                          "Both keep the kept pairs; the map takes the node form")
+    ap.add_argument("--nograd", default=None, choices=["bf16", "fp8"],
+                    help="time the no-grad forward (no LSE stored) in this input dtype "
+                         "instead of the workload's passes: map build + forward")
     ap.add_argument("--traffic-command", default="",
                     help="with --traffic-summary: the command line the passes ran, recorded")
     args = ap.parse_args()
@@ -324,31 +330,41 @@ def main():
             sys.exit("--fold needs a token-form workload (rollout groups)")
         print(json.dumps(fold_bench(cfg, lay, args.steps, args.warmup)), flush=True)
         return
-    q, k, v, do = wl.workload_tensors(cfg, lay)
+    if args.nograd:
+        args.no_cpu_baseline = True
+        q, k, v, do = wl.make_tensors(lay.T, cfg.hq, cfg.hkv, cfg.d, args.nograd, cfg.sigma,
+                                      cfg.idx, with_grad_out=False)
+        passes = f"fwd, no grad (no LSE), {args.nograd} inputs"
+    else:
+        q, k, v, do = wl.workload_tensors(cfg, lay)
+        passes = cfg.passes
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
-    backward = cfg.passes != "fwd"
+    backward = cfg.passes != "fwd" and not args.nograd
+    dtype_name = args.nograd or cfg.dtype
     do = do.to(dev) if backward else None
     if lay.kind == "tokens":
         labels = (torch.as_tensor(lay.group).to(dev), torch.as_tensor(lay.suffix).to(dev),
                   torch.as_tensor(lay.is_prefix).to(dev))
     tdt = q.dtype
     gdt = torch.float32 if args.grad_dtype == "fp32" else tdt
-    o = torch.empty_like(q)
-    lse = torch.empty(cfg.hq, lay.T, device=dev, dtype=torch.float32)
+    o = torch.empty(q.shape, device=dev,
+                    dtype=torch.bfloat16 if tdt == torch.float8_e4m3fn else tdt)
+    lse = None if args.nograd else torch.empty(cfg.hq, lay.T, device=dev, dtype=torch.float32)
     grads = (torch.empty(q.shape, dtype=gdt, device=dev), torch.empty(k.shape, dtype=gdt, device=dev),
              torch.empty(v.shape, dtype=gdt, device=dev))
     stream = torch.cuda.current_stream(dev)
 
     def build_map():
         if lay.kind == "draft":
-            return psa.layout_tile_map(lay, dev, block_m=TILE, block_n=TILE)
+            return psa.layout_tile_map(lay, dev, block_m=TILE, block_n=TILE, dtype=tdt, d=cfg.d)
         if lay.kind == "tokens":
             return psa.build_tile_map_tokens(*labels, TILE, TILE, form=args.form)
         return psa.build_tile_map_tree(lay.node_lengths, lay.sample_paths, lay.T, dev, TILE, TILE,
                                        form=args.form)
 
     m0 = build_map()
-    ws = torch.empty(max(psa.bwd_workspace_size(m0, q, k), 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(psa.bwd_workspace_size(m0, q, k) if backward else 0, 1),
+                     dtype=torch.uint8, device=dev)
     info = dict(m0.info)
     del m0
 
@@ -361,7 +377,7 @@ def main():
         ev(0)
         m = build_map()
         ev(1)
-        psa.fwd(m, q, k, v, out=o, lse=lse)
+        psa.fwd(m, q, k, v, out=o, lse=lse, with_lse=lse is not None)
         ev(2)
         if backward:
             for i, nm in enumerate(names[2:]):
@@ -409,7 +425,8 @@ def main():
     kept_flops = kept * hq * (f_fwd + (f_bwd if backward else 0))
     ms_step = wall * 1e3 / args.steps
     value = tile_flops / (ms_step * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[cfg.dtype]
+    peak = PEAK_TFLOPS[dtype_name]
+    dom_peak = PEAK_FP8_FWD if dtype_name == "fp8" else peak
 
     # dominant kernel: algorithmic FLOPs per launch (fwd 4d; dK/dV 8d = S, dP, dV, dK;
     # dQ 2d: its S and dP are recomputations) per kept pair per q head
@@ -418,7 +435,8 @@ def main():
     dom = max(cand, key=cand.get)
     achieved = kept * hq * algo[dom] / (avg[dom] * 1e-3) / 1e12
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}_{cfg.name}.json")
+    variant = f"_nograd_{args.nograd}" if args.nograd else ""
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}{variant}_{cfg.name}.json")
     if os.path.exists(tpath):
         with open(tpath) as fh:
             t = json.load(fh)
@@ -436,21 +454,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": dtype_name,
         "data": "synthetic (seeded N(0, sigma) Q/K/V/dO; layout as the workload states)",
         "config": {"workload": describe(cfg, lay, args.layout, args.form), "T": lay.T,
                    "T_real": lay.T_real, "map_form": ["interval", "nodes"][info["form"]],
                    "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": d,
-                   "passes": cfg.passes, "grad_dtype": args.grad_dtype,
-                   "bwd_p_ds": "hi+lo bf16" if args.split else "bf16, hi+lo where large",
+                   "passes": passes, "grad_dtype": args.grad_dtype if backward else None,
+                   "bwd_p_ds": (("hi+lo bf16" if args.split else "bf16, hi+lo where large")
+                                if backward else None),
                    "tiles_128": {"full": info["n_full"], "partial": info["n_partial"]},
                    "kept_pairs_per_head": kept},
-        "pct_bf16_peak" if cfg.dtype == "bf16" else "pct_fp32_peak": round(100 * value / peak, 2),
+        f"pct_{dtype_name}_peak": round(100 * value / peak, 2),
         "kept_pair_tflops": round(kept_flops / (ms_step * 1e-3) / 1e12, 2),
         "tokens_per_s": round(lay.T_real / (ms_step * 1e-3), 1),
         "stage_ms": {nm: round(avg[nm], 4) for nm in names},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "peak": round(dom_peak, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / dom_peak, 4),
                      "traffic": traffic,
                      "algorithmic_flops_per_launch": kept * hq * algo[dom],
                      "avg_launch_ms": round(avg[dom], 4)},

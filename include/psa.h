@@ -58,7 +58,9 @@ typedef enum {
   PSA_ERR_VALUE = 10        /* a scalar argument is invalid (e.g. non-finite scale)     */
 } psa_status;
 
-typedef enum { PSA_FP32 = 0, PSA_BF16 = 1 } psa_dtype;
+/* Element types.  PSA_FP8_E4M3 (OCP e4m3 Q, K, V; O written in bf16) is taken by
+ * psa_fwd only, for forwards without gradient. */
+typedef enum { PSA_FP32 = 0, PSA_BF16 = 1, PSA_FP8_E4M3 = 2 } psa_dtype;
 typedef enum { PSA_PASS_FWD = 0, PSA_PASS_BWD = 1 } psa_pass;
 
 /* Opaque, library-owned, immutable after it is built. */
@@ -225,7 +227,10 @@ void psa_tile_map_destroy(psa_tile_map* map);
  * NULL for a forward whose LSE is not needed (no backward follows, e.g. the extra
  * no-grad log-prob passes of a policy-gradient step): then only O is written.
  * scale <= 0 selects 1/sqrt(d).  T must equal the map's T; the map's tile shape must
- * be psa_tile_shape(PSA_PASS_FWD, dtype, d).  Asynchronous on `stream`.
+ * be psa_tile_shape(PSA_PASS_FWD, dtype, d).  With PSA_FP8_E4M3, q, k, v hold OCP
+ * e4m3 bytes taken at face value (no per-tensor scale; fold one into `scale` for Q K^T
+ * and into O afterwards for V), products accumulate in fp32, P is rounded to bf16 for
+ * P V as in the bf16 path, and o is bf16.  Asynchronous on `stream`.
  * Errors: PSA_ERR_NULL, PSA_ERR_SHAPE, PSA_ERR_DTYPE, PSA_ERR_UNSUPPORTED,
  * PSA_ERR_MAP_MISMATCH, PSA_ERR_VALUE, PSA_ERR_HIP.
  */

@@ -275,7 +275,8 @@ psa_status finish_lists(psa_tile_map* m, const int64_t* info_h, psa_tile_map** o
 psa_status check_attn_args(const psa_tile_map* map, psa_dtype dtype, int64_t T, int32_t hq,
                            int32_t hkv, int32_t d, float scale, psa_pass pass) {
   if (!map) return psa_set_error(PSA_ERR_NULL, "map is NULL");
-  if (dtype != PSA_FP32 && dtype != PSA_BF16) return psa_set_error(PSA_ERR_DTYPE, "unknown dtype");
+  if (dtype != PSA_FP32 && dtype != PSA_BF16 && dtype != PSA_FP8_E4M3)
+    return psa_set_error(PSA_ERR_DTYPE, "unknown dtype");
   if (T < 0 || T > kMaxT) return psa_set_error(PSA_ERR_SHAPE, "T out of range");
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return psa_set_error(PSA_ERR_SHAPE, "need hq >= 1, hkv >= 1 and hq % hkv == 0");
@@ -338,7 +339,8 @@ const char* psa_last_error(void) { return g_last_error.c_str(); }
 psa_status psa_tile_shape(psa_pass pass, psa_dtype dtype, int32_t d, int32_t* block_m,
                           int32_t* block_n) {
   if (!block_m || !block_n) return psa_set_error(PSA_ERR_NULL, "output pointer is NULL");
-  if (dtype != PSA_FP32 && dtype != PSA_BF16) return psa_set_error(PSA_ERR_DTYPE, "unknown dtype");
+  if (dtype != PSA_FP32 && dtype != PSA_BF16 && dtype != PSA_FP8_E4M3)
+    return psa_set_error(PSA_ERR_DTYPE, "unknown dtype");
   bool ok = pass == PSA_PASS_FWD ? fwd_supported(dtype, d)
                                  : pass == PSA_PASS_BWD ? bwd_supported(dtype, d) : false;
   if (!ok) return psa_set_error(PSA_ERR_UNSUPPORTED, "no kernel for this pass / dtype / head_dim");

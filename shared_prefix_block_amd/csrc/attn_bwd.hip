@@ -1055,7 +1055,9 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
 }  // namespace
 }  // namespace psa
 
-bool bwd_supported(psa_dtype dt, int32_t d) { return fwd_supported(dt, d); }
+bool bwd_supported(psa_dtype dt, int32_t d) {
+  return dt != PSA_FP8_E4M3 && fwd_supported(dt, d);
+}
 
 size_t bwd_workspace_bytes(const AttnShape& s) {
   return 2 * psa::ws_align(size_t(s.T) * s.hq * sizeof(float));

@@ -36,6 +36,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 struct bf16_t {  // raw bfloat16 storage
   uint16_t bits;
 };
+struct fp8_t {  // raw fp8 storage, OCP e4m3 (the forward's scores take it)
+  uint8_t bits;
+};
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -52,6 +56,14 @@ struct Frag<bf16_t> {
 template <>
 struct Frag<float> {
   f32x4 lo, hi;
+};
+// fp8: the 32 consecutive reduction-index values one lane feeds to a 32x32 product over
+// 64 reduction indices (lane half h holds indices 32h .. 32h+31 of both operands; any
+// assignment the two operands share gives the same sum, and a probe of the MFMA with
+// small integers confirmed this one exactly).
+template <>
+struct Frag<fp8_t> {
+  i32x8 v;
 };
 
 template <typename T>
@@ -146,6 +158,24 @@ __device__ __forceinline__ void mma(f32x16& c, const Frag<float>& a, const Frag<
   c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[1], b.hi[1], c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[2], b.hi[2], c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[3], b.hi[3], c, 0, 0, 0);
+}
+
+// OCP e4m3 x e4m3 on the 32x32x64 scaled MFMA with unit scales (exponent 127).  Its
+// products are exact; a probe found its sums within ~1e-4 relative of fp32 sums when
+// the terms span many binades.
+__device__ __forceinline__ void mma(f32x16& c, const Frag<fp8_t>& a, const Frag<fp8_t>& b) {
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four OCP e4m3 bytes of w -> two packed bf16 pairs (exact: every e4m3 value is a bf16
+// value, and the fp32 conversion's low half is zero).
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(int(w), 0));
+  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(int(w), 1));
+  const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(int(w), 2));
+  const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(int(w), 3));
+  lo = (a >> 16) | (b & 0xffff0000u);
+  hi = (c >> 16) | (d & 0xffff0000u);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -260,6 +290,7 @@ __device__ __forceinline__ void mark_ready(f32x4& v) { asm("" : "+v"(v)); }
 __device__ __forceinline__ void mark_ready(float& v) { asm("" : "+v"(v)); }
 __device__ __forceinline__ void mark_ready(int32_t& v) { asm("" : "+v"(v)); }
 __device__ __forceinline__ void mark_ready(Frag<bf16_t>& f) { mark_ready(f.v); }
+__device__ __forceinline__ void mark_ready(Frag<fp8_t>& f) { asm("" : "+v"(f.v)); }
 __device__ __forceinline__ void mark_ready(Frag<float>& f) {
   mark_ready(f.lo);
   mark_ready(f.hi);
@@ -429,8 +460,13 @@ struct RowStage {
 // registers; the caller waits for them (vmcnt) before the barrier that publishes
 // the tile.
 // ---------------------------------------------------------------------------
+// The chunk permutation of row r stays inside the row (values below NC).  Rows of 4
+// chunks (64 bytes: e4m3 at d = 64) put 4 rows in one 256-byte bank sweep, so rows
+// r and r + 4 differ by r >> 2 alone.
 template <int NC>
 __device__ __forceinline__ int swz(int r) {
+  static_assert(NC == 4 || NC == 8 || NC == 16 || NC == 32, "chunks per row");
+  if constexpr (NC == 4) return (r >> 2) & 3;
   return NC >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 

@@ -62,12 +62,16 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays below 2^8
 template <typename T, int D, bool NODES>
 struct FwdCfg {
   static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
+  // fp8 inputs: the scores on the fp8 MFMA; V is widened to bf16 on its way to LDS
+  // (exactly) and the PV product, the softmax and O are those of the bf16 path
+  static constexpr bool kFp8 = std::is_same<T, fp8_t>::value;
+  using PT = typename std::conditional<kFp8, bf16_t, T>::type;  // P, V tile, O type
   static constexpr int NW = 4;
   static constexpr int NT = NW * 64;
   static constexpr int BM = 32 * NW;
   static_assert(BM == kTileM, "q-tile must match the map");
   static constexpr int EB = int(sizeof(T));
-  static constexpr int BN = (!kBf16 && D * EB > 256) ? 32 : 64;  // keys per sub-step
+  static constexpr int BN = (!kBf16 && !kFp8 && D * EB > 256) ? 32 : 64;  // keys per sub-step
   static constexpr int NSUB = kTileN / BN;
   static constexpr int KS = D + 16 / EB;                  // K row stride (elements)
   static constexpr int VS = kBf16 ? D + 32 / EB : BN + 16 / EB;  // V (row-major) or V^T
@@ -77,12 +81,14 @@ struct FwdCfg {
   // bf16 tiles come in by direct-to-LDS loads into swizzled, unpadded tiles (two
   // stages of K | V | mask words); fp32 tiles go through registers into padded tiles.
   // Mask words per key: end[] (interval form) or lo[] | w[] (node form).
-  static constexpr bool kDma = kBf16;
+  // fp8: K by direct-to-LDS loads (rows of D bytes), V through registers (widened).
+  static constexpr bool kDma = kBf16 || kFp8;
   static constexpr int MW = NODES ? 2 : 1;
-  static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + MW * BN * 4;
+  static constexpr int KT_BYTES = BN * D * EB;  // K tile (row-major, swizzled)
+  static constexpr int VT_BYTES = BN * D * 2;   // V tile (bf16, row-major, swizzled)
+  static constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES + MW * BN * 4;
   static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * MW * BN * 4;
-  static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
+  static constexpr int WAVES_PER_EU = ((kBf16 || kFp8) && D <= 128) ? 2 : 1;
 };
 
 template <typename T, int D, bool NODES>
@@ -111,7 +117,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
 
-  Frag<T> qf[D / 16];  // loaded below, once the first tile's loads are in flight
+  using PT = typename C::PT;
+  constexpr int NQF = C::kFp8 ? D / 64 : D / 16;  // Q fragments (reduction steps of S)
+  Frag<T> qf[NQF];  // loaded below, once the first tile's loads are in flight
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -147,13 +155,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   window_load(0);
   mark_ready(*reinterpret_cast<int32_t*>(&wreg));
 
-  RowStage<T, C::BN, D, C::KS, C::NT> kst;
-  using VStage = typename std::conditional<C::kBf16, RowStage<T, C::BN, D, C::VS, C::NT>,
-                                           TransStage<T, C::BN, D, C::VS, C::NT>>::type;
+  // register-path staging (fp32 only; the DMA paths never touch it)
+  using RT = typename std::conditional<C::kDma, float, T>::type;
+  RowStage<RT, C::BN, D, C::KS, C::NT> kst;
+  using VStage = typename std::conditional<C::kBf16, RowStage<RT, C::BN, D, C::VS, C::NT>,
+                                           TransStage<RT, C::BN, D, C::VS, C::NT>>::type;
   VStage vst;
-  DmaTile<C::BN, D, C::NT> dt;
-  const int pitch = int(ldk) * 2;
+  DmaTile<C::BN, C::kFp8 ? D / 2 : D, C::NT> dt;  // K (and bf16 V) tile loads
+  const int pitch = int(ldk) * C::EB;
   if constexpr (C::kDma) dt.init(pitch);
+  // fp8: this thread's 16-byte chunks of the next V tile, widened at commit_v
+  constexpr int NVC = C::kFp8 ? C::BN * (D / 16) / C::NT : 1;
+  u32x4 vreg[NVC];
   int32_t e_reg = 0, kv_reg = 0, w_reg = 0;
   int32_t qkey = 0;  // node form: this row's node number (0: a pad or past T)
   const int32_t* const ev = NODES ? p.nlo : p.end;
@@ -163,7 +176,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   // current sub-step's S product, where the MFMAs hide their issue cost.  Without a
   // next sub-step the descriptors cover 0 bytes and the loads only write zeros into
   // the idle buffer.
-  constexpr int NL = DmaTile<C::BN, D, C::NT>::N;  // loads per tile and wave
+  constexpr int NL = DmaTile<C::BN, C::kFp8 ? D / 2 : D, C::NT>::N;  // loads per tile, wave
+  constexpr int NDMA = C::kFp8 ? NL : 2 * NL;  // K and (bf16) V tile loads per stage
   DmaRsrc rk{}, rvv{};
   char* st_next = smem;
   auto dma_part = [&](int j) {
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
         dma_load16(rk, dt.voff[j], st_next + (j * (C::NT / 64) + w) * 1024);
       else
         dma_load16(rvv, dt.voff[j - NL],
-                   st_next + C::TILE_BYTES + ((j - NL) * (C::NT / 64) + w) * 1024);
+                   st_next + C::KT_BYTES + ((j - NL) * (C::NT / 64) + w) * 1024);
     }
   };
 
@@ -185,13 +199,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       char* st = smem + (n & 1) * C::STAGE_BYTES;
       st_next = st;
       rk = dma_rsrc(K + kv0 * ldk + koff, nvalid * pitch);
-      rvv = dma_rsrc(V + kv0 * ldk + koff, nvalid * pitch);
+      if constexpr (C::kFp8) {  // V into registers (rows past the end read 0)
+        const auto rs = buf_rsrc(V + kv0 * ldk + koff, nvalid * pitch);
+#pragma unroll
+        for (int it = 0; it < NVC; ++it) {
+          const int cidx = it * C::NT + int(threadIdx.x);
+          vreg[it] = buf_load16(rs, (cidx / (D / 16)) * pitch + (cidx % (D / 16)) * 16);
+        }
+      } else {
+        rvv = dma_rsrc(V + kv0 * ldk + koff, nvalid * pitch);
+      }
+      char* mw = st + C::KT_BYTES + C::VT_BYTES;
       if (wave == 0)  // keys past the end read end = 0 (or w = 0): never visible
-        dma_load4(dma_rsrc(ev + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
+        dma_load4(dma_rsrc(ev + kv0, nvalid * 4), lane * 4, mw);
       if constexpr (NODES)
-        if (wave == 1)
-          dma_load4(dma_rsrc(p.nw + kv0, nvalid * 4), lane * 4,
-                    st + 2 * C::TILE_BYTES + C::BN * 4);
+        if (wave == 1) dma_load4(dma_rsrc(p.nw + kv0, nvalid * 4), lane * 4, mw + C::BN * 4);
     } else {  // into registers; commit() stores them
       // mask words first: the loads retire in order, so waiting for them at commit
       // does not wait for the K/V reads issued after them
@@ -199,14 +221,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       e_reg = int32_t(buf_load4(buf_rsrc(ev + kv0, nvalid * 4), r * 4));
       if constexpr (NODES) w_reg = int32_t(buf_load4(buf_rsrc(p.nw + kv0, nvalid * 4), r * 4));
       kv_reg = r < nvalid ? int32_t(kv0 + r) : 0;
-      kst.load(K + kv0 * ldk + koff, ldk, nvalid);
-      vst.load(V + kv0 * ldk + koff, ldk, nvalid);
+      kst.load(reinterpret_cast<const RT*>(K) + kv0 * ldk + koff, ldk, nvalid);
+      vst.load(reinterpret_cast<const RT*>(V) + kv0 * ldk + koff, ldk, nvalid);
     }
   };
   auto commit = [&](int b) {  // registers -> LDS buffer b (register path)
     T* kb = buf0 + b * C::BUF_ELEMS;
-    kst.store(kb);
-    vst.store(kb + C::K_ELEMS);
+    kst.store(reinterpret_cast<RT*>(kb));
+    vst.store(reinterpret_cast<RT*>(kb + C::K_ELEMS));
     if (threadIdx.x < C::BN) {
       if constexpr (NODES) {  // lo | w
         es0[b * 2 * C::BN + threadIdx.x] = e_reg;
@@ -217,22 +239,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     }
   };
 
+  // fp8: the staged V chunks of the next sub-step, widened to bf16 into buffer b
+  auto commit_v = [&](int b) {
+    if constexpr (C::kFp8) {
+      char* vt = smem + b * C::STAGE_BYTES + C::KT_BYTES;
+#pragma unroll
+      for (int it = 0; it < NVC; ++it) {
+        const int cidx = it * C::NT + int(threadIdx.x);
+        const int r = cidx / (D / 16), cc = cidx % (D / 16);
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fp8x4_to_bf16(vreg[it][j], w[2 * j], w[2 * j + 1]);
+        *reinterpret_cast<u32x4*>(vt + swz_off<D / 8>(r, 2 * cc)) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(vt + swz_off<D / 8>(r, 2 * cc + 1)) =
+            u32x4{w[4], w[5], w[6], w[7]};
+      }
+    }
+  };
+
   if (n_steps > 0) {
     issue(0, int(entry(0) & 0x3fffffffu));
     if constexpr (C::kDma) {
 #pragma unroll
-      for (int j = 0; j < 2 * NL; ++j) dma_part(j);
+      for (int j = 0; j < NDMA; ++j) dma_part(j);
+      commit_v(0);
     } else {
       commit(0);
     }
   }
   {  // Q stays in registers; its loads overlap the first tile's
-    const T* qp = Q + (qrow * hq + h) * D + 8 * half;
+    if constexpr (C::kFp8) {  // lane half h: bytes 64 s + 32 h .. +32 of the row
+      const char* qp = reinterpret_cast<const char*>(Q + (qrow * hq + h) * D) + 32 * half;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = qvalid ? frag_load(qp + 16 * s) : frag_zero<T>();
+      for (int s = 0; s < NQF; ++s) {
+        u32x4 a = u32x4{0u, 0u, 0u, 0u}, bb = a;
+        if (qvalid) {
+          a = *reinterpret_cast<const u32x4*>(qp + 64 * s);
+          bb = *reinterpret_cast<const u32x4*>(qp + 64 * s + 16);
+        }
+        qf[s].v = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]),
+                        int(bb[0]), int(bb[1]), int(bb[2]), int(bb[3])};
+      }
+    } else {
+      const T* qp = Q + (qrow * hq + h) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[s] = qvalid ? frag_load(qp + 16 * s) : frag_zero<T>();
+    }
     if constexpr (NODES) qkey = qvalid ? p.nkey[qrow] : 0;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) mark_ready(qf[s]);
+    for (int s = 0; s < NQF; ++s) mark_ready(qf[s]);
     if constexpr (NODES) mark_ready(qkey);
   }
   if constexpr (!C::kDma) __syncthreads();
@@ -263,7 +318,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
     const T* Ks = buf0 + b * C::BUF_ELEMS;       // register-path buffer
     const T* Vs = Ks + C::K_ELEMS;
-    const int32_t* Es = C::kDma ? reinterpret_cast<const int32_t*>(st + 2 * C::TILE_BYTES)
+    const int32_t* Es = C::kDma ? reinterpret_cast<const int32_t*>(st + C::KT_BYTES + C::VT_BYTES)
                                 : es0 + b * C::MW * C::BN;
 
     // a partial tile's sub-step whose keys all come after this wave's rows holds no
@@ -273,7 +328,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     if (partial && p.causal && kv0i > wave_last) {
       if constexpr (C::kDma) {
 #pragma unroll
-        for (int j = 0; j < 2 * NL; ++j) dma_part(j);
+        for (int j = 0; j < NDMA; ++j) dma_part(j);
       }
     } else {
       // S^T = K Q^T for BN keys x 32 queries (this wave)
@@ -285,7 +340,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
 #pragma unroll
         for (int kb = 0; kb < C::BN / 32; ++kb) acc_s[kb] = zero16();
         const T* kr = Ks + l32 * C::KS + 8 * half;
-        if constexpr (C::kDma) {
+        if constexpr (C::kFp8) {
+          // every K fragment of the sub-step first (two 16-byte chunks of a row per
+          // lane: bytes 64 s + 32 h .. +32), then the MFMAs over 64 reduction indices
+          constexpr int NS = D / 64, NK = C::BN / 32;
+          Frag<fp8_t> kq[NS][NK];
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb) {
+              const u32x4 a = frag_load_swz<D / 16>(st, 32 * kb + l32, 4 * s + 2 * half).v;
+              const u32x4 bb = frag_load_swz<D / 16>(st, 32 * kb + l32, 4 * s + 2 * half + 1).v;
+              kq[s][kb].v = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]),
+                                  int(bb[0]), int(bb[1]), int(bb[2]), int(bb[3])};
+            }
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb) mma(acc_s[kb], kq[s][kb], qf[s]);
+            // the next stage's K tile loads, spread over these steps
+#pragma unroll
+            for (int j = 0; j < NDMA; ++j)
+              if ((j * NS) / NDMA == s) dma_part(j);
+          }
+        } else if constexpr (C::kDma) {
           // K fragments read PF reduction steps ahead of their MFMAs, so that LDS
           // latency overlaps the MFMAs in flight
           constexpr int NS = D / 16, NK = C::BN / 32, PF = 3;
@@ -416,11 +494,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
         // their MFMAs, so that LDS latency overlaps the MFMAs in flight (at d = 128
         // the compiler's own order of the reads is faster, at d = 256 this one)
         constexpr int NT16 = C::BN / 16, ND = D / 32, NI = NT16 * ND, PF = 3;
-        Frag<T> pfr[NT16];
+        Frag<PT> pfr[NT16];
 #pragma unroll
-        for (int t = 0; t < NT16; ++t) pfr[t] = frag_from<T>(&sv[t >> 1][(t & 1) * 8]);
-        const char* vst = st + C::TILE_BYTES;
-        Frag<T> va[PF];
+        for (int t = 0; t < NT16; ++t) pfr[t] = frag_from<PT>(&sv[t >> 1][(t & 1) * 8]);
+        const char* vst = st + C::KT_BYTES;
+        Frag<PT> va[PF];
 #pragma unroll
         for (int i = 0; i < PF - 1; ++i)
           va[i] = frag_load_tr_swz<D / 8>(vst, 16 * (i / ND), 32 * (i % ND));
@@ -441,12 +519,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       } else {
 #pragma unroll
         for (int t = 0; t < C::BN / 16; ++t) {
-          const Frag<T> pf = frag_from<T>(&sv[t >> 1][(t & 1) * 8]);
+          const Frag<PT> pf = frag_from<PT>(&sv[t >> 1][(t & 1) * 8]);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            Frag<T> va;
+            Frag<PT> va;
             if constexpr (C::kDma)
-              va = frag_load_tr_swz<D / 8>(st + C::TILE_BYTES, 16 * t, 32 * db);
+              va = frag_load_tr_swz<D / 8>(st + C::KT_BYTES, 16 * t, 32 * db);
             else if constexpr (C::kBf16)
               va = frag_load_tr(Vs, C::VS, 16 * t, 32 * db);
             else
@@ -457,6 +535,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       }
     }
 
+    if constexpr (C::kFp8) {  // the next sub-step's V, widened (the barrier at the top
+      if (n + 1 < n_steps) commit_v(b ^ 1);  // of the next step publishes it)
+    }
     if constexpr (!C::kDma) {
       if (n + 1 < n_steps) commit(b ^ 1);
       __syncthreads();
@@ -467,7 +548,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   const float lt = l + __shfl_xor(l, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qvalid) {
-    T* op = static_cast<T*>(p.o) + (qrow * hq + h) * D;
+    PT* op = static_cast<PT*>(p.o) + (qrow * hq + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -475,7 +556,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
         const int d = 32 * db + g * 8 + half * 4;
         vec4_store(op + d, vec4_from(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
                                      acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv,
-                                     static_cast<T*>(nullptr)));
+                                     static_cast<PT*>(nullptr)));
       }
     if (half == 0 && p.lse)  // no LSE store for a forward without gradient
       p.lse[int64_t(h) * ntok + qrow] =
@@ -522,7 +603,7 @@ hipError_t launch_fwd_t(const psa_tile_map& map, const AttnShape& s, const void*
 }  // namespace psa
 
 bool fwd_supported(psa_dtype dt, int32_t d) {
-  if (dt == PSA_BF16) return d == 64 || d == 128 || d == 256;
+  if (dt == PSA_BF16 || dt == PSA_FP8_E4M3) return d == 64 || d == 128 || d == 256;
   if (dt == PSA_FP32) return d == 64 || d == 128;
   return false;
 }
@@ -531,11 +612,18 @@ hipError_t launch_fwd(const psa_tile_map& map, psa_dtype dt, const AttnShape& s,
                       const void* q, const void* k, const void* v, void* o, float* lse,
                       hipStream_t stream) {
   using psa::bf16_t;
+  using psa::fp8_t;
   if (dt == PSA_BF16) {
     switch (s.d) {
       case 64: return psa::launch_fwd_t<bf16_t, 64>(map, s, q, k, v, o, lse, stream);
       case 128: return psa::launch_fwd_t<bf16_t, 128>(map, s, q, k, v, o, lse, stream);
       case 256: return psa::launch_fwd_t<bf16_t, 256>(map, s, q, k, v, o, lse, stream);
+    }
+  } else if (dt == PSA_FP8_E4M3) {
+    switch (s.d) {
+      case 64: return psa::launch_fwd_t<fp8_t, 64>(map, s, q, k, v, o, lse, stream);
+      case 128: return psa::launch_fwd_t<fp8_t, 128>(map, s, q, k, v, o, lse, stream);
+      case 256: return psa::launch_fwd_t<fp8_t, 256>(map, s, q, k, v, o, lse, stream);
     }
   } else {
     switch (s.d) {

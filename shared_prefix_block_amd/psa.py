@@ -22,7 +22,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpsa.so"
 _lib = None
 _lock = threading.Lock()
 
-PSA_FP32, PSA_BF16 = 0, 1
+PSA_FP32, PSA_BF16, PSA_FP8_E4M3 = 0, 1, 2
 PASS_FWD, PASS_BWD = 0, 1
 STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_LAYOUT",
           4: "PSA_ERR_DTYPE", 5: "PSA_ERR_UNSUPPORTED", 6: "PSA_ERR_MAP_MISMATCH",
@@ -129,7 +129,9 @@ def _dtype_code(dt: torch.dtype) -> int:
         return PSA_FP32
     if dt == torch.bfloat16:
         return PSA_BF16
-    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+    if dt == torch.float8_e4m3fn:
+        return PSA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {dt} (float32, bfloat16 or float8_e4m3fn)")
 
 
 def tile_shape(pass_: int, dtype: torch.dtype, d: int):
@@ -311,13 +313,21 @@ def _check_qkv(q, k, v):
 def fwd(m: TileMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None, with_lse: bool = True):
-    """O [T, hq, d] (q's dtype) and LSE [hq, T] float32.  with_lse=False: a forward
-    without gradient; no LSE is written and None is returned in its place."""
+    """O [T, hq, d] (q's dtype; bfloat16 for float8_e4m3fn inputs) and LSE [hq, T]
+    float32.  with_lse=False: a forward without gradient; no LSE is written and None is
+    returned in its place."""
     lib = load()
     _check_qkv(q, k, v)
     T, hq, d = q.shape
     hkv = k.shape[1]
-    o = torch.empty_like(q) if out is None else out
+    o_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    if out is None:
+        o = torch.empty(q.shape, device=q.device, dtype=o_dtype)
+    else:
+        if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous() \
+                or out.device != q.device:
+            raise ValueError(f"out must be a contiguous {o_dtype} tensor of q's shape and device")
+        o = out
     if not with_lse:
         lse_t = None
     else:

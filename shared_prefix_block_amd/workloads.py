@@ -362,7 +362,7 @@ def draft_layout(doc_lens: Sequence[int], block_size: int, blocks_per_doc,
 # ----------------------------------------------------------------------------
 # tensors
 # ----------------------------------------------------------------------------
-TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 
 def make_tensors(T: int, hq: int, hkv: int, d: int, dtype: str, sigma: float = 1.0,

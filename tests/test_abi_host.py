@@ -54,6 +54,11 @@ def test_tile_shape(lib):
     assert lib.psa_tile_shape(0, 1, 96, ctypes.byref(bm), ctypes.byref(bn)) == 5
     assert lib.psa_tile_shape(0, 0, 256, ctypes.byref(bm), ctypes.byref(bn)) == 5
     assert lib.psa_tile_shape(0, 7, 128, ctypes.byref(bm), ctypes.byref(bn)) == 4
+    # e4m3 inputs: forward only, at the bf16 head sizes
+    for d in (64, 128, 256):
+        assert lib.psa_tile_shape(0, 2, d, ctypes.byref(bm), ctypes.byref(bn)) == 0
+        assert lib.psa_tile_shape(1, 2, d, ctypes.byref(bm), ctypes.byref(bn)) == 5
+    assert lib.psa_tile_shape(0, 2, 96, ctypes.byref(bm), ctypes.byref(bn)) == 5
     assert lib.psa_tile_shape(0, 1, 128, None, ctypes.byref(bn)) == 1
 
 
