@@ -146,11 +146,11 @@ KERNEL_STAGE = {"fwd_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bw
 TRAFFIC_PASSES = ("FETCH_SIZE", "WRITE_SIZE")
 
 
-def traffic_summary(pmc_dir: str, workload: str, calib_mb: int, command: str) -> None:
-    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, each
-    with --calib-mb) into profiles/traffic_<stage>_<workload>.json, one per attention
-    kernel: the counters (KiB per dispatch) scaled so that the reference negation over
-    calib_mb MiB reads and writes exactly calib_mb MiB."""
+def traffic_from_pmc(pmc_dir: str, calib_mb: int) -> dict:
+    """Per attention stage: the kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
+    averaged over its dispatches) from the counter CSVs under pmc_dir, each with the
+    factor that makes the reference negation over calib_mb MiB read and write exactly
+    calib_mb MiB."""
     import csv
     import glob
 
@@ -184,12 +184,23 @@ def traffic_summary(pmc_dir: str, workload: str, calib_mb: int, command: str) ->
                     e = out.setdefault(stage, {"kernel": short})
                     e[counter + "_KiB"] = kib
                     e[counter + "_scale"] = factor
+    for e in out.values():
+        if all(c + "_KiB" in e for c in TRAFFIC_PASSES):
+            e["bytes_per_launch"] = int(sum(e[c + "_KiB"] * e[c + "_scale"] * 1024
+                                            for c in TRAFFIC_PASSES))
+    return out
+
+
+def traffic_summary(pmc_dir: str, workload: str, calib_mb: int, command: str) -> None:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, each
+    with --calib-mb) into profiles/traffic_<stage>_<workload>.json, one per attention
+    kernel (traffic_from_pmc)."""
+    out = traffic_from_pmc(pmc_dir, calib_mb)
     src_hash = kernel_source_hash()
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for stage, e in out.items():
-        if not all(c + "_KiB" in e for c in TRAFFIC_PASSES):
+        if "bytes_per_launch" not in e:
             continue
-        e["bytes_per_launch"] = int(sum(e[c + "_KiB"] * e[c + "_scale"] * 1024 for c in TRAFFIC_PASSES))
         e["kernel_source_hash"] = src_hash
         e["command"] = command
         path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")

@@ -1,0 +1,70 @@
+"""Host-side logic of bench.py (no GPU): the single-GPU guard and the HBM-traffic
+arithmetic that turns rocprofv3 counter CSVs into bytes per launch."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr
+
+
+def _write_pmc(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                           "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                 "Counter_Value"], r)))
+
+
+NEG = "void at::native::elementwise_kernel<128, 4, neg>(int, F)"
+DKDV = "void psa::(anonymous namespace)::dkdv_kernel<psa::bf16_t, float, 128, 0, 0, false>(BwdParams)"
+FWD = "void psa::(anonymous namespace)::fwd_kernel<psa::bf16_t, 128, false>(FwdParams)"
+FWD32 = "void psa::(anonymous namespace)::fwd_kernel<float, 64, false>(FwdParams)"
+
+
+def test_traffic_scaling_by_the_reference_copy(tmp_path):
+    """FETCH_SIZE reads half of the negation's 64 MiB (factor 2), WRITE_SIZE all of it
+    (factor 1); per-channel rows of one dispatch add up, dispatches of one kernel
+    average, fp32 variants are not attention traffic of the bf16 path."""
+    mib = 64
+    kib = mib * 1024.0
+    _write_pmc(str(tmp_path / "FETCH_SIZE" / "a" / "run_counter_collection.csv"), [
+        (1, NEG, "FETCH_SIZE", kib / 4), (1, NEG, "FETCH_SIZE", kib / 4),  # two channels
+        (2, DKDV, "FETCH_SIZE", 1000.0), (3, DKDV, "FETCH_SIZE", 3000.0),
+        (4, FWD, "FETCH_SIZE", 500.0), (5, FWD32, "FETCH_SIZE", 9.0),
+    ])
+    _write_pmc(str(tmp_path / "WRITE_SIZE" / "a" / "run_counter_collection.csv"), [
+        (1, NEG, "WRITE_SIZE", kib),
+        (2, DKDV, "WRITE_SIZE", 100.0), (3, DKDV, "WRITE_SIZE", 300.0),
+        (4, FWD, "WRITE_SIZE", 50.0),
+    ])
+    out = bench.traffic_from_pmc(str(tmp_path), mib)
+    assert set(out) == {"bwd_dkdv", "fwd"}
+    d = out["bwd_dkdv"]
+    assert d["kernel"] == "dkdv_kernel<bf16_t, float, 128, 0, 0, false>"
+    assert d["FETCH_SIZE_scale"] == pytest.approx(2.0)
+    assert d["WRITE_SIZE_scale"] == pytest.approx(1.0)
+    assert d["FETCH_SIZE_KiB"] == pytest.approx(2000.0)
+    assert d["bytes_per_launch"] == int((2000.0 * 2 + 200.0) * 1024)
+    assert out["fwd"]["bytes_per_launch"] == int((500.0 * 2 + 50.0) * 1024)
+
+
+def test_traffic_needs_the_reference_copy(tmp_path):
+    _write_pmc(str(tmp_path / "x" / "run_counter_collection.csv"),
+               [(1, DKDV, "FETCH_SIZE", 1.0), (1, DKDV, "WRITE_SIZE", 1.0)])
+    with pytest.raises(SystemExit, match="reference negation"):
+        bench.traffic_from_pmc(str(tmp_path), 64)
