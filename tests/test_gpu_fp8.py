@@ -131,7 +131,7 @@ def test_fp8_zero_query_closed_form():
         compare(f"o[{h}]", o[:, h], mean_v, BF, out_round=OUT_ROUND)
 
 
-@pytest.mark.parametrize("idx", [2, 4, 6])
+@pytest.mark.parametrize("idx", [2, 4, 5, 6])
 def test_fp8_workload_sampled(idx):
     """The workloads' full-size layouts in e4m3, at sampled rows and their boundaries."""
     cfg = wl.WORKLOADS[idx]
