@@ -304,10 +304,21 @@ def _check_qkv(q, k, v):
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
         if t.dtype != q.dtype:
             raise TypeError("q, k, v must share a dtype")
     if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
         raise ValueError("shape mismatch between q and k/v")
+
+
+def _check_buf(t: torch.Tensor, shape, dtype: torch.dtype, device, name: str) -> None:
+    """A caller-supplied buffer the kernels read or write whole: its shape, dtype,
+    layout and device must be the ones they assume."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape "
+                         f"{tuple(shape)} on {device}")
 
 
 def fwd(m: TileMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -324,14 +335,15 @@ def fwd(m: TileMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if out is None:
         o = torch.empty(q.shape, device=q.device, dtype=o_dtype)
     else:
-        if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous() \
-                or out.device != q.device:
-            raise ValueError(f"out must be a contiguous {o_dtype} tensor of q's shape and device")
+        _check_buf(out, q.shape, o_dtype, q.device, "out")
         o = out
     if not with_lse:
         lse_t = None
+    elif lse is None:
+        lse_t = torch.empty(hq, T, device=q.device, dtype=torch.float32)
     else:
-        lse_t = torch.empty(hq, T, device=q.device, dtype=torch.float32) if lse is None else lse
+        _check_buf(lse, (hq, T), torch.float32, q.device, "lse")
+        lse_t = lse
     with torch.cuda.device(q.device):
         _check(lib.psa_fwd(m.handle, _dtype_code(q.dtype), T, hq, hkv, d,
                            0.0 if scale is None else float(scale), _ptr(q), _ptr(k), _ptr(v),
@@ -358,23 +370,26 @@ def bwd(m: TileMap, q, k, v, o, lse, do, scale: Optional[float] = None,
     buffers."""
     lib = load()
     _check_qkv(q, k, v)
-    for t in (o, do):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("o and do must match q")
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [hq, T]")
     T, hq, d = q.shape
     hkv = k.shape[1]
+    _check_buf(o, q.shape, q.dtype, q.device, "o")
+    _check_buf(do, q.shape, q.dtype, q.device, "do")
+    _check_buf(lse, (hq, T), torch.float32, q.device, "lse")
     need = bwd_workspace_size(m, q, k)
     ws = workspace
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif not ws.is_contiguous() or ws.device != q.device:
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
     if out is None:
         dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
         dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
         dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
     else:
         dq, dk, dv = out
+        _check_buf(dq, q.shape, grad_dtype, q.device, "dq")
+        _check_buf(dk, k.shape, grad_dtype, q.device, "dk")
+        _check_buf(dv, v.shape, grad_dtype, q.device, "dv")
     with torch.cuda.device(q.device):
         _check(lib.psa_bwd_stages(m.handle, _dtype_code(q.dtype), _dtype_code(grad_dtype), T, hq,
                                   hkv, d, 0.0 if scale is None else float(scale), _ptr(q), _ptr(k),

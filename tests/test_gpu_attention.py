@@ -347,6 +347,22 @@ def test_map_mismatch_errors():
     with pytest.raises(psa.PsaError) as ei:
         psa.bwd(m, q, k, v, o, lse, do, workspace=small)
     assert ei.value.name == "PSA_ERR_WORKSPACE"
+    # caller buffers the kernels would read or write past: refused before any launch
+    with pytest.raises(ValueError, match="lse"):
+        psa.fwd(m, q, k, v, lse=torch.empty(2, lay.T - 1, device="cuda"))
+    with pytest.raises(ValueError, match="out"):
+        psa.fwd(m, q, k, v, out=torch.empty(q.shape, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match="lse"):
+        psa.bwd(m, q, k, v, o, lse[:1], do)
+    with pytest.raises(ValueError, match="dq"):
+        psa.bwd(m, q, k, v, o, lse, do, out=(torch.empty(q.shape, dtype=torch.bfloat16,
+                                                         device="cuda"),) + tuple(
+            torch.empty(k.shape, device="cuda") for _ in range(2)))
+    with pytest.raises(ValueError, match="workspace"):
+        psa.bwd(m, q, k, v, o, lse, do, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="do"):
+        psa.bwd(m, q, k, v, o, lse, do[:, :1].contiguous())
+    torch.cuda.synchronize()
 
 
 def test_autograd_wrapper():
