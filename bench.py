@@ -146,11 +146,11 @@ KERNEL_STAGE = {"fwd_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bw
 TRAFFIC_PASSES = ("FETCH_SIZE", "WRITE_SIZE")
 
 
-def traffic_from_pmc(pmc_dir: str, calib_mb: int) -> dict:
+def traffic_from_pmc(pmc_dir: str, calib_mb: int, dtype_tag: str = "bf16") -> dict:
     """Per attention stage: the kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
     averaged over its dispatches) from the counter CSVs under pmc_dir, each with the
     factor that makes the reference negation over calib_mb MiB read and write exactly
-    calib_mb MiB."""
+    calib_mb MiB.  Only kernels instantiated for dtype_tag ("bf16" or "fp8") count."""
     import csv
     import glob
 
@@ -178,7 +178,7 @@ def traffic_from_pmc(pmc_dir: str, calib_mb: int) -> dict:
         factor = ref_kib / max(calib)
         for name, kib in avg.items():
             for sym, stage in KERNEL_STAGE.items():
-                if sym in name and "bf16" in name:
+                if sym in name and f"{dtype_tag}_t" in name:
                     short = name.replace("void ", "").replace("(anonymous namespace)::", "")
                     short = short.replace("psa::", "").rsplit("(", 1)[0]
                     e = out.setdefault(stage, {"kernel": short})
@@ -191,11 +191,13 @@ def traffic_from_pmc(pmc_dir: str, calib_mb: int) -> dict:
     return out
 
 
-def traffic_summary(pmc_dir: str, workload: str, calib_mb: int, command: str) -> None:
+def traffic_summary(pmc_dir: str, workload: str, calib_mb: int, command: str,
+                    nograd: str = "") -> None:
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, each
-    with --calib-mb) into profiles/traffic_<stage>_<workload>.json, one per attention
-    kernel (traffic_from_pmc)."""
-    out = traffic_from_pmc(pmc_dir, calib_mb)
+    with --calib-mb) into profiles/traffic_<stage>[_nograd_<dtype>]_<workload>.json, one
+    per attention kernel (traffic_from_pmc)."""
+    out = traffic_from_pmc(pmc_dir, calib_mb, "fp8" if nograd == "fp8" else "bf16")
+    variant = f"_nograd_{nograd}" if nograd else ""
     src_hash = kernel_source_hash()
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for stage, e in out.items():
@@ -203,7 +205,7 @@ def traffic_summary(pmc_dir: str, workload: str, calib_mb: int, command: str) ->
             continue
         e["kernel_source_hash"] = src_hash
         e["command"] = command
-        path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+        path = os.path.join(ROOT, "profiles", f"traffic_{stage}{variant}_{workload}.json")
         with open(path, "w") as fh:
             json.dump(e, fh, indent=1)
         print(path, e["bytes_per_launch"])
@@ -301,8 +303,7 @@ def main():
     if args.traffic_summary:
         from shared_prefix_block_amd import workloads as wl
         traffic_summary(args.traffic_summary, wl.WORKLOADS[args.workload].name,
-                        args.calib_mb or 512,
-                        args.traffic_command)
+                        args.calib_mb or 512, args.traffic_command, args.nograd or "")
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -34,6 +34,7 @@ NEG = "void at::native::elementwise_kernel<128, 4, neg>(int, F)"
 DKDV = "void psa::(anonymous namespace)::dkdv_kernel<psa::bf16_t, float, 128, 0, 0, false>(BwdParams)"
 FWD = "void psa::(anonymous namespace)::fwd_kernel<psa::bf16_t, 128, false>(FwdParams)"
 FWD32 = "void psa::(anonymous namespace)::fwd_kernel<float, 64, false>(FwdParams)"
+FWD8 = "void psa::(anonymous namespace)::fwd_kernel<psa::fp8_t, 128, false>(FwdParams)"
 
 
 def test_traffic_scaling_by_the_reference_copy(tmp_path):
@@ -61,6 +62,19 @@ def test_traffic_scaling_by_the_reference_copy(tmp_path):
     assert d["FETCH_SIZE_KiB"] == pytest.approx(2000.0)
     assert d["bytes_per_launch"] == int((2000.0 * 2 + 200.0) * 1024)
     assert out["fwd"]["bytes_per_launch"] == int((500.0 * 2 + 50.0) * 1024)
+
+
+def test_traffic_of_the_e4m3_forward(tmp_path):
+    """With dtype_tag fp8 only the e4m3 kernels count."""
+    kib = 64 * 1024.0
+    _write_pmc(str(tmp_path / "F" / "run_counter_collection.csv"), [
+        (1, NEG, "FETCH_SIZE", kib / 2), (2, FWD8, "FETCH_SIZE", 300.0),
+        (3, FWD, "FETCH_SIZE", 500.0), (1, NEG, "WRITE_SIZE", kib),
+        (2, FWD8, "WRITE_SIZE", 40.0), (3, FWD, "WRITE_SIZE", 50.0)])
+    out = bench.traffic_from_pmc(str(tmp_path), 64, "fp8")
+    assert set(out) == {"fwd"}
+    assert out["fwd"]["kernel"] == "fwd_kernel<fp8_t, 128, false>"
+    assert out["fwd"]["bytes_per_launch"] == int((300.0 * 2 + 40.0) * 1024)
 
 
 def test_traffic_needs_the_reference_copy(tmp_path):
