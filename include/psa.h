@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PSA_ABI_VERSION 4
+#define PSA_ABI_VERSION 5  /* 5: PSA_FP8_E4M3 forward */
 
 typedef enum {
   PSA_OK = 0,

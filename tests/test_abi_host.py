@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.psa_abi_version() == 4
+    assert lib.psa_abi_version() == 5
     for code, name in psa.STATUS.items():
         s = lib.psa_status_string(code).decode()
         assert s and s != "unknown status", name
