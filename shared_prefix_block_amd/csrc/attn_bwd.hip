@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const int hk = int(w_id % hkv);
   const int kt = p.korder[w_id / hkv];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t kvrow = int64_t(kt) * C::BK + 32 * wave + l32;
   const bool kvvalid = kvrow < ntok;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   char* st_next = smem;
   auto dma_part = [&](int j) {
     if constexpr (C::kDma) {
-      const int w = threadIdx.x >> 6;
+      const int w = wave;
       if (j < NT_LOADS)
         dma_load16(rq, dt.voff[j], st_next + (j * (C::NT / 64) + w) * 1024);
       else
@@ -643,7 +643,7 @@ void dq_kernel(BwdParams p) {
   const int qt = p.qorder[w_id / hq];
   const int hk = h / rep;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t qrow = int64_t(qt) * C::BM + 32 * wave + l32;
   const int wave_last = qt * C::BM + 32 * wave + 31;  // this wave's last row

@@ -44,6 +44,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// The wave's index in its work-group, as a wave-uniform (scalar) value: addresses and
+// branches derived from it then stay in scalar registers.  (The backward kernels and
+// DmaTile::load take it; in the forward it measured slower: the compiler schedules
+// that loop differently.)
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+}
+
 // ---------------------------------------------------------------------------
 // fragments
 // ---------------------------------------------------------------------------
@@ -529,7 +537,7 @@ struct DmaTile {
   __device__ __forceinline__ void load(const void* src, int nvalid, int pitch_bytes,
                                        char* dst) const {
     const DmaRsrc rs = dma_rsrc(src, nvalid * pitch_bytes);
-    const int w = threadIdx.x >> 6;
+    const int w = wave_id();
 #pragma unroll
     for (int j = 0; j < N; ++j) dma_load16(rs, voff[j], dst + (j * NW + w) * 1024);
   }
