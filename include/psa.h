@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PSA_ABI_VERSION 5  /* 5: PSA_FP8_E4M3 forward */
+#define PSA_ABI_VERSION 6  /* 5: PSA_FP8_E4M3 forward; 6: psa_unfold_rows takes dst_bytes */
 
 typedef enum {
   PSA_OK = 0,
@@ -223,6 +223,14 @@ void psa_tile_map_destroy(psa_tile_map* map);
 
 /*
  * Forward: O = softmax(scale * Q K^T masked) V per q head, and LSE.
+ * Defined by unsloth "prefix_grouper_kernel.py": flex_shared_prefix_attention (the
+ * call: Q, K, V and the block mask; GQA through enable_gqa; the default scale
+ * 1/sqrt(head_dim) of _run_flex) with the mask of _make_mask_mod; its module docstring
+ * (masked blocks are skipped) and the comment on the flash block sizes (a completion
+ * row's prompt run and own run go through one softmax).  The result is the dense
+ * masked softmax of that definition; the block skipping only leaves out tiles whose
+ * every pair is masked.
+ * Supported: d in {64, 128, 256} for PSA_FP32 and PSA_BF16 (and PSA_FP8_E4M3 here).
  * Device pointers: q, k, v (inputs), o, lse (outputs, fully overwritten).  lse may be
  * NULL for a forward whose LSE is not needed (no backward follows, e.g. the extra
  * no-grad log-prob passes of a policy-gradient step): then only O is written.
@@ -244,7 +252,12 @@ psa_status psa_bwd_workspace_size(const psa_tile_map* map, psa_dtype dtype, int6
 
 /*
  * Backward (FlashAttention-2 style): dQ, dK, dV of sum(dO * O) given the forward's
- * O and LSE.  dK and dV sum over the q heads that share a kv head.  Device pointers:
+ * O and LSE.  The pages give no backward of their own: the unsloth page's
+ * flex_shared_prefix_attention is differentiated by autograd, so this is the exact
+ * gradient of the forward above (the analytic softmax-attention gradient,
+ * dS = P * (dP - rowsum(dO * O)), restricted to the kept pairs).  dK and dV sum over
+ * the q heads that share a kv head (the gradient of enable_gqa).  Supported: d in
+ * {64, 128, 256} for PSA_FP32 and PSA_BF16.  Device pointers:
  * q, k, v, o, lse, dout (inputs, element type `dtype`), dq, dk, dv (outputs, element
  * type `grad_dtype`, fully overwritten), workspace (caller-owned scratch of at least
  * psa_bwd_workspace_size bytes, contents undefined on entry and exit).
@@ -321,7 +334,8 @@ psa_status psa_bwd_stages(const psa_tile_map* map, psa_dtype dtype, psa_dtype gr
  *     entry and exit; the call uploads its segment table there, on `stream`).
  * Asynchronous on `stream`.  Errors (nothing is launched): PSA_ERR_NULL, PSA_ERR_SHAPE (T
  * too short or out of range), PSA_ERR_LAYOUT (negative lengths, comp_ptr not starting
- * at 0 or decreasing), PSA_ERR_WORKSPACE, PSA_ERR_HIP.
+ * at 0 or decreasing), PSA_ERR_WORKSPACE, PSA_ERR_VALUE (a capturing stream),
+ * PSA_ERR_HIP.
  */
 psa_status psa_fold_workspace_size(int64_t n_groups, int64_t n_comp, size_t* bytes);
 psa_status psa_fold_rollouts(int64_t n_groups, const int32_t* prompt_len,
@@ -340,13 +354,18 @@ psa_status psa_fold_rollouts(int64_t n_groups, const int32_t* prompt_len,
  * sum over completions of (P_g + R_gi) rows.  A group without completions gives no
  * sample.  row_bytes: a positive multiple of 4 (rows move as 16-byte words when
  * row_bytes, src and dst allow it).  Device pointers src, dst (4-byte aligned);
- * workspace as psa_fold_rollouts.  Asynchronous on `stream`.  Errors as
+ * dst_bytes: the bytes dst holds (at least the unfolded rows times row_bytes, else
+ * PSA_ERR_SHAPE); workspace as psa_fold_rollouts.  Asynchronous on `stream`.  Errors as
  * psa_fold_rollouts.
+ *
+ * Fold and unfold copy their segment table from library-owned pinned host memory to
+ * the workspace on `stream`; they refuse a stream that is being captured into a graph
+ * (PSA_ERR_VALUE), since a replay would copy that host memory again.
  */
 psa_status psa_unfold_rows(int64_t n_groups, const int32_t* prompt_len,
                            const int32_t* comp_ptr, const int32_t* comp_len, int64_t T,
-                           int64_t row_bytes, const void* src, void* dst, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           int64_t row_bytes, const void* src, void* dst, size_t dst_bytes,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -162,21 +162,30 @@ def grad_rows(meta, q, k, v, do, rows: Sequence[int], scale: Optional[float] = N
 
 
 def grad_cols(meta, q, k, v, do, cols: Sequence[int], scale: Optional[float] = None,
-              block_rows: int = 512):
-    """(dK, dV) of the listed key/value rows only.
+              block_rows: int = 512, kv_heads: Optional[Sequence[int]] = None):
+    """(dK, dV) of the listed key/value rows only, [len(cols), hkv, d] each, or
+    [len(cols), len(kv_heads), d] for the listed kv heads alone (then only the q heads
+    that read those kv heads are computed).
 
     Each listed column needs, for every row that sees it, that row's full softmax
-    (LSE) and D = rowsum(dO * O); those rows are recomputed densely over their
-    group, and only the listed columns of dS and P are reduced."""
+    (LSE) and D = rowsum(dO * O); those rows are recomputed over their group, and only
+    the listed columns of dS and P are reduced.  A block of rows is taken over the
+    columns of its group that at least one of its rows sees: every other column is
+    masked for the whole block, so its scores are -inf, its probabilities 0, and it
+    adds nothing to any sum (the same reason the groups are taken one at a time)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     T, hq, d = q.shape
     hkv = k.shape[1]
     rep = hq // hkv
     sc = _scale(d, scale)
+    heads = list(range(hkv)) if kv_heads is None else [int(x) for x in kv_heads]
+    if any(not 0 <= x < hkv for x in heads) or len(set(heads)) != len(heads):
+        raise ValueError("kv_heads must be distinct kv head indices")
+    slot = {hk: i for i, hk in enumerate(heads)}
     sel = np.asarray(cols, dtype=np.int64)
     pos = {int(c): i for i, c in enumerate(sel)}
-    dk = np.zeros((len(sel), hkv, d))
-    dv = np.zeros((len(sel), hkv, d))
+    dk = np.zeros((len(sel), len(heads), d))
+    dv = np.zeros((len(sel), len(heads), d))
     for comp in meta.components():
         want = np.intersect1d(comp, sel)
         if len(want) == 0:
@@ -188,18 +197,25 @@ def grad_cols(meta, q, k, v, do, cols: Sequence[int], scale: Optional[float] = N
             blk = comp[b0:b0 + 4096]
             need.append(blk[meta.mask(blk, want).any(axis=1)])
         need = np.concatenate(need) if need else np.zeros(0, np.int64)
-        wpos = np.searchsorted(comp, want)
-        for h in range(hq):
-            hk = h // rep
-            kc, vc = k[comp, hk], v[comp, hk]
-            for b0 in range(0, len(need), block_rows):
-                blk = need[b0:b0 + block_rows]
-                p, _, _ = _softmax_block(meta, blk, comp, q[blk, h], kc, sc)
+        for b0 in range(0, len(need), block_rows):
+            blk = need[b0:b0 + block_rows]
+            cc = comp[meta.mask(blk, comp).any(axis=0)]  # columns some row of blk sees
+            seen = np.isin(want, cc)  # listed columns no row of blk sees get nothing here
+            if not seen.any():
+                continue
+            wpos = np.searchsorted(cc, want[seen])
+            ow = oi[seen]
+            for h in range(hq):
+                hk = h // rep
+                if hk not in slot:
+                    continue
+                kc, vc = k[cc, hk], v[cc, hk]
+                p, _, _ = _softmax_block(meta, blk, cc, q[blk, h], kc, sc)
                 ob = p @ vc
                 dob = do[blk, h]
                 dd = (dob * ob).sum(axis=1)
                 pw = p[:, wpos]
                 dsw = pw * (dob @ vc[wpos].T - dd[:, None])
-                dk[oi, hk] += sc * (dsw.T @ q[blk, h])
-                dv[oi, hk] += pw.T @ dob
+                dk[ow, slot[hk]] += sc * (dsw.T @ q[blk, h])
+                dv[ow, slot[hk]] += pw.T @ dob
     return dk, dv

@@ -867,14 +867,80 @@ size_t fold_table_bytes(int64_t n_groups, int64_t n_comp) {
   return align_up(std::max<size_t>(std::max(fold, unfold), 1), 256);
 }
 
+// Host staging of the segment tables: library-owned pinned buffers.  A buffer is
+// handed out again only once the copy that last read it has completed (an event
+// recorded after that copy), so the caller's table can be a temporary and the copy is
+// a true asynchronous DMA.  The copy reads host memory when it runs, which a captured
+// graph would repeat on every replay: fold and unfold refuse stream capture.
+struct Staging {
+  void* h = nullptr;
+  size_t bytes = 0;
+  hipEvent_t ev = nullptr;
+};
+std::mutex g_stage_mu;
+std::vector<Staging> g_stage;
+constexpr size_t kStageCount = 4;
+
+psa_status check_not_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return psa_hip_error(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return psa_set_error(PSA_ERR_VALUE,
+                         "fold / unfold upload a host table and cannot be captured in a graph");
+  return PSA_OK;
+}
+
 template <typename S>
 psa_status upload_table(const std::vector<S>& table, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   const size_t need = table.size() * sizeof(S);
   if (!workspace || workspace_bytes < need)
     return psa_set_error(PSA_ERR_WORKSPACE, "workspace smaller than psa_fold_workspace_size");
-  hipError_t e = hipMemcpyAsync(workspace, table.data(), need, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return psa_hip_error(e, "segment table upload");
+  psa_status st = check_not_capturing(stream);
+  if (st != PSA_OK) return st;
+  std::lock_guard<std::mutex> lock(g_stage_mu);
+  // a buffer whose last copy is done (the smallest one that fits), else a new one,
+  // else wait for the first
+  int pick = -1;
+  for (size_t i = 0; i < g_stage.size(); ++i) {
+    const Staging& b = g_stage[i];
+    if (b.bytes < need) continue;
+    if (b.ev && hipEventQuery(b.ev) != hipSuccess) continue;
+    if (pick < 0 || b.bytes < g_stage[pick].bytes) pick = int(i);
+  }
+  hipError_t e = hipSuccess;
+  if (pick < 0) {
+    if (g_stage.size() < kStageCount) {
+      g_stage.push_back(Staging{});
+      pick = int(g_stage.size()) - 1;
+    } else {
+      pick = 0;
+      if (g_stage[0].ev && (e = hipEventSynchronize(g_stage[0].ev)) != hipSuccess)
+        return psa_hip_error(e, "segment table staging wait");
+    }
+  }
+  (void)hipGetLastError();  // a query of an unfinished event leaves hipErrorNotReady
+  Staging& b = g_stage[pick];
+  if (b.bytes < need) {
+    if (b.h) (void)hipHostFree(b.h);
+    b.h = nullptr;
+    b.bytes = 0;
+    const size_t bytes = align_up(std::max<size_t>(need, 1), 4096);
+    if ((e = hipHostMalloc(&b.h, bytes, hipHostMallocPortable)) != hipSuccess) {
+      b.h = nullptr;
+      return psa_hip_error(e, "pinned staging allocation");
+    }
+    b.bytes = bytes;
+  }
+  if (!b.ev && (e = hipEventCreateWithFlags(&b.ev, hipEventDisableTiming)) != hipSuccess) {
+    b.ev = nullptr;
+    return psa_hip_error(e, "staging event");
+  }
+  std::memcpy(b.h, table.data(), need);
+  if ((e = hipMemcpyAsync(workspace, b.h, need, hipMemcpyHostToDevice, stream)) != hipSuccess ||
+      (e = hipEventRecord(b.ev, stream)) != hipSuccess)
+    return psa_hip_error(e, "segment table upload");
   return PSA_OK;
 }
 
@@ -951,8 +1017,8 @@ psa_status psa_fold_rollouts(int64_t n_groups, const int32_t* prompt_len, const 
 
 psa_status psa_unfold_rows(int64_t n_groups, const int32_t* prompt_len, const int32_t* comp_ptr,
                            const int32_t* comp_len, int64_t T, int64_t row_bytes,
-                           const void* src, void* dst, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           const void* src, void* dst, size_t dst_bytes, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   Rollouts r;
   psa_status st = check_rollouts(n_groups, prompt_len, comp_ptr, comp_len, &r);
   if (st != PSA_OK) return st;
@@ -980,6 +1046,10 @@ psa_status psa_unfold_rows(int64_t n_groups, const int32_t* prompt_len, const in
     }
     flat = c_start;
   }
+  if (uint64_t(out) * uint64_t(row_bytes) > dst_bytes)
+    return psa_set_error(PSA_ERR_SHAPE, "dst holds " + std::to_string(dst_bytes) +
+                                            " bytes, the unfolded rows take " +
+                                            std::to_string(out * row_bytes));
   if (segs.empty()) return PSA_OK;
   const bool w16 = row_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(dst) % 16 == 0;

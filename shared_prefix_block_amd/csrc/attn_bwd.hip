@@ -59,6 +59,7 @@ struct BwdParams {
   float scale;  // softmax scale
   int64_t n_work;
   int32_t chunk;
+  int32_t c0;  // first output column of a launch that accumulates a column slice
 };
 
 // ---------------------------------------------------------------------------
@@ -128,9 +129,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // sub-steps (CSC entries x q heads of the group x BMS-row slices) are staged in a
 // double-buffered LDS pipeline.  bf16 needs only row-major Q and dO tiles: the
 // transposed operands of dV^T += dO^T P and dK^T += Q^T dS come from the LDS
-// transpose read.  fp32 stages transposed copies instead.
+// transpose read.  fp32 stages transposed copies instead, and only the tiles its
+// PART uses; where two buffers would not fit in LDS (fp32, d = 256) it stages one.
+// CS > 1 (fp32, d = 256) splits the accumulated output into CS column slices, one
+// per launch (columns c0 .. c0 + D / CS - 1), so that K, V and the accumulators fit.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool NODES>
+template <typename T, int D, bool NODES, int PART = 0, int CS = 1>
 struct DkdvCfg {
   static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static constexpr int NW = 4;
@@ -144,29 +148,40 @@ struct DkdvCfg {
   // through the transpose read; a 32-byte pad keeps both free of bank conflicts
   static constexpr int NS = D + (kBf16 ? 32 : 16) / EB;
   static constexpr int TS = BMS + 16 / EB;  // transposed tile stride (fp32 only)
+  static constexpr bool kDV = PART != 2, kDK = PART != 1;
+  static constexpr int DC = D / CS;  // accumulated output columns per launch
   static constexpr int N_ELEMS = BMS * NS;
-  static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
-  static constexpr int BUF_ELEMS = 2 * (N_ELEMS + T_ELEMS);
+  static constexpr int T_ELEMS = kBf16 ? 0 : DC * TS;
+  // register-path buffer (fp32): Q | dO (for dP) | Q^T (for dK) | dO^T (for dV)
+  static constexpr int OFF_G = N_ELEMS;
+  static constexpr int OFF_QT = OFF_G + (kDK ? N_ELEMS : 0);
+  static constexpr int OFF_GT = OFF_QT + (kDK ? T_ELEMS : 0);
+  static constexpr int BUF_ELEMS = OFF_GT + (kDV ? T_ELEMS : 0);
   // bf16: Q | dO | L2 | D (| node numbers) stages filled by direct-to-LDS loads into
   // swizzled, unpadded tiles (as the forward's K and V); fp32: through registers.
   static constexpr bool kDma = kBf16;
   static constexpr int LW = NODES ? 3 : 2;  // per-row words: L2, D (, key)
   static constexpr int TILE_BYTES = BMS * D * 2;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES + LW * BMS * 4;
-  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * LW * BMS * 4;
+  static constexpr int NBUF = 2 * BUF_ELEMS * EB + 2 * LW * BMS * 4 <= kLdsMax ? 2 : 1;
+  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : NBUF * BUF_ELEMS * EB + 2 * LW * BMS * 4;
+  static_assert(CS == 1 || !kDma, "column slices exist on the register path only");
+  static_assert(LDS_BYTES <= kLdsMax, "LDS");
 };
 
 // PART: 0 computes dK and dV together; 1 only dV, 2 only dK.  At d = 256 K, V and
 // both accumulators do not fit one wave's registers, so the pair is split into two
-// passes (dV: S and P only; dK: S, dP and dS), at the price of recomputing S.
-template <typename T, typename G, int D, int MODE, int PART, bool NODES>
+// passes (dV: S and P only; dK: S, dP and dS), at the price of recomputing S; fp32
+// inputs take the two passes from d = 128 on (room for their partial sums).
+template <typename T, typename G, int D, int MODE, int PART, bool NODES, int CS = 1>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
-  using C = DkdvCfg<T, D, NODES>;
-  constexpr bool kDV = PART != 2, kDK = PART != 1;
-  static_assert(PART == 0 || C::kDma, "split passes exist on the DMA path only");
+  using C = DkdvCfg<T, D, NODES, PART, CS>;
+  constexpr bool kDV = C::kDV, kDK = C::kDK;
+  constexpr int DC = C::DC;
+  constexpr bool kSingle = !C::kDma && C::NBUF == 1;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   T* const buf0 = reinterpret_cast<T*>(smem);
-  float* const ld0 = reinterpret_cast<float*>(smem + 2 * C::BUF_ELEMS * C::EB);  // [2][LW][BMS]
+  float* const ld0 = reinterpret_cast<float*>(smem + C::NBUF * C::BUF_ELEMS * C::EB);  // [2][LW][BMS]
 
   const int64_t w_id = xcd_remap(blockIdx.x, p.chunk);
   if (w_id >= p.n_work) return;
@@ -195,12 +210,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const T* Gg = static_cast<const T*>(p.dout);
 
   Frag<T> kf[D / 16], vf[D / 16];  // loaded below, once the first tile's loads are in flight
-  f32x16 adk[D / 32], adv[D / 32];
+  f32x16 adk[DC / 32], adv[DC / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < DC / 32; ++db) {
     adk[db] = zero16();
     adv[db] = zero16();
   }
+  const int c0 = CS > 1 ? p.c0 : 0;
   const float c = p.c;
   const int64_t ldq = int64_t(hq) * D;
 
@@ -247,7 +263,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   mark_ready(*reinterpret_cast<int32_t*>(&wreg));
 
   RowStage<T, C::BMS, D, C::NS, C::NT> qst, gst;
-  using TStage = TransStage<T, C::BMS, D, C::TS, C::NT>;
+  using TStage = TransStage<T, C::BMS, DC, C::TS, C::NT>;
   typename std::conditional<C::kBf16, int, TStage>::type qtst, gtst;
   float l2_reg = INFINITY, dl_reg = 0.f;
   int32_t qk_reg = 0;
@@ -304,20 +320,20 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         l2_valid = rr < nvalid;
       }
       qst.load(qp, ldq, nvalid);
-      gst.load(gp, ldq, nvalid);
+      if constexpr (kDK) gst.load(gp, ldq, nvalid);
       if constexpr (!C::kBf16) {
-        qtst.load(qp, ldq, nvalid);
-        gtst.load(gp, ldq, nvalid);
+        if constexpr (kDK) qtst.load(qp + c0, ldq, nvalid);
+        if constexpr (kDV) gtst.load(gp + c0, ldq, nvalid);
       }
     }
   };
   auto commit = [&](int b) {  // register path
     T* base = buf0 + b * C::BUF_ELEMS;
     qst.store(base);
-    gst.store(base + C::N_ELEMS);
+    if constexpr (kDK) gst.store(base + C::OFF_G);
     if constexpr (!C::kBf16) {
-      qtst.store(base + 2 * C::N_ELEMS);
-      gtst.store(base + 2 * C::N_ELEMS + C::T_ELEMS);
+      if constexpr (kDK) qtst.store(base + C::OFF_QT);
+      if constexpr (kDV) gtst.store(base + C::OFF_GT);
     }
     if (threadIdx.x < C::BMS) {
       ld0[(b * C::LW + 0) * C::BMS + threadIdx.x] = l2_valid ? l2_reg : INFINITY;
@@ -359,7 +375,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   if constexpr (!C::kDma) __syncthreads();
 
   for (int n = 0; n < n_steps; ++n) {
-    const int b = n & 1;
+    const int b = kSingle ? 0 : n & 1;
     if constexpr (C::kDma) {
       // this wave's loads of stage n are in; after the barrier everyone's are, and
       // every wave is done with stage n - 1, which the next issue overwrites
@@ -375,7 +391,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         window_load(nxt.e - e0);
         mark_ready(*reinterpret_cast<int32_t*>(&wreg));
       }
-      issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu));
+      // one buffer: the next sub-step is staged after this one's math
+      if constexpr (!kSingle) issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu));
     } else if constexpr (C::kDma) {
       st_next = smem + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
       rq = dma_rsrc(Qg, 0);
@@ -384,9 +401,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 
     const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
     const T* Qs = buf0 + b * C::BUF_ELEMS;       // register-path buffer
-    const T* Gs = Qs + C::N_ELEMS;
-    const T* Qt = Qs + 2 * C::N_ELEMS;
-    const T* Gt = Qt + C::T_ELEMS;
+    const T* Gs = Qs + C::OFF_G;
+    const T* Qt = Qs + C::OFF_QT;
+    const T* Gt = Qs + C::OFF_GT;
     const float* Ls = C::kDma ? reinterpret_cast<const float*>(st + 2 * C::TILE_BYTES)
                               : ld0 + (b * C::LW + 0) * C::BMS;
     const float* Dsh = Ls + C::BMS;
@@ -445,7 +462,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int s = 0; s < D / 16; ++s) {
             mma(sacc, frag_load(qr + 16 * s), kf[s]);
-            mma(pacc, frag_load(gr + 16 * s), vf[s]);
+            if constexpr (kDK) mma(pacc, frag_load(gr + 16 * s), vf[s]);
           }
         }
         float pv[16], ds[16];
@@ -533,38 +550,42 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
             }
           }
         } else {
+          // fp32: dV += dO^T P and dK += Q^T dS over these 32 queries (two 16-query
+          // fragments t).  The products go into fresh blocks that are then added to the
+          // accumulators: a key seen by ~10^3 rows would otherwise take ~10^3 MFMA
+          // steps in one chain, each rounding at the magnitude of the running sum; per
+          // 32 queries the sum rounds there once.
+          Frag<T> pf[2], sf[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          // dV += dO^T P and dK += Q^T dS over these 16 queries: P and dS rounded to
-          // the MFMA type, then, where split_wanted, the residuals in a second pass
-          auto products = [&](const Frag<T>& pf, const Frag<T>& sf) {
+          for (int t = 0; t < 2; ++t) {
+            if constexpr (kDV) pf[t] = frag_from<T>(pv + 8 * t);
+            if constexpr (kDK) sf[t] = frag_from<T>(ds + 8 * t);
+          }
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              Frag<T> ga, qa;
-              if constexpr (C::kDma) {
-                ga = frag_load_tr_swz<D / 8>(st + C::TILE_BYTES, 32 * qb + 16 * t, 32 * db);
-                qa = frag_load_tr_swz<D / 8>(st, 32 * qb + 16 * t, 32 * db);
-              } else if constexpr (C::kBf16) {
-                ga = frag_load_tr(Gs, C::NS, 32 * qb + 16 * t, 32 * db);
-                qa = frag_load_tr(Qs, C::NS, 32 * qb + 16 * t, 32 * db);
-              } else {
-                const int col0 = 32 * qb + 16 * t + 8 * half;
-                ga = frag_load(Gt + (32 * db + l32) * C::TS + col0);
-                qa = frag_load(Qt + (32 * db + l32) * C::TS + col0);
-              }
-              mma(adv[db], ga, pf);
-              mma(adk[db], qa, sf);
+          for (int db = 0; db < DC / 32; ++db) {
+            f32x16 pvp = zero16(), pkp = zero16();
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int col0 = 32 * qb + 16 * t + 8 * half;
+              if constexpr (kDV) mma(pvp, frag_load(Gt + (32 * db + l32) * C::TS + col0), pf[t]);
+              if constexpr (kDK) mma(pkp, frag_load(Qt + (32 * db + l32) * C::TS + col0), sf[t]);
             }
-          };
-          const Frag<T> pf = frag_from<T>(pv + 8 * t), sf = frag_from<T>(ds + 8 * t);
-          products(pf, sf);
-          if (split_wanted<T, MODE, true>(pv + 8 * t, ds + 8 * t))
-            products(frag_residual(pv + 8 * t, pf), frag_residual(ds + 8 * t, sf));
-        }
+            if constexpr (kDV) adv[db] += pvp;
+            if constexpr (kDK) adk[db] += pkp;
+            // one column block's partial sums at a time (registers)
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
-    if constexpr (!C::kDma) {
+    if constexpr (kSingle) {  // every wave is done with the buffer: stage the next step
+      if (n + 1 < n_steps) {
+        __syncthreads();
+        issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu));
+        commit(0);
+      }
+      __syncthreads();
+    } else if constexpr (!C::kDma) {
       if (n + 1 < n_steps) commit(b ^ 1);
       __syncthreads();
     }
@@ -573,11 +594,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   if constexpr (C::kDma) wait_vmcnt<0>();  // no load into LDS outlives the work-group
 
   if (kvvalid) {
-    G* dkp = static_cast<G*>(p.dk) + (kvrow * hkv + hk) * D;
-    G* dvp = static_cast<G*>(p.dv) + (kvrow * hkv + hk) * D;
+    G* dkp = static_cast<G*>(p.dk) + (kvrow * hkv + hk) * D + c0;
+    G* dvp = static_cast<G*>(p.dv) + (kvrow * hkv + hk) * D + c0;
     const float sc = p.scale;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DC / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * db + g * 8 + half * 4;
@@ -595,9 +616,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dq: the forward's walk over the CSR list with K and V staged row-major in a
 // double-buffered LDS pipeline; Q and dO stay in registers.  bf16 takes K^T for
-// dQ^T += K^T dS^T from the LDS transpose read of the K tile; fp32 stages K^T.
+// dQ^T += K^T dS^T from the LDS transpose read of the K tile; fp32 stages K^T, in one
+// buffer where two would not fit (d = 256), and then for the launch's column slice
+// of dQ only (CS slices, columns c0 .. c0 + D / CS - 1).
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool NODES>
+template <typename T, int D, bool NODES, int CS = 1>
 struct DqCfg {
   static constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
   static constexpr int NW = 4;
@@ -610,8 +633,9 @@ struct DqCfg {
   static constexpr int NSUB = kTileN / BN;
   static constexpr int NS = D + (kBf16 ? 32 : 16) / EB;  // see DkdvCfg::NS
   static constexpr int TS = BN + 16 / EB;
+  static constexpr int DC = D / CS;  // dQ columns per launch
   static constexpr int N_ELEMS = BN * NS;
-  static constexpr int T_ELEMS = kBf16 ? 0 : D * TS;
+  static constexpr int T_ELEMS = kBf16 ? 0 : DC * TS;
   static constexpr int BUF_ELEMS = 2 * N_ELEMS + T_ELEMS;
   // bf16: K | V | mask words (end[], or lo[] | w[]) stages filled by direct-to-LDS
   // loads into swizzled tiles (as the forward); fp32: through registers
@@ -619,21 +643,26 @@ struct DqCfg {
   static constexpr int MW = NODES ? 2 : 1;
   static constexpr int TILE_BYTES = BN * D * 2;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES + MW * 256;
-  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : 2 * BUF_ELEMS * EB + 2 * MW * BN * 4;
+  static constexpr int NBUF = 2 * BUF_ELEMS * EB + 2 * MW * BN * 4 <= kLdsMax ? 2 : 1;
+  static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : NBUF * BUF_ELEMS * EB + 2 * MW * BN * 4;
   static constexpr int WAVES_PER_EU = (kBf16 && D <= 128) ? 2 : 1;
+  static_assert(CS == 1 || !kDma, "column slices exist on the register path only");
+  static_assert(LDS_BYTES <= kLdsMax, "LDS");
 };
 
 // PRE: the kernel also does the preparation of its rows (bwd_pre_kernel's work): it
 // holds dO for exactly its (row, head) pairs, so it loads O beside it, forms D and
 // LSE in log2 units in registers and writes them to the workspace for the dK/dV
 // kernel, which then runs after it.
-template <typename T, typename G, int D, int MODE, bool PRE, bool NODES>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, D, NODES>::WAVES_PER_EU)))
+template <typename T, typename G, int D, int MODE, bool PRE, bool NODES, int CS = 1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<T, D, NODES, CS>::WAVES_PER_EU)))
 void dq_kernel(BwdParams p) {
-  using C = DqCfg<T, D, NODES>;
+  using C = DqCfg<T, D, NODES, CS>;
+  constexpr int DC = C::DC;
+  constexpr bool kSingle = !C::kDma && C::NBUF == 1;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   T* const buf0 = reinterpret_cast<T*>(smem);
-  int32_t* const es0 = reinterpret_cast<int32_t*>(smem + 2 * C::BUF_ELEMS * C::EB);
+  int32_t* const es0 = reinterpret_cast<int32_t*>(smem + C::NBUF * C::BUF_ELEMS * C::EB);
 
   const int64_t w_id = xcd_remap(blockIdx.x, p.chunk);
   if (w_id >= p.n_work) return;
@@ -657,9 +686,10 @@ void dq_kernel(BwdParams p) {
 
   Frag<T> qf[D / 16], gf[D / 16];  // loaded below, once the first tile's loads are in flight
   float l2 = INFINITY, dl = 0.f;
-  f32x16 adq[D / 32];
+  f32x16 adq[DC / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) adq[db] = zero16();
+  for (int db = 0; db < DC / 32; ++db) adq[db] = zero16();
+  const int c0 = CS > 1 ? p.c0 : 0;
   const float c = p.c;
   const int64_t ldk = int64_t(hkv) * D;
   const int64_t koff = int64_t(hk) * D;
@@ -687,7 +717,7 @@ void dq_kernel(BwdParams p) {
   mark_ready(*reinterpret_cast<int32_t*>(&wreg));
 
   RowStage<T, C::BN, D, C::NS, C::NT> kst, vst;
-  using TStage = TransStage<T, C::BN, D, C::TS, C::NT>;
+  using TStage = TransStage<T, C::BN, DC, C::TS, C::NT>;
   typename std::conditional<C::kBf16, int, TStage>::type ktst;
   DmaTile<C::BN, D, C::NT> dt;
   const int pitch = int(ldk) * 2;
@@ -718,7 +748,7 @@ void dq_kernel(BwdParams p) {
       }
       kst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
       vst.load(Vg + kv0 * ldk + koff, ldk, nvalid);
-      if constexpr (!C::kBf16) ktst.load(Kg + kv0 * ldk + koff, ldk, nvalid);
+      if constexpr (!C::kBf16) ktst.load(Kg + kv0 * ldk + koff + c0, ldk, nvalid);
     }
   };
   auto commit = [&](int b) {  // register path
@@ -780,7 +810,7 @@ void dq_kernel(BwdParams p) {
   if constexpr (!C::kDma) __syncthreads();
 
   for (int n = 0; n < n_steps; ++n) {
-    const int b = n & 1;
+    const int b = kSingle ? 0 : n & 1;
     if constexpr (C::kDma) {  // see the forward kernel
       wait_vmcnt<0>();
       __syncthreads();
@@ -793,7 +823,8 @@ void dq_kernel(BwdParams p) {
         window_load((n + 1) / C::NSUB);
         mark_ready(*reinterpret_cast<int32_t*>(&wreg));
       }
-      issue(n + 1, int(entry(n + 1) & 0x3fffffffu));
+      // one buffer: the next sub-step is staged after this one's math
+      if constexpr (!kSingle) issue(n + 1, int(entry(n + 1) & 0x3fffffffu));
     }
 
     const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
@@ -930,29 +961,29 @@ void dq_kernel(BwdParams p) {
           }
         }
       } else {
+        // fp32: dQ^T += K^T dS^T over these BN keys, into a fresh block that is then
+        // added to dQ (one chain over every key of a long list would round at the
+        // magnitude of the running sum on each of its steps)
 #pragma unroll
-        for (int t = 0; t < C::BN / 16; ++t) {
-          // dQ^T += K^T dS^T over these 16 keys: dS rounded, then where split_wanted
-          // its residual in a second pass
-          const float* dst = &ds[t >> 1][(t & 1) * 8];
-          auto products = [&](const Frag<T>& sf) {
+        for (int db = 0; db < DC / 32; ++db) {
+          f32x16 part = zero16();
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              Frag<T> ka;
-              if constexpr (C::kBf16)
-                ka = frag_load_tr(Ks, C::NS, 16 * t, 32 * db);
-              else
-                ka = frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half);
-              mma(adq[db], ka, sf);
-            }
-          };
-          const Frag<T> sf = frag_from<T>(dst);
-          products(sf);
-          if (split_wanted<T, MODE, false>(nullptr, dst)) products(frag_residual(dst, sf));
+          for (int t = 0; t < C::BN / 16; ++t)
+            mma(part, frag_load(Kt + (32 * db + l32) * C::TS + 16 * t + 8 * half),
+                frag_from<T>(&ds[t >> 1][(t & 1) * 8]));
+          adq[db] += part;
+          __builtin_amdgcn_sched_barrier(0);  // one partial block at a time (registers)
         }
       }
     }
-    if constexpr (!C::kDma) {
+    if constexpr (kSingle) {  // every wave is done with the buffer: stage the next step
+      if (n + 1 < n_steps) {
+        __syncthreads();
+        issue(n + 1, int(entry(n + 1) & 0x3fffffffu));
+        commit(0);
+      }
+      __syncthreads();
+    } else if constexpr (!C::kDma) {
       if (n + 1 < n_steps) commit(b ^ 1);
       __syncthreads();
     }
@@ -960,10 +991,10 @@ void dq_kernel(BwdParams p) {
   if constexpr (C::kDma) wait_vmcnt<0>();  // no load into LDS outlives the work-group
 
   if (qvalid) {
-    G* dqp = static_cast<G*>(p.dq) + (qrow * hq + h) * D;
+    G* dqp = static_cast<G*>(p.dq) + (qrow * hq + h) * D + c0;
     const float sc = p.scale;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DC / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * db + g * 8 + half * 4;
@@ -1012,7 +1043,14 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.hkv = s.hkv;
   p.scale = s.scale;
   p.c = s.scale * kLog2e;
+  p.c0 = 0;
   const int rep = s.hq / s.hkv;
+  // fp32 at d >= 128: dV and dK in separate passes (room for the per-sub-step partial
+  // sums of fp32), and at d = 256 each of them, and dQ, in two launches of half the
+  // columns
+  constexpr bool kF32 = std::is_same<T, float>::value;
+  constexpr int CS = kF32 && D > 128 ? 2 : 1;
+  constexpr bool kTwoPass = D > 128 || (kF32 && D >= 128);
 
   // PREPARE together with DQ: the dQ kernel does the preparation of its rows and
   // runs first; dK/dV then reads what it wrote.
@@ -1023,8 +1061,16 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
     p.chunk = rep * 2;
     const int64_t per = 8 * int64_t(p.chunk);
     const int64_t grid = (p.n_work + per - 1) / per * per;
-    hipLaunchKernelGGL((dq_kernel<T, G, D, MODE, PRE, NODES>), dim3(unsigned(grid)), dim3(256),
-                       0, stream, p);
+    p.c0 = 0;
+    hipLaunchKernelGGL((dq_kernel<T, G, D, MODE, PRE, NODES, CS>), dim3(unsigned(grid)),
+                       dim3(256), 0, stream, p);
+    // the other column slices read the D and LSE rows the first one prepared
+    for (int c = 1; c < CS; ++c) {
+      p.c0 = c * (D / CS);
+      hipLaunchKernelGGL((dq_kernel<T, G, D, MODE, false, NODES, CS>), dim3(unsigned(grid)),
+                         dim3(256), 0, stream, p);
+    }
+    p.c0 = 0;
   };
   if (fused) {
     launch_dq(std::true_type{});
@@ -1038,11 +1084,18 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
     p.chunk = 2;
     const int64_t per = 8 * int64_t(p.chunk);
     const int64_t grid = (p.n_work + per - 1) / per * per;
-    if constexpr (D > 128) {  // dV and dK in two passes (see dkdv_kernel)
-      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 1, NODES>), dim3(unsigned(grid)),
-                         dim3(256), 0, stream, p);
-      hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 2, NODES>), dim3(unsigned(grid)),
-                         dim3(256), 0, stream, p);
+    if constexpr (kTwoPass) {  // dV and dK in two passes (see dkdv_kernel)
+      for (int c = 0; c < CS; ++c) {  // each in column slices (fp32, d = 256)
+        p.c0 = c * (D / CS);
+        hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 1, NODES, CS>), dim3(unsigned(grid)),
+                           dim3(256), 0, stream, p);
+      }
+      for (int c = 0; c < CS; ++c) {
+        p.c0 = c * (D / CS);
+        hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 2, NODES, CS>), dim3(unsigned(grid)),
+                           dim3(256), 0, stream, p);
+      }
+      p.c0 = 0;
     } else {
       hipLaunchKernelGGL((dkdv_kernel<T, G, D, MODE, 0, NODES>), dim3(unsigned(grid)),
                          dim3(256), 0, stream, p);
@@ -1093,6 +1146,7 @@ hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype gdt, cons
     switch (s.d) {
       case 64: PSA_BWD(float, float, 64, psa::kSplitAdaptive);
       case 128: PSA_BWD(float, float, 128, psa::kSplitAdaptive);
+      case 256: PSA_BWD(float, float, 256, psa::kSplitAdaptive);
     }
   }
 #undef PSA_BWD_BF16

@@ -42,6 +42,7 @@ struct fp8_t {  // raw fp8 storage, OCP e4m3 (the forward's scores take it)
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLdsMax = 160 * 1024;  // LDS bytes a work-group may take on gfx950
 constexpr float kLn2 = 0.6931471805599453f;
 
 // The wave's index in its work-group, as a wave-uniform (scalar) value: addresses and

@@ -516,21 +516,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
           if (i + PF - 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
         }
-      } else {
+      } else if constexpr (C::kDma) {
 #pragma unroll
         for (int t = 0; t < C::BN / 16; ++t) {
           const Frag<PT> pf = frag_from<PT>(&sv[t >> 1][(t & 1) * 8]);
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            Frag<PT> va;
-            if constexpr (C::kDma)
-              va = frag_load_tr_swz<D / 8>(st + C::KT_BYTES, 16 * t, 32 * db);
-            else if constexpr (C::kBf16)
-              va = frag_load_tr(Vs, C::VS, 16 * t, 32 * db);
-            else
-              va = frag_load(Vs + (32 * db + l32) * C::VS + 16 * t + 8 * half);
-            mma(acc[db], va, pf);
-          }
+          for (int db = 0; db < D / 32; ++db)
+            mma(acc[db], frag_load_tr_swz<D / 8>(st + C::KT_BYTES, 16 * t, 32 * db), pf);
+        }
+      } else {
+        // fp32: the sub-step's product goes into a fresh block and is added to O
+        // afterwards.  One accumulator chain over every key of a long list would round
+        // at the magnitude of the running sum on each of its ~keys/2 steps; per-sub-step
+        // partial sums round there once per sub-step.
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          f32x16 part = zero16();
+#pragma unroll
+          for (int t = 0; t < C::BN / 16; ++t)
+            mma(part, frag_load(Vs + (32 * db + l32) * C::VS + 16 * t + 8 * half),
+                frag_from<PT>(&sv[t >> 1][(t & 1) * 8]));
+          acc[db] += part;
         }
       }
     }
@@ -604,7 +610,7 @@ hipError_t launch_fwd_t(const psa_tile_map& map, const AttnShape& s, const void*
 
 bool fwd_supported(psa_dtype dt, int32_t d) {
   if (dt == PSA_BF16 || dt == PSA_FP8_E4M3) return d == 64 || d == 128 || d == 256;
-  if (dt == PSA_FP32) return d == 64 || d == 128;
+  if (dt == PSA_FP32) return d == 64 || d == 128 || d == 256;
   return false;
 }
 
@@ -629,6 +635,7 @@ hipError_t launch_fwd(const psa_tile_map& map, psa_dtype dt, const AttnShape& s,
     switch (s.d) {
       case 64: return psa::launch_fwd_t<float, 64>(map, s, q, k, v, o, lse, stream);
       case 128: return psa::launch_fwd_t<float, 128>(map, s, q, k, v, o, lse, stream);
+      case 256: return psa::launch_fwd_t<float, 256>(map, s, q, k, v, o, lse, stream);
     }
   }
   return hipErrorInvalidValue;

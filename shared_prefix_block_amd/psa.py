@@ -100,7 +100,7 @@ def load() -> ctypes.CDLL:
             "psa_fold_workspace_size": (ctypes.c_int, [I64, I64, ctypes.POINTER(SZ)]),
             "psa_fold_rollouts": (ctypes.c_int, [I64, P, P, P, P, P, I64, I32, I32, P, P, P, P,
                                                  P, P, P, SZ, P]),
-            "psa_unfold_rows": (ctypes.c_int, [I64, P, P, P, I64, I64, P, P, P, SZ, P]),
+            "psa_unfold_rows": (ctypes.c_int, [I64, P, P, P, I64, I64, P, P, SZ, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -281,11 +281,21 @@ def build_tile_map_draft(ctx_len: int, block_size: int, anchors: torch.Tensor,
     lib = load()
     if block_m is None or block_n is None:
         block_m, block_n = tile_shape(PASS_FWD, dtype, d)
-    for t, dt in ((anchors, torch.int32), (keep, torch.uint8), (ctx_doc, torch.int32),
-                  (anchor_doc, torch.int32)):
-        if t is not None and (t.dtype != dt or not t.is_cuda or not t.is_contiguous()):
-            raise TypeError("draft arrays must be contiguous device tensors (int32 / uint8)")
     n = anchors.numel()
+    arrays = [(t, dt, size, name) for t, dt, size, name in (
+        (anchors, torch.int32, n, "anchors"), (keep, torch.uint8, n, "keep"),
+        (ctx_doc, torch.int32, ctx_len, "ctx_doc"), (anchor_doc, torch.int32, n, "anchor_doc"))
+        if t is not None]
+    for t, _, size, name in arrays:
+        if t.numel() != size:
+            raise ValueError(f"{name} must hold {size} values, not {t.numel()}")
+    if (ctx_doc is None) != (anchor_doc is None):
+        raise ValueError("ctx_doc and anchor_doc go together (both or neither)")
+    for t, dt, _, name in arrays:
+        if t.device != anchors.device:
+            raise ValueError(f"{name} is on {t.device}, anchors on {anchors.device}")
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise TypeError("draft arrays must be contiguous device tensors (int32 / uint8)")
     if T is None:
         T = ctx_len + n * block_size
     dev = anchors.device
@@ -466,11 +476,21 @@ class Rollouts:
                 np_ptr(self.comp_len))
 
 
-def fold_workspace(r: Rollouts, device) -> torch.Tensor:
-    lib = load()
+def _fold_ws_bytes(r: Rollouts) -> int:
     b = ctypes.c_size_t(0)
-    _check(lib.psa_fold_workspace_size(r.n_groups, r.n_comp, ctypes.byref(b)))
-    return torch.empty(b.value, dtype=torch.uint8, device=device)
+    _check(load().psa_fold_workspace_size(r.n_groups, r.n_comp, ctypes.byref(b)))
+    return b.value
+
+
+def fold_workspace(r: Rollouts, device) -> torch.Tensor:
+    return torch.empty(_fold_ws_bytes(r), dtype=torch.uint8, device=device)
+
+
+def _check_ws(ws: torch.Tensor, r: Rollouts, device) -> None:
+    if not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < _fold_ws_bytes(r):
+        raise ValueError("workspace smaller than psa_fold_workspace_size")
 
 
 def fold_rollouts(r: Rollouts, prompt_tok: torch.Tensor, comp_tok: torch.Tensor, T: int,
@@ -479,14 +499,22 @@ def fold_rollouts(r: Rollouts, prompt_tok: torch.Tensor, comp_tok: torch.Tensor,
     """input_ids, labels, position_ids, group, suffix (int32 [T]) and is_prefix (uint8
     [T]) of the folded layout; prompt_tok / comp_tok: int32 device tokens."""
     lib = load()
-    dev = prompt_tok.device if prompt_tok.numel() else comp_tok.device
-    for t in (prompt_tok, comp_tok):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise ValueError("token buffers must be contiguous int32")
+    dev = prompt_tok.device
+    n_prompt = int(r.prompt_len.sum())
+    toks = ((prompt_tok, n_prompt, "prompt_tok"), (comp_tok, r.fold_len - n_prompt, "comp_tok"))
+    for t, size, name in toks:
+        if t.numel() != size:
+            raise ValueError(f"{name} must hold {size} tokens, not {t.numel()}")
+    if comp_tok.device != dev:
+        raise ValueError("prompt_tok and comp_tok must be on one device")
+    for t, _, name in toks:
+        if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
     out = {k: torch.empty(T, dtype=torch.int32, device=dev)
            for k in ("input_ids", "labels", "position_ids", "group", "suffix")}
     out["is_prefix"] = torch.empty(T, dtype=torch.uint8, device=dev)
     ws = fold_workspace(r, dev) if workspace is None else workspace
+    _check_ws(ws, r, dev)
     with torch.cuda.device(dev):
         _check(lib.psa_fold_rollouts(*r._tables(), _ptr(prompt_tok), _ptr(comp_tok), T, pad_id,
                                      ignore_index, _ptr(out["input_ids"]), _ptr(out["labels"]),
@@ -500,14 +528,22 @@ def unfold_rows(r: Rollouts, src: torch.Tensor, out: Optional[torch.Tensor] = No
                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Rows of a folded [T, ...] device tensor gathered per sample ([prompt_g | c_gi])."""
     lib = load()
-    if not src.is_contiguous():
-        raise ValueError("src must be contiguous")
+    if src.dim() < 1 or src.shape[0] < r.fold_len:
+        raise ValueError(f"src must have at least the folded layout's {r.fold_len} rows")
+    if not src.is_contiguous() or not src.is_cuda:
+        raise ValueError("src must be a contiguous device tensor [T, ...]")
     T = src.shape[0]
-    row_bytes = src[0].numel() * src.element_size() if T else 0
-    dst = torch.empty((r.unfold_len,) + tuple(src.shape[1:]), dtype=src.dtype,
-                      device=src.device) if out is None else out
+    row_bytes = (src.numel() // T) * src.element_size() if T else 0
+    shape = (r.unfold_len,) + tuple(src.shape[1:])
+    if out is None:
+        dst = torch.empty(shape, dtype=src.dtype, device=src.device)
+    else:
+        _check_buf(out, shape, src.dtype, src.device, "out")
+        dst = out
     ws = fold_workspace(r, src.device) if workspace is None else workspace
+    _check_ws(ws, r, src.device)
     with torch.cuda.device(src.device):
-        _check(lib.psa_unfold_rows(*r._tables(), T, row_bytes, _ptr(src), _ptr(dst), _ptr(ws),
-                                   ws.numel(), _stream(src.device)))
+        _check(lib.psa_unfold_rows(*r._tables(), T, row_bytes, _ptr(src), _ptr(dst),
+                                   dst.numel() * dst.element_size(), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(src.device)))
     return dst

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.psa_abi_version() == 5
+    assert lib.psa_abi_version() == 6
     for code, name in psa.STATUS.items():
         s = lib.psa_status_string(code).decode()
         assert s and s != "unknown status", name
@@ -52,7 +52,12 @@ def test_tile_shape(lib):
     assert (bm.value, bn.value) == (128, 128)
     assert lib.psa_tile_shape(1, 0, 64, ctypes.byref(bm), ctypes.byref(bn)) == 0
     assert lib.psa_tile_shape(0, 1, 96, ctypes.byref(bm), ctypes.byref(bn)) == 5
-    assert lib.psa_tile_shape(0, 0, 256, ctypes.byref(bm), ctypes.byref(bn)) == 5
+    # fp32 and bf16: d in {64, 128, 256}, both passes
+    for dt in (0, 1):
+        for d in (64, 128, 256):
+            for pass_ in (0, 1):
+                assert lib.psa_tile_shape(pass_, dt, d, ctypes.byref(bm), ctypes.byref(bn)) == 0
+    assert lib.psa_tile_shape(1, 0, 512, ctypes.byref(bm), ctypes.byref(bn)) == 5
     assert lib.psa_tile_shape(0, 7, 128, ctypes.byref(bm), ctypes.byref(bn)) == 4
     # e4m3 inputs: forward only, at the bf16 head sizes
     for d in (64, 128, 256):
@@ -180,12 +185,16 @@ def test_fold_rejects_bad_tables(lib):
 def test_unfold_rejects_bad_rows(lib):
     arr = lambda a: (ctypes.c_int32 * len(a))(*a)  # noqa: E731
     fake = ctypes.c_void_p(256)
-    call = lambda T, rb, ws=1 << 20: lib.psa_unfold_rows(  # noqa: E731
-        1, arr([2]), arr([0, 2]), arr([1, 1]), T, rb, fake, fake, fake, ws, None)
+    call = lambda T, rb, ws=1 << 20, dst=1 << 20: lib.psa_unfold_rows(  # noqa: E731
+        1, arr([2]), arr([0, 2]), arr([1, 1]), T, rb, fake, fake, dst, fake, ws, None)
     assert call(4, 6) == 2    # row_bytes not a multiple of 4
     assert call(4, 0) == 2
     assert call(3, 8) == 2    # T shorter than the folded length
     assert call(4, 8, ws=8) == 7
+    # the two samples [p | c0], [p | c1] take 6 rows of 8 bytes: 47 bytes of dst are short
+    assert call(4, 8, dst=47) == 2
+    assert b"dst holds 47 bytes" in lib.psa_last_error()
+    assert call(4, 8, dst=48, ws=8) == 7  # 48 bytes pass the dst check
     b = ctypes.c_size_t(0)
     assert lib.psa_fold_workspace_size(3, 7, ctypes.byref(b)) == 0 and b.value >= 256
     assert lib.psa_fold_workspace_size(-1, 7, ctypes.byref(b)) == 2

@@ -72,6 +72,23 @@ def test_fuzz_tokens(seed):
     _check_full(lay, hq, hkv, d, dt, seed)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_fuzz_fp32_d256(seed):
+    """fp32 at head_dim 256: the dQ and dK launches that each take half the columns,
+    the dV pass, one LDS buffer where two do not fit; token layouts and trees."""
+    rng = np.random.default_rng(900 + seed)
+    if seed % 2:
+        nl, paths = wl.random_tree(rng, max_nodes=8, max_len=130)
+        lay = wl.tree_layout(nl, paths, extra_pad=int(rng.integers(0, 50)))
+    else:
+        specs = wl.random_group_specs(rng, max_groups=3, max_p=200, max_g=4, max_r=150)
+        lay = wl.tokens_layout(specs, pad_multiple=int(rng.integers(1, 130)))
+    if lay.T == 0:
+        return
+    hq, hkv = [(2, 2), (4, 2), (3, 1)][seed % 3]
+    _check_full(lay, hq, hkv, 256, "fp32", seed)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_fuzz_trees(seed):
     rng = np.random.default_rng(800 + seed)
@@ -83,7 +100,8 @@ def test_fuzz_trees(seed):
     _check_full(lay, hq, hkv, d, dt, seed)
 
 
-VARIANTS = [(64, "fp32"), (128, "fp32"), (64, "bf16"), (128, "bf16"), (256, "bf16")]
+VARIANTS = [(64, "fp32"), (128, "fp32"), (256, "fp32"), (64, "bf16"), (128, "bf16"),
+            (256, "bf16")]
 
 
 @pytest.mark.parametrize("d,dtype", VARIANTS)
@@ -137,7 +155,8 @@ def test_bwd_flags_rejected():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (128, "bf16"), (256, "bf16")])
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (256, "fp32"), (128, "bf16"),
+                                     (256, "bf16")])
 def test_forward_without_lse(d, dtype):
     """The no-grad forward (lse NULL) writes the same O as the full forward and leaves
     the memory an LSE would go to alone."""
@@ -156,7 +175,7 @@ def test_forward_without_lse(d, dtype):
     compare("o", o2, oa.forward(meta_from_layout(lay), q, k, v)[0], DT[dtype])
 
 
-@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "bf16"), (256, "bf16")])
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (256, "fp32"), (128, "bf16"), (256, "bf16")])
 def test_stage_orders_agree(d, dtype):
     """psa_bwd runs dQ with the preparation of its rows first, then dK/dV; the stages run
     one by one (prepare, dK/dV, dQ) must give the same gradients, both at the parity bar
@@ -220,6 +239,18 @@ def _sample(T, n, rng, extra=()):
     return np.asarray(sorted(base), dtype=np.int64)
 
 
+def _prompt_keys(lay, g):
+    """Prompt keys of group g: its first and last, the keys on both sides of every
+    128-key tile edge inside the prompt (at most 4 edges, spread), and the middle."""
+    start = sum(p + sum(rs) for p, rs in lay.specs[:g])
+    p = lay.specs[g][0]
+    keys = {start, start + p - 1, start + p // 2}
+    edges = [t for t in range(start + 1, start + p) if t % 128 == 0]
+    for t in edges[:: max(1, len(edges) // 4)][:4]:
+        keys |= {t - 1, t}
+    return np.asarray(sorted(keys), dtype=np.int64)
+
+
 def _boundaries(lay):
     """Token positions around group / completion / node boundaries and tile edges."""
     pts = []
@@ -280,6 +311,18 @@ def test_workload_parity_sampled(idx, split):
     dk, dv = oa.grad_cols(meta, q, k, v, do, cols)
     compare("dk", got["dk"][cols], dk, tdt)
     compare("dv", got["dv"][cols], dv, tdt)
+    if lay.kind == "tokens" and not small:
+        # prompt keys of a large group, element by element on one kv head: the keys
+        # with the longest CSC lists (every completion tile of the group walks them),
+        # where the oracle has to recompute every row of the group
+        g = int(np.argmax([p for p, _ in lay.specs]))
+        pcols = _prompt_keys(lay, g)
+        heads = [g % cfg.hkv]
+        say(f"workload {idx}: {len(pcols)} prompt keys of group {g} (P={lay.specs[g][0]}), "
+            f"kv head {heads[0]}")
+        dkp, dvp = oa.grad_cols(meta, q, k, v, do, pcols, kv_heads=heads)
+        compare("dk prompt keys", got["dk"][pcols][:, heads], dkp, tdt)
+        compare("dv prompt keys", got["dv"][pcols][:, heads], dvp, tdt)
     # whole-tensor identities: sum_kv dV = sum_q dO (rows with a key), sum_kv dK = 0
     rep = cfg.hq // cfg.hkv
     dv_sum = got["dv"].double().sum(0).cpu()  # [hkv, d]

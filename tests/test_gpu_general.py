@@ -127,15 +127,10 @@ def test_forced_node_form_matches_interval_form(case):
 
 @pytest.mark.parametrize("seed", range(24))
 def test_attention_general_fuzz(seed):
-    """Node runs up to 130 tokens with bf16 inputs, up to 80 with fp32: a key near the
-    root of a larger tree collects dV from ~10^3 rows at magnitudes ~5, where the fp32
-    kernels sit at the 1e-5 bar whatever the layout (a 17-node tree of 1076 tokens
-    gives 1.1e-5 in the node form and 0.94e-5 in depth-first order through the
-    interval form, the same elements off: LSE and accumulation rounding, not the
-    mask)."""
+    """Node runs up to 130 tokens, every dtype."""
     hq, hkv, d, dtype = CASES[seed % len(CASES)]
     rng = np.random.default_rng(5200 + seed)
-    lay = _general_layout(rng, KINDS[seed % 3], max_len=130 if dtype == "bf16" else 80)
+    lay = _general_layout(rng, KINDS[seed % 3], max_len=130)
     if lay.T == 0:
         return
     tdt = DT[dtype]
@@ -153,6 +148,31 @@ def test_attention_general_fuzz(seed):
     compare("dq", dq, wdq, tdt)
     compare("dk", dk, wdk, tdt)
     compare("dv", dv, wdv, tdt)
+
+
+@pytest.mark.parametrize("form", ["auto", "nodes"])
+def test_fp32_long_accumulation_chain(form):
+    """A 17-node tree of 1368 tokens (and pads) with fp32 inputs, d = 128: keys near
+    its root collect dV from ~10^3 rows at magnitudes ~5.  With one fp32 accumulator
+    chain over all of them the rounding of the running sum alone reached 1.1e-5 here
+    (above the 1e-5 bar); the kernels now add each sub-step's products to the sums as
+    a partial block.  The same tree as the fuzz case of seed 17."""
+    rng = np.random.default_rng(5200 + 17)
+    lay = _general_layout(rng, "tree", max_len=130)
+    assert lay.T_real == 1368 and len(lay.node_lengths) == 17
+    hq, hkv, d, dtype = 4, 2, 128, "fp32"
+    say(f"fp32 long chain form={form} T={lay.T}")
+    q, k, v, do = wl.make_tensors(lay.T, hq, hkv, d, dtype, 1.0, 17)
+    m = psa.layout_tile_map(lay, "cuda", dtype=torch.float32, d=d, form=form)
+    qd, kd, vd, dod = (x.cuda() for x in (q, k, v, do))
+    o, lse = psa.fwd(m, qd, kd, vd)
+    dq, dk, dv = psa.bwd(m, qd, kd, vd, o, lse, dod)
+    torch.cuda.synchronize()
+    wo, wl_, wdq, wdk, wdv = oa.backward(meta_from_layout(lay), q, k, v, do)
+    for name, got, want in (("o", o, wo), ("lse", lse, wl_), ("dq", dq, wdq), ("dk", dk, wdk),
+                            ("dv", dv, wdv)):
+        err, _ = compare(name, got, want, torch.float32)
+        say(f"  {name}: max-abs {err:.3e}")
 
 
 @pytest.mark.parametrize("which", ["chunked", "tokens", "tree"])

@@ -277,6 +277,29 @@ def test_sampled_paths_agree_with_full():
     np.testing.assert_allclose(dv_c, dv[cols], rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("kv_heads", [[0], [1], [1, 0], [2]])
+def test_sampled_columns_for_some_kv_heads(kv_heads):
+    """grad_cols restricted to kv heads (the full-size checks of the large workloads
+    take one or two) equals the full backward on those heads, on layouts whose row
+    blocks see different column sets: a long prompt, completions of several lengths, a
+    tree, and blocks of 16 rows so that each block prunes its own columns."""
+    lay = wl.tokens_layout([(40, [5, 30, 0, 17]), (3, [9])], pad_multiple=16)
+    tree = wl.tree_layout([12, 7, 9, 5, 11], [[0, 1, 3], [0, 1, 4], [0, 2]], extra_pad=3)
+    for layout, hq, hkv in ((lay, 6, 3), (tree, 3, 3)):
+        if max(kv_heads) >= hkv:
+            continue
+        meta = meta_from_layout(layout)
+        q, k, v, do = _rand(layout.T, hq, hkv, 8, 31)
+        _, _, _, dk, dv = oa.backward(meta, q, k, v, do)
+        cols = np.arange(layout.T)
+        dk_c, dv_c = oa.grad_cols(meta, q, k, v, do, cols, block_rows=16, kv_heads=kv_heads)
+        assert dk_c.shape == (layout.T, len(kv_heads), 8)
+        np.testing.assert_allclose(dk_c, dk[:, kv_heads], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv_c, dv[:, kv_heads], rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oa.grad_cols(meta_from_layout(lay), *_rand(lay.T, 6, 3, 8, 31), [0], kv_heads=[3])
+
+
 def test_gradient_sum_identities():
     """Rows of P sum to 1, so sum_kv dV = sum_q dO over non-empty rows; and
     sum_kv dS = 0 per row, so sum_kv dK = 0 (per kv head, over the group)."""
