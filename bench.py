@@ -98,97 +98,206 @@ def describe(cfg, lay, layout_mode="packed", form="auto") -> str:
             f"hq={cfg.hq}/hkv={cfg.hkv}, d={cfg.d}, {cfg.dtype}")
 
 
-def cpu_baseline(cfg, lay, min_seconds=10.0):
-    """Time the float64 oracle on whole groups (trees) of the workload, all heads, one
-    after another until at least min_seconds of CPU work (or the whole workload) is
-    done; scale to the workload's effective FLOPs by the sample's share of the kept
-    pairs.  Groups never see each other, so a group is a self-contained slice."""
+def _parts(lay):
+    """The self-contained slices of a packed layout: its groups (token form) or trees."""
+    from shared_prefix_block_amd import workloads as wl
+
+    if lay.kind == "tokens":
+        return [("group", spec) for spec in lay.specs]
+    per = 21  # root, 4 branches, 16 leaves
+    out = []
+    for t in range(len(lay.node_lengths) // per):
+        nodes = set(range(per * t, per * t + per))
+        paths = [[n - per * t for n in pth] for pth in lay.sample_paths if pth[0] in nodes]
+        out.append(("tree", (lay.node_lengths[per * t:per * t + per], paths)))
+    return out
+
+
+def _part_layout(kind, spec):
+    from shared_prefix_block_amd import workloads as wl
+
+    if kind == "group":
+        return wl.tokens_layout([spec])
+    return wl.tree_layout(*spec)
+
+
+def oracle_dense_flops(lay, hq: int, d: int, backward: bool) -> float:
+    """The float64 oracle's own work: per group (tree) and q head, dense products over
+    the group's columns; S and P V forward (4 d per pair of the group), plus dP, dQ,
+    dK and dV backward (8 d more)."""
+    sizes = []
+    for kind, spec in _parts(lay):
+        sizes.append(spec[0] + sum(spec[1]) if kind == "group" else sum(spec[0]))
+    per_pair = (12 if backward else 4) * d
+    return float(sum(n * n for n in sizes)) * hq * per_pair
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, lay, budget_flop: float = 1.2e12) -> dict:
+    """The float64 oracle, unchanged, timed on a bounded sample of the workload: its
+    first group (tree), on as many q heads as keep the oracle's dense work of the
+    sample under budget_flop (then its completions cut too, if one head is still over),
+    forward alone and forward + backward.  The oracle's time follows its dense work
+    (oracle_dense_flops), so each time is scaled to the whole workload by the ratio of
+    that work; tokens/s = real tokens / scaled time."""
     from threadpoolctl import threadpool_info
 
     from oracle import attention as oa
     from oracle.mask import meta_from_layout
     from shared_prefix_block_amd import workloads as wl
 
-    if lay.kind == "tokens":
-        parts = [wl.tokens_layout([spec]) for spec in lay.specs]
-        unit = "group"
-    else:
-        per = 21  # root, 4 branches, 16 leaves
-        parts = []
-        for t in range(len(lay.node_lengths) // per):
-            nodes = set(range(per * t, per * t + per))
-            paths = [[n - per * t for n in pth] for pth in lay.sample_paths if pth[0] in nodes]
-            parts.append(wl.tree_layout(lay.node_lengths[per * t:per * t + per], paths))
-        unit = "tree"
-    done, pairs, dt = 0, 0, 0.0
-    for sub in parts:
-        q, k, v, do = wl.make_tensors(sub.T, cfg.hq, cfg.hkv, cfg.d, cfg.dtype, cfg.sigma,
-                                      cfg.idx)
-        meta = meta_from_layout(sub)
+    backward = cfg.passes != "fwd"
+    kind, spec = _parts(lay)[0]
+    rep = cfg.hq // cfg.hkv
+    hkv_s = cfg.hkv
+    sub = _part_layout(kind, spec)
+    while hkv_s > 1 and oracle_dense_flops(sub, hkv_s * rep, cfg.d, backward) > budget_flop:
+        hkv_s = (hkv_s + 1) // 2
+    hq_s = hkv_s * rep
+    cut = ""
+    if kind == "group":
+        p, rs = spec
+        while len(rs) > 1 and oracle_dense_flops(sub, hq_s, cfg.d, backward) > budget_flop:
+            rs = rs[: max(1, len(rs) * 3 // 4)]
+            sub = _part_layout(kind, (p, rs))
+        if len(rs) < len(spec[1]):
+            cut = f" with {len(rs)} of its {len(spec[1])} completions"
+    q, k, v, do = wl.make_tensors(sub.T, hq_s, hkv_s, cfg.d, cfg.dtype, cfg.sigma, cfg.idx)
+    meta = meta_from_layout(sub)
+    t0 = time.perf_counter()
+    oa.forward(meta, q, k, v)
+    t_fwd = time.perf_counter() - t0
+    t_fb = None
+    if backward:
         t0 = time.perf_counter()
-        if cfg.passes == "fwd":
-            oa.forward(meta, q, k, v)
-        else:
-            oa.backward(meta, q, k, v, do)
-        dt += time.perf_counter() - t0
-        done += 1
-        pairs += kept_pairs(sub)
-        if dt >= min_seconds:
-            break
-    frac = pairs / kept_pairs(lay)
-    what = f"{done} of {len(parts)} {unit}s (first {done}), all {cfg.hq} q heads"
+        oa.backward(meta, q, k, v, do)
+        t_fb = time.perf_counter() - t0
+    scale_f = oracle_dense_flops(lay, cfg.hq, cfg.d, False) / oracle_dense_flops(
+        sub, hq_s, cfg.d, False)
+    scale_b = oracle_dense_flops(lay, cfg.hq, cfg.d, True) / oracle_dense_flops(
+        sub, hq_s, cfg.d, True)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
-    return {"sample": what, "frac": frac, "seconds": dt, "cores": int(threads)}
+    est_fwd = t_fwd * scale_f
+    est_fb = t_fb * scale_b if backward else None
+    sample = (f"{'group' if kind == 'group' else 'tree'} 0 of {len(_parts(lay))}{cut}, "
+              f"{hq_s} of {cfg.hq} q heads ({hkv_s} kv heads): fwd {t_fwd:.2f} s"
+              + (f", fwd+bwd {t_fb:.2f} s" if backward else "")
+              + " of the float64 dense-mask oracle, scaled by the oracle's dense work")
+    sig = lambda x: None if x is None else float(f"{x:.4g}")  # noqa: E731
+    return {"sample": sample, "sample_fwd_s": sig(t_fwd), "sample_fwd_bwd_s": sig(t_fb),
+            "est_fwd_s": sig(est_fwd), "est_fwd_bwd_s": sig(est_fb),
+            "tokens_per_s": sig(lay.T_real / (est_fb if backward else est_fwd)),
+            "oracle_dense_gflop": sig(oracle_dense_flops(lay, cfg.hq, cfg.d, backward) / 1e9),
+            "blas_threads": int(threads)}
 
 
 KERNEL_STAGE = {"fwd_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bwd_dq"}
 TRAFFIC_PASSES = ("FETCH_SIZE", "WRITE_SIZE")
+BUSY_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", "GRBM_COUNT")
+N_CU, N_XCD = 256, 8
 
 
-def traffic_from_pmc(pmc_dir: str, calib_mb: int, dtype_tag: str = "bf16") -> dict:
-    """Per attention stage: the kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
-    averaged over its dispatches) from the counter CSVs under pmc_dir, each with the
-    factor that makes the reference negation over calib_mb MiB read and write exactly
-    calib_mb MiB.  Only kernels instantiated for dtype_tag ("bf16" or "fp8") count."""
+def _per_dispatch(pmc_dir: str, counter: str) -> dict:
+    """Kernel name -> the counter per dispatch (summed over its rows, averaged over the
+    kernel's dispatches) from the rocprofv3 counter CSVs under pmc_dir."""
     import csv
     import glob
 
-    def per_dispatch(counter):
-        vals = {}
-        for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
-            with open(f) as fh:
-                for r in csv.DictReader(fh):
-                    if r["Counter_Name"] != counter:
-                        continue
-                    key = (r["Kernel_Name"], r["Dispatch_Id"])
-                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-        by_kernel = {}
-        for (name, _), v in vals.items():
-            by_kernel.setdefault(name, []).append(v)
-        return {k: sum(v) / len(v) for k, v in by_kernel.items()}
+    vals = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (name, _), v in vals.items():
+        by_kernel.setdefault(name, []).append(v)
+    return {k: sum(v) / len(v) for k, v in by_kernel.items()}
 
+
+def _stage_kernels(avg: dict, dtype_tag: str):
+    """(stage, short kernel name, value) of the attention kernels for one input dtype."""
+    for name, val in avg.items():
+        for sym, stage in KERNEL_STAGE.items():
+            if sym in name and f"{dtype_tag}_t" in name:
+                short = name.replace("void ", "").replace("(anonymous namespace)::", "")
+                yield stage, short.replace("psa::", "").rsplit("(", 1)[0], val
+
+
+def traffic_from_pmc(pmc_dir: str, calib_mb: int, dtype_tag: str = "bf16") -> dict:
+    """Per attention stage: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over
+    each kernel's dispatches, summed over the kernels of the stage: at d = 256 a stage
+    is several launches) from the counter CSVs under pmc_dir, each with the factor that
+    makes the reference negation over calib_mb MiB read and write exactly calib_mb MiB.
+    Only kernels instantiated for dtype_tag ("bf16" or "fp8") count."""
     out = {}
     ref_kib = calib_mb * 1024.0
     for counter in TRAFFIC_PASSES:
-        avg = per_dispatch(counter)
+        avg = _per_dispatch(pmc_dir, counter)
         calib = [v for k, v in avg.items() if "elementwise_kernel" in k and v > 0.25 * ref_kib]
         if not calib:
             raise SystemExit(f"no reference negation kernel found for {counter} in {pmc_dir}")
         factor = ref_kib / max(calib)
-        for name, kib in avg.items():
-            for sym, stage in KERNEL_STAGE.items():
-                if sym in name and f"{dtype_tag}_t" in name:
-                    short = name.replace("void ", "").replace("(anonymous namespace)::", "")
-                    short = short.replace("psa::", "").rsplit("(", 1)[0]
-                    e = out.setdefault(stage, {"kernel": short})
-                    e[counter + "_KiB"] = kib
-                    e[counter + "_scale"] = factor
+        for stage, short, kib in _stage_kernels(avg, dtype_tag):
+            e = out.setdefault(stage, {"kernels": []})
+            if short not in e["kernels"]:
+                e["kernels"].append(short)
+            e[counter + "_KiB"] = e.get(counter + "_KiB", 0.0) + kib
+            e[counter + "_scale"] = factor
     for e in out.values():
+        e["kernel"] = " + ".join(e["kernels"])
         if all(c + "_KiB" in e for c in TRAFFIC_PASSES):
             e["bytes_per_launch"] = int(sum(e[c + "_KiB"] * e[c + "_scale"] * 1024
                                             for c in TRAFFIC_PASSES))
     return out
+
+
+def busy_from_pmc(pmc_dir: str, dtype_tag: str = "bf16") -> dict:
+    """Per attention stage, from one rocprofv3 --pmc pass of BUSY_COUNTERS: MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs x 4 SIMDs), CU busy =
+    SQ_BUSY_CU_CYCLES / (GRBM_GUI_ACTIVE / 8 x 256), and the clock GRBM_GUI_ACTIVE /
+    GRBM_COUNT x 100 MHz is not taken here (its reference clock is not documented);
+    cycles are summed over the kernels of a stage."""
+    tot = {}
+    for counter in BUSY_COUNTERS:
+        for stage, short, val in _stage_kernels(_per_dispatch(pmc_dir, counter), dtype_tag):
+            e = tot.setdefault(stage, {"kernels": []})
+            if short not in e["kernels"]:
+                e["kernels"].append(short)
+            e[counter] = e.get(counter, 0.0) + val
+    out = {}
+    for stage, e in tot.items():
+        if not all(c in e for c in BUSY_COUNTERS[:3]) or e["GRBM_GUI_ACTIVE"] <= 0:
+            continue
+        xcd_clk = e["GRBM_GUI_ACTIVE"] / N_XCD
+        out[stage] = {"kernel": " + ".join(e["kernels"]),
+                      "mfma_busy": round(e["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_clk * N_CU * 4), 4),
+                      "cu_busy": round(e["SQ_BUSY_CU_CYCLES"] / (xcd_clk * N_CU), 4),
+                      **{c: e[c] for c in BUSY_COUNTERS if c in e}}
+    return out
+
+
+def busy_summary(pmc_dir: str, workload: str, command: str) -> None:
+    """profiles/busy_<workload>.json from one rocprofv3 --pmc pass of BUSY_COUNTERS."""
+    out = {"kernel_source_hash": kernel_source_hash(), "command": command,
+           "stages": busy_from_pmc(pmc_dir)}
+    path = os.path.join(ROOT, "profiles", f"busy_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(path, {k: v["mfma_busy"] for k, v in out["stages"].items()})
 
 
 def traffic_summary(pmc_dir: str, workload: str, calib_mb: int, command: str,
@@ -265,68 +374,45 @@ def fold_bench(cfg, lay, steps: int, warmup: int) -> dict:
                          "traffic": None, "algorithmic_bytes_per_launch": unfold_bytes}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"])
-    ap.add_argument("--split", action="store_true",
-                    help="backward with P and dS as hi + lo bf16 pairs (PSA_BWD_SPLIT_PDS)")
-    ap.add_argument("--calib-mb", type=int, default=0,
-                    help="before warm-up, run one elementwise negation over this many MiB of "
-                         "fp32 (reads and writes that many bytes): the reference kernel the "
-                         "HBM byte counters are scaled by")
-    ap.add_argument("--traffic-summary", metavar="PMC_DIR",
-                    help="no timing: write the profiles/traffic_*.json files from the two "
-                         "rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) under PMC_DIR")
-    ap.add_argument("--fold", action="store_true",
-                    help="time the fold of the workload's rollout groups and the unfold of a "
-                         "folded [T, hq, d] tensor instead of the attention step (token-form "
-                         "workloads)")
-    ap.add_argument("--form", default="auto", choices=["auto", "nodes"],
-                    help="tile-map encoding: auto (the interval form for packed layouts) or "
-                         "the node form forced (the general encoding, on the same tiles)")
-    ap.add_argument("--layout", default="packed", choices=["packed", "chunked", "bfs"],
-                    help="packed (as the workload states); chunked: each group's completions "
-                         "interleaved in turns of 64 tokens after its prompt (token-form "
-                         "workloads); bfs: tree nodes in breadth-first order (tree workloads). "
-                         "Both keep the kept pairs; the map takes the node form")
-    ap.add_argument("--nograd", default=None, choices=["bf16", "fp8"],
-                    help="time the no-grad forward (no LSE stored) in this input dtype "
-                         "instead of the workload's passes: map build + forward")
-    ap.add_argument("--traffic-command", default="",
-                    help="with --traffic-summary: the command line the passes ran, recorded")
-    args = ap.parse_args()
-    if args.traffic_summary:
-        from shared_prefix_block_amd import workloads as wl
-        traffic_summary(args.traffic_summary, wl.WORKLOADS[args.workload].name,
-                        args.calib_mb or 512, args.traffic_command, args.nograd or "")
-        return
+def _stats(xs) -> dict:
+    import numpy as np
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures the single-GPU hot path only: the shared-prefix attention "
-              "path has no cross-GPU step here (groups and heads shard with no communication); "
-              "run it with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4)}
 
+
+def _profile_json(prefix: str, workload: str):
+    """A committed counter summary of this workload, if its kernel sources are the
+    current ones (else None: the counters were taken on other code)."""
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t
+
+
+def run_config(idx: int, args, cold_iters: int = 5) -> dict:
+    """Time one workload: K steps of (map build, forward, backward as psa_bwd runs it:
+    dQ with the preparation of its rows, then dK/dV) after W warm-up steps; HIP events
+    on the launch stream around every stage of every step, and the wall clock between
+    two device synchronisations around the K steps.  Then cold_iters steps, each after
+    a 512 MiB write that evicts the 256 MB last-level cache (outside the timed stages)."""
+    import numpy as np
     import torch
 
     from shared_prefix_block_amd import psa
     from shared_prefix_block_amd import workloads as wl
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    psa.load()
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cfg = wl.WORKLOADS[args.workload]
+    cfg = wl.WORKLOADS[idx]
     lay = wl.layout_for(cfg)
     if args.layout == "chunked":
         if lay.kind != "tokens":
             sys.exit("--layout chunked needs a token-form workload")
-        import numpy as np
         lay = wl.shuffled_tokens_layout(lay.specs, np.random.default_rng(cfg.idx),
                                         prompt_first=True, relabel=False, chunk=64,
                                         n_pad=lay.T - lay.T_real)
@@ -335,15 +421,11 @@ def main():
             sys.exit("--layout bfs needs a tree workload")
         nl, paths = wl.reorder_tree(lay.node_lengths, lay.sample_paths)
         lay = wl.tree_layout(nl, paths, extra_pad=lay.T - lay.T_real)
-    if args.layout != "packed" or lay.kind == "draft":
-        args.no_cpu_baseline = True  # the oracle's sample slices packed groups
     if args.fold:
         if lay.kind != "tokens":
             sys.exit("--fold needs a token-form workload (rollout groups)")
-        print(json.dumps(fold_bench(cfg, lay, args.steps, args.warmup)), flush=True)
-        return
+        return {"fold": fold_bench(cfg, lay, args.steps, args.warmup)}
     if args.nograd:
-        args.no_cpu_baseline = True
         q, k, v, do = wl.make_tensors(lay.T, cfg.hq, cfg.hkv, cfg.d, args.nograd, cfg.sigma,
                                       cfg.idx, with_grad_out=False)
         passes = f"fwd, no grad (no LSE), {args.nograd} inputs"
@@ -362,8 +444,11 @@ def main():
     o = torch.empty(q.shape, device=dev,
                     dtype=torch.bfloat16 if tdt == torch.float8_e4m3fn else tdt)
     lse = None if args.nograd else torch.empty(cfg.hq, lay.T, device=dev, dtype=torch.float32)
-    grads = (torch.empty(q.shape, dtype=gdt, device=dev), torch.empty(k.shape, dtype=gdt, device=dev),
-             torch.empty(v.shape, dtype=gdt, device=dev))
+    grads = None
+    if backward:
+        grads = (torch.empty(q.shape, dtype=gdt, device=dev),
+                 torch.empty(k.shape, dtype=gdt, device=dev),
+                 torch.empty(v.shape, dtype=gdt, device=dev))
     stream = torch.cuda.current_stream(dev)
 
     def build_map():
@@ -380,7 +465,6 @@ def main():
     info = dict(m0.info)
     del m0
 
-    # the backward as psa_bwd runs it: dQ with the preparation of its rows, then dK/dV
     names = ["map", "fwd"] + (["bwd_dq", "bwd_dkdv"] if backward else [])
     stage_of = {"bwd_dq": psa.STAGE_PREPARE | psa.STAGE_DQ, "bwd_dkdv": psa.STAGE_DKDV}
 
@@ -409,25 +493,43 @@ def main():
         step()
     torch.cuda.synchronize(dev)
 
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+
     # timed region: K full steps, wall clock between two device synchronisations
-    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-                  for _ in range(args.steps)]
+    all_events = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     maps = []
-    for s in range(args.steps):
-        maps.append(step(all_events[s]))
+    for s_ in range(args.steps):
+        maps.append(step(all_events[s_]))
         if len(maps) > 2:
             maps.pop(0)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     del maps
 
-    per = {nm: [] for nm in names}
-    for evs in all_events:
-        for i, nm in enumerate(names):
-            per[nm].append(evs[i].elapsed_time(evs[i + 1]))
-    avg = {nm: sum(x) / len(x) for nm, x in per.items()}
+    def stage_times(events_list):
+        per = {nm: [] for nm in names}
+        for evs in events_list:
+            for i, nm in enumerate(names):
+                per[nm].append(evs[i].elapsed_time(evs[i + 1]))
+        return per
+
+    per = stage_times(all_events)
+    cold = []
+    if cold_iters and not args.no_cold:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for i in range(cold_iters):
+            scratch.fill_(i + 1)  # 512 MiB written: the last-level cache holds none of the inputs
+            torch.cuda.synchronize(dev)
+            evs = new_events()
+            m = step(evs)
+            torch.cuda.synchronize(dev)
+            cold.append(evs)
+            del m
+        del scratch
+    cper = stage_times(cold) if cold else None
 
     kept = kept_pairs(lay)
     tiles = info["n_full"] + info["n_partial"]
@@ -436,25 +538,161 @@ def main():
     tile_flops = tiles * TILE * TILE * hq * (f_fwd + (f_bwd if backward else 0))
     kept_flops = kept * hq * (f_fwd + (f_bwd if backward else 0))
     ms_step = wall * 1e3 / args.steps
-    value = tile_flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype_name]
-    dom_peak = PEAK_FP8_FWD if dtype_name == "fp8" else peak
-
-    # dominant kernel: algorithmic FLOPs per launch (fwd 4d; dK/dV 8d = S, dP, dV, dK;
-    # dQ 2d: its S and dP are recomputations) per kept pair per q head
-    algo = {"fwd": 4 * d, "bwd_dkdv": 8 * d, "bwd_dq": 2 * d}
-    cand = {k_: avg[k_] for k_ in algo if k_ in avg}
-    dom = max(cand, key=cand.get)
-    achieved = kept * hq * algo[dom] / (avg[dom] * 1e-3) / 1e12
-    traffic = None
+    fwd_peak = PEAK_FP8_FWD if dtype_name == "fp8" else peak
+    med = {nm: float(np.median(per[nm])) for nm in names}
+    mean = {nm: sum(per[nm]) / len(per[nm]) for nm in names}
+    t_fwd = med["fwd"]
+    t_bwd = med["bwd_dq"] + med["bwd_dkdv"] if backward else 0.0
+    res = {
+        "workload": describe(cfg, lay, args.layout, args.form), "name": cfg.name,
+        "T": lay.T, "T_real": lay.T_real, "map_form": ["interval", "nodes"][info["form"]],
+        "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": d, "dtype": dtype_name, "passes": passes,
+        "sigma": cfg.sigma,
+        "grad_dtype": args.grad_dtype if backward else None,
+        "bwd_p_ds": (("hi+lo bf16" if args.split else "bf16, hi+lo where large")
+                     if backward and dtype_name == "bf16" else None),
+        "tiles_128": {"full": info["n_full"], "partial": info["n_partial"]},
+        "kept_pairs_per_head": kept,
+        "ms_per_step": round(ms_step, 4),
+        "tflops_unmasked_tiles": round(tile_flops / (ms_step * 1e-3) / 1e12, 2),
+        "tflops_kept_pairs": round(kept_flops / (ms_step * 1e-3) / 1e12, 2),
+        f"pct_{dtype_name}_peak": round(100 * tile_flops / (ms_step * 1e-3) / 1e12 / peak, 2),
+        "fwd_pct_peak": round(100 * kept * hq * f_fwd / (t_fwd * 1e-3) / 1e12 / fwd_peak, 2),
+        "bwd_pct_peak": (round(100 * kept * hq * f_bwd / (t_bwd * 1e-3) / 1e12 / peak, 2)
+                         if backward else None),
+        "tokens_per_s": round(lay.T_real / ((t_fwd + t_bwd) * 1e-3), 1),
+        "stage_ms": {nm: _stats(per[nm]) for nm in names},
+        "cold_stage_ms": ({nm: _stats(cper[nm]) for nm in names} if cper else None),
+    }
+    # MFMA busy and HBM rate of the attention kernels: committed rocprofv3 counter
+    # summaries of this workload, when they were taken on the current kernel sources
     variant = f"_nograd_{args.nograd}" if args.nograd else ""
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{dom}{variant}_{cfg.name}.json")
-    if os.path.exists(tpath):
-        with open(tpath) as fh:
-            t = json.load(fh)
-        if t.get("kernel_source_hash") == kernel_source_hash():
-            traffic = t.get("bytes_per_launch")
+    if args.layout == "packed" and args.form == "auto" and not args.split:
+        busy = _profile_json("busy" + variant, cfg.name)
+        if busy:
+            res["mfma_busy"] = {st: e["mfma_busy"] for st, e in busy["stages"].items()
+                                if st in med}
+        hbm = {}
+        for st in names[1:]:
+            t = _profile_json(f"traffic_{st}{variant}", cfg.name)
+            if t and t.get("bytes_per_launch"):
+                hbm[st] = {"bytes_per_launch": t["bytes_per_launch"],
+                           "gb_per_s": round(t["bytes_per_launch"] / (med[st] * 1e-3) / 1e9, 1)}
+        if hbm:
+            res["hbm"] = hbm
+    # the dominant kernel: algorithmic FLOPs per launch (fwd 4d; dK/dV 8d = S, dP, dV,
+    # dK; dQ 2d: its S and dP are recomputations) per kept pair per q head, over its
+    # event-timed average launch
+    algo = {"fwd": 4 * d, "bwd_dkdv": 8 * d, "bwd_dq": 2 * d}
+    cand = {k_: mean[k_] for k_ in algo if k_ in mean}
+    dom = max(cand, key=cand.get)
+    dom_peak = fwd_peak if dom == "fwd" else peak
+    achieved = kept * hq * algo[dom] / (mean[dom] * 1e-3) / 1e12
+    traffic = None
+    t = _profile_json(f"traffic_{dom}{variant}", cfg.name)
+    if t and args.layout == "packed" and args.form == "auto":
+        traffic = t.get("bytes_per_launch")
+    res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                       "peak": round(dom_peak, 1), "unit": "TFLOP/s",
+                       "frac": round(achieved / dom_peak, 4), "traffic": traffic,
+                       "algorithmic_flops_per_launch": kept * hq * algo[dom],
+                       "avg_launch_ms": round(mean[dom], 4)}
+    res["_tile_flops"] = tile_flops
+    if not args.no_cpu_baseline and args.layout == "packed" and lay.kind != "draft" \
+            and not args.nograd:
+        del q, k, v, do, o, lse, grads, ws
+        torch.cuda.empty_cache()
+        res["cpu_oracle"] = cpu_baseline(cfg, lay)
+    return res
 
+
+HEADLINE = 4  # the largest single-GPU workload: 19.5 TFLOP of kept-pair work per step
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=None,
+                    help="time this workload alone (default: the long-prompt workload 4 as "
+                         "the headline, and every workload 1-5 in the same line)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps")
+    ap.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--split", action="store_true",
+                    help="backward with P and dS as hi + lo bf16 pairs (PSA_BWD_SPLIT_PDS)")
+    ap.add_argument("--calib-mb", type=int, default=0,
+                    help="before warm-up, run one elementwise negation over this many MiB of "
+                         "fp32 (reads and writes that many bytes): the reference kernel the "
+                         "HBM byte counters are scaled by")
+    ap.add_argument("--traffic-summary", metavar="PMC_DIR",
+                    help="no timing: write the profiles/traffic_*.json files from the two "
+                         "rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) under PMC_DIR")
+    ap.add_argument("--busy-summary", metavar="PMC_DIR",
+                    help="no timing: write profiles/busy_<workload>.json from one rocprofv3 "
+                         "counter pass of " + " ".join(BUSY_COUNTERS) + " under PMC_DIR")
+    ap.add_argument("--fold", action="store_true",
+                    help="time the fold of the workload's rollout groups and the unfold of a "
+                         "folded [T, hq, d] tensor instead of the attention step (token-form "
+                         "workloads)")
+    ap.add_argument("--form", default="auto", choices=["auto", "nodes"],
+                    help="tile-map encoding: auto (the interval form for packed layouts) or "
+                         "the node form forced (the general encoding, on the same tiles)")
+    ap.add_argument("--layout", default="packed", choices=["packed", "chunked", "bfs"],
+                    help="packed (as the workload states); chunked: each group's completions "
+                         "interleaved in turns of 64 tokens after its prompt (token-form "
+                         "workloads); bfs: tree nodes in breadth-first order (tree workloads). "
+                         "Both keep the kept pairs; the map takes the node form")
+    ap.add_argument("--nograd", default=None, choices=["bf16", "fp8"],
+                    help="time the no-grad forward (no LSE stored) in this input dtype "
+                         "instead of the workload's passes: map build + forward")
+    ap.add_argument("--traffic-command", default="",
+                    help="with --traffic-summary / --busy-summary: the command line the "
+                         "counter passes ran, recorded")
+    args = ap.parse_args()
+    if args.traffic_summary or args.busy_summary:
+        from shared_prefix_block_amd import workloads as wl
+        name = wl.WORKLOADS[args.workload or HEADLINE].name
+        if args.traffic_summary:
+            traffic_summary(args.traffic_summary, name, args.calib_mb or 512,
+                            args.traffic_command, args.nograd or "")
+        if args.busy_summary:
+            busy_summary(args.busy_summary, name, args.traffic_command)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures the single-GPU hot path only: the shared-prefix attention "
+              "path has no cross-GPU step here (groups and heads shard with no communication); "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from shared_prefix_block_amd import psa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    psa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    head = args.workload or HEADLINE
+    special = (args.fold or args.nograd or args.layout != "packed" or args.form != "auto"
+               or args.split or args.grad_dtype != "fp32")
+    order = [head] if (args.workload or special) else [head] + [i for i in (1, 2, 3, 5)]
+    results = {}
+    for idx in order:
+        print(f"# workload {idx}", file=sys.stderr, flush=True)
+        results[idx] = run_config(idx, args)
+        torch.cuda.empty_cache()
+        if "fold" in results[idx]:
+            print(json.dumps(results[idx]["fold"]), flush=True)
+            return
+    h = results[head]
+    tile_flops = h.pop("_tile_flops")
+    for r in results.values():
+        r.pop("_tile_flops", None)
+    value = tile_flops / (h["ms_per_step"] * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -462,41 +700,34 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype_name,
-        "data": "synthetic (seeded N(0, sigma) Q/K/V/dO; layout as the workload states)",
-        "config": {"workload": describe(cfg, lay, args.layout, args.form), "T": lay.T,
-                   "T_real": lay.T_real, "map_form": ["interval", "nodes"][info["form"]],
-                   "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": d,
-                   "passes": passes, "grad_dtype": args.grad_dtype if backward else None,
-                   "bwd_p_ds": (("hi+lo bf16" if args.split else "bf16, hi+lo where large")
-                                if backward else None),
-                   "tiles_128": {"full": info["n_full"], "partial": info["n_partial"]},
-                   "kept_pairs_per_head": kept},
-        f"pct_{dtype_name}_peak": round(100 * value / peak, 2),
-        "kept_pair_tflops": round(kept_flops / (ms_step * 1e-3) / 1e12, 2),
-        "tokens_per_s": round(lay.T_real / (ms_step * 1e-3), 1),
-        "stage_ms": {nm: round(avg[nm], 4) for nm in names},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": round(dom_peak, 1), "unit": "TFLOP/s",
-                     "frac": round(achieved / dom_peak, 4),
-                     "traffic": traffic,
-                     "algorithmic_flops_per_launch": kept * hq * algo[dom],
-                     "avg_launch_ms": round(avg[dom], 4)},
+        "dtype": h["dtype"],
+        "data": "synthetic (seeded N(0, sigma) Q/K/V, N(0,1) dO; layouts as the workloads state)",
+        "config": {"workload": h["workload"], "T": h["T"], "T_real": h["T_real"],
+                   "map_form": h["map_form"], "hq": h["hq"], "hkv": h["hkv"],
+                   "head_dim": h["head_dim"], "passes": h["passes"],
+                   "grad_dtype": h["grad_dtype"], "bwd_p_ds": h["bwd_p_ds"],
+                   "tiles_128": h["tiles_128"], "kept_pairs_per_head": h["kept_pairs_per_head"]},
+        f"pct_{h['dtype']}_peak": h[f"pct_{h['dtype']}_peak"],
+        "kept_pair_tflops": h["tflops_kept_pairs"],
+        "fwd_pct_peak": h["fwd_pct_peak"],
+        "bwd_pct_peak": h["bwd_pct_peak"],
+        "tokens_per_s": h["tokens_per_s"],
+        "stage_ms": h["stage_ms"],
+        "roofline": h["roofline"],
     }
-    if not args.no_cpu_baseline:
-        cb = cpu_baseline(cfg, lay)
-        work_tile_flops = tile_flops * cb["frac"]
-        out["cpu_baseline"] = {"value": round(work_tile_flops / cb["seconds"] / 1e12, 6),
-                               "unit": "TFLOP/s", "cores": cb["cores"], "kind": "oracle",
-                               "sample": f"{cb['sample']}: {cb['seconds']:.2f} s of float64 "
-                                         f"dense-mask oracle "
-                                         f"({'fwd' if not backward else 'fwd+bwd'}), "
-                                         f"scaled by its share {cb['frac']:.4f} of the "
-                                         f"workload's kept pairs"}
+    if "cpu_oracle" in h:
+        c = h["cpu_oracle"]
+        est = c["est_fwd_bwd_s"] or c["est_fwd_s"]
+        out["cpu_baseline"] = {"value": round(tile_flops / est / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": c["blas_threads"], "kind": "oracle",
+                               "sample": c["sample"],
+                               "affinity_cores": len(os.sched_getaffinity(0)),
+                               "cpu_model": cpu_model()}
+    out["configs"] = {str(i): r for i, r in results.items()}
     print(json.dumps(out), flush=True)
 
 

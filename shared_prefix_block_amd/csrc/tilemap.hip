@@ -24,10 +24,13 @@
 // pre-order range of its node's subtree, and keep(q, kv) is kv <= q with q's node in
 // kv's subtree, which is the same rule written on nodes.
 #include <hip/hip_runtime.h>
-#include <hipcub/hipcub.hpp>
 
 #include <climits>
 #include <cstdint>
+#include <cstring>
+
+#include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_select.hpp>
 
 #include "psa_internal.h"
 
@@ -802,8 +805,8 @@ size_t tokens_nodes_scratch_bytes(int64_t T) {
   size_t sort_b = 0, uniq_b = 0;
   uint64_t* none = nullptr;
   int64_t* cnt = nullptr;
-  (void)hipcub::DeviceRadixSort::SortKeys(nullptr, sort_b, none, none, int64_t(n), 0, 64);
-  (void)hipcub::DeviceSelect::Unique(nullptr, uniq_b, none, none, cnt, int64_t(n));
+  (void)rocprim::radix_sort_keys(nullptr, sort_b, none, none, n, 0, 64);
+  (void)rocprim::unique(nullptr, uniq_b, none, none, cnt, n);
   const size_t arr = (n * 8 + 255) / 256 * 256;
   return 3 * arr + 256 + (sort_b > uniq_b ? sort_b : uniq_b);
 }
@@ -829,10 +832,11 @@ hipError_t launch_tokens_nodes(int64_t T, const int32_t* group, const int32_t* s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   size_t b = tmp_bytes;
-  e = hipcub::DeviceRadixSort::SortKeys(tmp, b, comp, sorted, T, 0, 64, stream);
+  e = rocprim::radix_sort_keys(tmp, b, comp, sorted, size_t(T), 0, 64, stream);
   if (e != hipSuccess) return e;
   b = tmp_bytes;
-  e = hipcub::DeviceSelect::Unique(tmp, b, sorted, uniq, n_uniq, T, stream);
+  e = rocprim::unique(tmp, b, sorted, uniq, n_uniq, size_t(T), rocprim::equal_to<uint64_t>(),
+                      stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_node_number, dim3(unsigned(blocks)), dim3(256), 0, stream, T, group,
                      is_prefix, comp, uniq, n_uniq, key, lo, w);
@@ -855,8 +859,7 @@ size_t draft_scratch_bytes(int64_t n_blocks) {
   size_t sort_b = 0;
   uint64_t* none = nullptr;
   int32_t* ni = nullptr;
-  (void)hipcub::DeviceRadixSort::SortPairs(nullptr, sort_b, none, none, ni, ni, int64_t(n), 0,
-                                           64);
+  (void)rocprim::radix_sort_pairs(nullptr, sort_b, none, none, ni, ni, n, 0, 64);
   const size_t a8 = (n * 8 + 255) / 256 * 256, a4 = (n * 4 + 255) / 256 * 256;
   return 2 * a8 + 3 * a4 + sort_b;
 }
@@ -885,8 +888,8 @@ hipError_t launch_draft_nodes(int64_t T, int64_t S, int32_t bs, int64_t n_blocks
     hipLaunchKernelGGL(k_draft_composite, dim3(unsigned(blocks)), dim3(256), 0, stream, S,
                        n_blocks, anchors, keep, anchor_doc, comp, idx, err);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = hipcub::DeviceRadixSort::SortPairs(tmp, tmp_bytes, comp, sorted, idx, order, n_blocks,
-                                           0, 64, stream);
+    e = rocprim::radix_sort_pairs(tmp, tmp_bytes, comp, sorted, idx, order, size_t(n_blocks), 0,
+                                  64, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_draft_rank, dim3(unsigned(blocks)), dim3(256), 0, stream, n_blocks,
                        sorted, order, rank);

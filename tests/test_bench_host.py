@@ -82,3 +82,52 @@ def test_traffic_needs_the_reference_copy(tmp_path):
                [(1, DKDV, "FETCH_SIZE", 1.0), (1, DKDV, "WRITE_SIZE", 1.0)])
     with pytest.raises(SystemExit, match="reference negation"):
         bench.traffic_from_pmc(str(tmp_path), 64)
+
+
+DKDV1 = "void psa::(anonymous namespace)::dkdv_kernel<psa::bf16_t, float, 256, 0, 1, false, 1>(BwdParams)"
+DKDV2 = "void psa::(anonymous namespace)::dkdv_kernel<psa::bf16_t, float, 256, 0, 2, false, 1>(BwdParams)"
+
+
+def test_traffic_sums_the_launches_of_a_stage(tmp_path):
+    """At d = 256 dK/dV is two launches (dV pass, dK pass): the stage's bytes are the sum."""
+    kib = 64 * 1024.0
+    _write_pmc(str(tmp_path / "F" / "run_counter_collection.csv"), [
+        (1, NEG, "FETCH_SIZE", kib / 2), (2, DKDV1, "FETCH_SIZE", 100.0),
+        (3, DKDV2, "FETCH_SIZE", 300.0), (1, NEG, "WRITE_SIZE", kib),
+        (2, DKDV1, "WRITE_SIZE", 10.0), (3, DKDV2, "WRITE_SIZE", 30.0)])
+    out = bench.traffic_from_pmc(str(tmp_path), 64)
+    assert out["bwd_dkdv"]["bytes_per_launch"] == int((400.0 * 2 + 40.0) * 1024)
+    assert out["bwd_dkdv"]["kernel"].count("dkdv_kernel") == 2
+
+
+def test_mfma_busy_arithmetic(tmp_path):
+    """MFMA busy = MFMA busy cycles over (GRBM_GUI_ACTIVE / 8 XCDs) x 256 CUs x 4 SIMDs,
+    cycles summed over a stage's kernels and averaged over dispatches."""
+    act = 8 * 1000.0  # 1000 busy clocks per XCD
+    _write_pmc(str(tmp_path / "B" / "run_counter_collection.csv"), [
+        (1, DKDV, "GRBM_GUI_ACTIVE", act), (1, DKDV, "SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * 1000 * 1024),
+        (1, DKDV, "SQ_BUSY_CU_CYCLES", 0.5 * 1000 * 256), (1, DKDV, "GRBM_COUNT", 8 * 2000.0),
+        (2, DKDV, "GRBM_GUI_ACTIVE", act), (2, DKDV, "SQ_VALU_MFMA_BUSY_CYCLES", 0.75 * 1000 * 1024),
+        (2, DKDV, "SQ_BUSY_CU_CYCLES", 0.5 * 1000 * 256), (2, DKDV, "GRBM_COUNT", 8 * 2000.0),
+        (3, FWD32, "GRBM_GUI_ACTIVE", act)])
+    out = bench.busy_from_pmc(str(tmp_path))
+    assert set(out) == {"bwd_dkdv"}
+    assert out["bwd_dkdv"]["mfma_busy"] == pytest.approx(0.5)
+    assert out["bwd_dkdv"]["cu_busy"] == pytest.approx(0.5)
+
+
+def test_oracle_dense_work_and_bounded_sample():
+    """The oracle's dense work is per group: sum of |group|^2 x hq x (4 or 12) d; the
+    sample shrinks heads, then completions, to fit the budget, and its times scale to
+    the workload by that work."""
+    from shared_prefix_block_amd import workloads as wl
+    cfg = wl.WORKLOADS[2]
+    lay = wl.layout_for(cfg)
+    assert bench.oracle_dense_flops(lay, 32, 128, False) == 8 * 2560 ** 2 * 32 * 4 * 128
+    assert bench.oracle_dense_flops(lay, 32, 128, True) == 8 * 2560 ** 2 * 32 * 12 * 128
+    c = bench.cpu_baseline(cfg, lay, budget_flop=1e9)
+    assert "4 of 32 q heads (1 kv heads)" in c["sample"]
+    assert "with 1 of its 8 completions" in c["sample"]
+    scale = bench.oracle_dense_flops(lay, 32, 128, True) / (768 ** 2 * 4 * 12 * 128)
+    assert c["est_fwd_bwd_s"] == pytest.approx(c["sample_fwd_bwd_s"] * scale, rel=1e-2, abs=0.02)
+    assert c["tokens_per_s"] > 0 and c["blas_threads"] >= 1
