@@ -274,6 +274,25 @@ psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtyp
                    size_t workspace_bytes, void* stream);
 
 /*
+ * psa_bwd without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It runs what psa_bwd runs, with the workspace in
+ * a fixed device array that the library holds on each GPU it runs on until the
+ * process ends (looked up, not allocated, on a device's first call).  Limit: the
+ * backward's workspace, 2 x T x hq x 4 bytes (each plane rounded up to 256 bytes),
+ * must fit in 32 MiB (T x hq <= 4,194,240), else PSA_ERR_WORKSPACE before any launch.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one GPU (on
+ * different streams without ordering) race and must not be issued.  The array keeps
+ * the last call's contents, every byte a call reads is written by that call first.
+ * Arguments and other errors as psa_bwd.
+ */
+psa_status psa_bwd_noalloc(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype,
+                           int64_t T, int32_t hq, int32_t hkv, int32_t d, float scale,
+                           const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           void* stream);
+
+/*
  * The backward in stages, for callers that time or overlap them (psa_bwd runs all
  * three), with options.  flags is the OR of a nonzero set of stages:
  *   PSA_STAGE_PREPARE  D = rowsum(dO * O) and LSE in log2 units, into the workspace

@@ -823,6 +823,35 @@ psa_status psa_bwd(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtyp
                         dq, dk, dv, workspace, workspace_bytes, PSA_STAGE_ALL, stream);
 }
 
+psa_status psa_bwd_noalloc(const psa_tile_map* map, psa_dtype dtype, psa_dtype grad_dtype,
+                           int64_t T, int32_t hq, int32_t hkv, int32_t d, float scale,
+                           const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           void* stream) {
+  psa_status st = check_attn_args(map, dtype, T, hq, hkv, d, scale, PSA_PASS_BWD);
+  if (st != PSA_OK) return st;
+  if (grad_dtype != PSA_FP32 && grad_dtype != dtype)
+    return psa_set_error(PSA_ERR_DTYPE, "grad_dtype must be PSA_FP32 or the input dtype");
+  const size_t need = bwd_workspace_bytes(AttnShape{T, hq, hkv, d, 1.0f});
+  if (need > kBwdScratchBytes)
+    return psa_set_error(PSA_ERR_WORKSPACE,
+                         "psa_bwd_noalloc: these sizes need " + std::to_string(need) +
+                             " bytes of scratch, above its fixed " +
+                             std::to_string(kBwdScratchBytes) +
+                             " (2 x T x hq x 4 bytes); use psa_bwd with a workspace");
+  if (T == 0) return PSA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return psa_set_error(PSA_ERR_NULL, "tensor pointer is NULL");
+  void* ws = nullptr;
+  hipError_t e = bwd_scratch(&ws);
+  if (e != hipSuccess) return psa_hip_error(e, "device scratch of psa_bwd_noalloc");
+  AttnShape s{T, hq, hkv, d, scale > 0.f ? scale : 1.0f / std::sqrt(float(d))};
+  e = launch_bwd(*map, dtype, grad_dtype, s, q, k, v, o, lse, dout, dq, dk, dv, ws,
+                 PSA_STAGE_ALL, false, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return psa_hip_error(e, "backward launch");
+  return PSA_OK;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -1114,6 +1115,32 @@ bool bwd_supported(psa_dtype dt, int32_t d) {
 
 size_t bwd_workspace_bytes(const AttnShape& s) {
   return 2 * psa::ws_align(size_t(s.T) * s.hq * sizeof(float));
+}
+
+// The backward's workspace (D and LSE in log2 units, [hq, T] fp32 each) for callers
+// that cannot allocate: a file-scope device array, of which each GPU the library runs
+// on holds its own copy until the process ends.  In host code its name is only a
+// stand-in; the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[kBwdScratchBytes / sizeof(float)];
+
+hipError_t bwd_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype gdt, const AttnShape& s,

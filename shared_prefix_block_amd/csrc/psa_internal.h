@@ -139,6 +139,10 @@ hipError_t launch_fwd(const psa_tile_map& map, psa_dtype dt, const AttnShape& s,
                       hipStream_t stream);
 
 size_t bwd_workspace_bytes(const AttnShape& s);
+// The fixed device scratch of psa_bwd_noalloc (attn_bwd.hip): its size, and its
+// address on the current device (looked up once per device, never allocated).
+constexpr size_t kBwdScratchBytes = size_t{32} << 20;
+hipError_t bwd_scratch(void** ptr);
 hipError_t launch_bwd(const psa_tile_map& map, psa_dtype dt, psa_dtype grad_dt, const AttnShape& s,
                       const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -33,7 +33,7 @@ EXPORTS = ["psa_abi_version", "psa_status_string", "psa_last_error", "psa_tile_s
            "psa_tile_map_export", "psa_tile_map_destroy", "psa_fwd", "psa_bwd_workspace_size",
            "psa_bwd", "psa_bwd_stages", "psa_fold_workspace_size", "psa_fold_rollouts",
            "psa_unfold_rows", "psa_build_tile_map_tokens_ex", "psa_build_tile_map_tree_ex",
-           "psa_tile_map_export_nodes", "psa_build_tile_map_draft"]
+           "psa_tile_map_export_nodes", "psa_build_tile_map_draft", "psa_bwd_noalloc"]
 FORM_INTERVAL, FORM_NODES = 0, 1  # mask encodings of a map (info["form"])
 MAP_NODE_FORM = 1  # build flag: the node form even where the interval form exists
 DRAFT_CAUSAL = 1  # flag of psa_build_tile_map_draft: causal attention inside a block
@@ -97,6 +97,8 @@ def load() -> ctypes.CDLL:
                                        P, P, P, P, P, P, P, P, SZ, P]),
             "psa_bwd_stages": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, I64, I32, I32, I32, F,
                                               P, P, P, P, P, P, P, P, P, P, SZ, I32, P]),
+            "psa_bwd_noalloc": (ctypes.c_int, [P, ctypes.c_int, ctypes.c_int, I64, I32, I32, I32,
+                                               F, P, P, P, P, P, P, P, P, P, P]),
             "psa_fold_workspace_size": (ctypes.c_int, [I64, I64, ctypes.POINTER(SZ)]),
             "psa_fold_rollouts": (ctypes.c_int, [I64, P, P, P, P, P, I64, I32, I32, P, P, P, P,
                                                  P, P, P, SZ, P]),
