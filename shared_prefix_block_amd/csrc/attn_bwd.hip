@@ -629,8 +629,11 @@ struct DqCfg {
   static constexpr int BM = 32 * NW;
   static_assert(BM == kTileM, "q-tile must match the map");
   static constexpr int EB = int(sizeof(T));
-  // keys per sub-step: 32 where 64 would not fit two waves per SIMD in registers
-  static constexpr int BN = (D * EB > (kBf16 ? 128 : 256)) ? 32 : 64;
+  // keys per sub-step (one LDS stage, one barrier): bf16 stages 64 keys up to d = 128
+  // and runs the math in blocks of 32 keys (the dQ products of a block right after its
+  // dS, so two waves fit on a SIMD); fp32 and bf16 d = 256 stage 32 where 64 would not
+  // fit in registers or LDS
+  static constexpr int BN = kBf16 ? (D <= 128 ? 64 : 32) : (D * EB > 256 ? 32 : 64);
   static constexpr int NSUB = kTileN / BN;
   static constexpr int NS = D + (kBf16 ? 32 : 16) / EB;  // see DkdvCfg::NS
   static constexpr int TS = BN + 16 / EB;
@@ -836,12 +839,14 @@ void dq_kernel(BwdParams p) {
                                 : es0 + b * C::MW * C::BN;
 
     // keys of a partial tile all after this wave's rows: no kept pair (kv <= q is
-    // part of every causal mask), nothing to add to dQ
-    if (!(partial && p.causal && kv0i > wave_last)) {
+    // part of every causal mask), nothing to add to dQ (the DMA path decides per block
+    // of 32 keys)
+    if (C::kDma || !(partial && p.causal && kv0i > wave_last)) {
       const int qd = qrow_i - kv0i;
-      float ds[C::BN / 32][16];
+      float ds[C::kDma ? 1 : C::BN / 32][16];
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb) {
+        if (C::kDma && partial && p.causal && kv0i + 32 * kb > wave_last) continue;
         f32x16 sacc = zero16(), pacc = zero16();
         if constexpr (C::kDma) {
           // K and V fragments read PF reduction steps ahead of their MFMAs
@@ -923,45 +928,47 @@ void dq_kernel(BwdParams p) {
             }
           }
         }
+        float* const dsk = ds[C::kDma ? 0 : kb];
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) ds[kb][ii] = pv[ii] * (pacc[ii] - dl);
+        for (int ii = 0; ii < 16; ++ii) dsk[ii] = pv[ii] * (pacc[ii] - dl);
+        if constexpr (C::kDma) {
+          // dQ^T += K^T dS^T over this block's 32 keys (16-key fragments t): dS rounded,
+          // the (t, db) transposed K reads PF products ahead of their MFMAs; then, where
+          // split_wanted, the residuals
+          constexpr int ND = D / 32, NI = 2 * ND, PF = 3;
+          Frag<T> sf[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) sf[t] = frag_from<T>(dsk + 8 * t);
+          Frag<T> ka[PF];
+#pragma unroll
+          for (int i = 0; i < PF - 1; ++i)
+            ka[i] = frag_load_tr_swz<D / 8>(st, 32 * kb + 16 * (i / ND), 32 * (i % ND));
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            if (i + PF - 1 < NI) {
+              const int j = i + PF - 1;
+              ka[j % PF] = frag_load_tr_swz<D / 8>(st, 32 * kb + 16 * (j / ND), 32 * (j % ND));
+            }
+            mma(adq[i % ND], ka[i % PF], sf[i / ND]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 2);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            if (i + PF - 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (split_wanted<T, MODE, false>(nullptr, dsk + 8 * t)) {
+              const Frag<T> sl = frag_residual(dsk + 8 * t, sf[t]);
+#pragma unroll
+              for (int db = 0; db < ND; ++db)
+                mma(adq[db], frag_load_tr_swz<D / 8>(st, 32 * kb + 16 * t, 32 * db), sl);
+            }
+          }
+        }
       }
-      if constexpr (C::kDma) {
-        // dQ^T += K^T dS^T: dS rounded, the (t, db) transposed K reads PF products
-        // ahead of their MFMAs; then, where split_wanted, the residuals
-        constexpr int ND = D / 32, NT16 = C::BN / 16, NI = NT16 * ND, PF = 3;
-        Frag<T> sf[NT16];
-#pragma unroll
-        for (int t = 0; t < NT16; ++t) sf[t] = frag_from<T>(&ds[t >> 1][(t & 1) * 8]);
-        Frag<T> ka[PF];
-#pragma unroll
-        for (int i = 0; i < PF - 1; ++i)
-          ka[i] = frag_load_tr_swz<D / 8>(st, 16 * (i / ND), 32 * (i % ND));
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          if (i + PF - 1 < NI) {
-            const int j = i + PF - 1;
-            ka[j % PF] = frag_load_tr_swz<D / 8>(st, 16 * (j / ND), 32 * (j % ND));
-          }
-          mma(adq[i % ND], ka[i % PF], sf[i / ND]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF - 1), 2);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          if (i + PF - 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-        }
-#pragma unroll
-        for (int t = 0; t < NT16; ++t) {
-          const float* dst = &ds[t >> 1][(t & 1) * 8];
-          if (split_wanted<T, MODE, false>(nullptr, dst)) {
-            const Frag<T> sl = frag_residual(dst, sf[t]);
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-              mma(adq[db], frag_load_tr_swz<D / 8>(st, 16 * t, 32 * db), sl);
-          }
-        }
-      } else {
+      if constexpr (!C::kDma) {
         // fp32: dQ^T += K^T dS^T over these BN keys, into a fresh block that is then
         // added to dQ (one chain over every key of a long list would round at the
         // magnitude of the running sum on each of its steps)
