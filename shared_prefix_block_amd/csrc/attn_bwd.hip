@@ -279,7 +279,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   // the descriptors cover 0 bytes and the loads only write zeros into the idle buffer.
   constexpr int NT_LOADS = DmaTile<C::BMS, D, C::NT>::N;  // per tile and wave
   DmaRsrc rq{}, rg{};
-  char* st_next = smem;
+  const uint32_t smem_u = lds_addr_u(smem);
+  uint32_t st_next = smem_u;  // LDS address of the stage being filled
   auto dma_part = [&](int j) {
     if constexpr (C::kDma) {
       const int w = wave;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const T* gp = Gg + q0 * ldq + int64_t(h) * D;
     const int64_t at = int64_t(h) * ntok + q0;
     if constexpr (C::kDma) {  // into LDS stage n & 1: Q | dO | L2 | D
-      char* st = smem + (n & 1) * C::STAGE_BYTES;
+      const uint32_t st = smem_u + (n & 1) * C::STAGE_BYTES;
       st_next = st;
       rq = dma_rsrc(qp, nvalid * pitch);
       rg = dma_rsrc(gp, nvalid * pitch);
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       // one buffer: the next sub-step is staged after this one's math
       if constexpr (!kSingle) issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu));
     } else if constexpr (C::kDma) {
-      st_next = smem + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
+      st_next = smem_u + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
       rq = dma_rsrc(Qg, 0);
       rg = rq;
     }
@@ -734,7 +735,7 @@ void dq_kernel(BwdParams p) {
     const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
     if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | mask words
-      char* st = smem + (n & 1) * C::STAGE_BYTES;
+      const uint32_t st = lds_addr_u(smem) + (n & 1) * C::STAGE_BYTES;
       dt.load(Kg + kv0 * ldk + koff, nvalid, pitch, st);
       dt.load(Vg + kv0 * ldk + koff, nvalid, pitch, st + C::TILE_BYTES);
       if (wave == 0 && lane < C::BN)  // keys past the end read end = 0 (or w = 0): never visible

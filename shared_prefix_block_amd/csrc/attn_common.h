@@ -499,21 +499,26 @@ __device__ __forceinline__ DmaRsrc dma_rsrc(const void* base, int bytes) {
               uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(bytes))), uint32_t(kBufWord3)};
   return r;
 }
+// LDS byte address of a pointer into the work-group's shared memory, wave-uniform.
+// Kernels take it once for their shared array and form stage addresses from it with
+// scalar arithmetic: converting a generic pointer per load costs vector instructions
+// (a 64-bit add, two readfirstlanes and a null check) on every load.
 __device__ __forceinline__ uint32_t lds_addr_u(void* p) {
   return uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(to_lds(p)))));
 }
-// 16 bytes per lane from byte offset voff of the buffer; lane i lands at dst + 16 i.
-__device__ __forceinline__ void dma_load16(const DmaRsrc& r, int voff, void* dst) {
+// 16 bytes per lane from byte offset voff of the buffer; lane i lands at LDS address
+// lds + 16 i (lds wave-uniform).
+__device__ __forceinline__ void dma_load16(const DmaRsrc& r, int voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(r.d), "s"(lds_addr_u(dst))
+               : "v"(voff), "s"(r.d), "s"(lds)
                : "memory");
 }
-// 4 bytes per lane; lane i lands at dst + 4 i.
-__device__ __forceinline__ void dma_load4(const DmaRsrc& r, int voff, void* dst) {
+// 4 bytes per lane; lane i lands at lds + 4 i.
+__device__ __forceinline__ void dma_load4(const DmaRsrc& r, int voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(r.d), "s"(lds_addr_u(dst))
+               : "v"(voff), "s"(r.d), "s"(lds)
                : "memory");
 }
 
@@ -534,9 +539,9 @@ struct DmaTile {
       voff[j] = r * pitch_bytes + c * 16;
     }
   }
-  // Enqueue the loads of rows [0, nvalid) of the tile at `src` into LDS at `dst`.
+  // Enqueue the loads of rows [0, nvalid) of the tile at `src` into LDS address `dst`.
   __device__ __forceinline__ void load(const void* src, int nvalid, int pitch_bytes,
-                                       char* dst) const {
+                                       uint32_t dst) const {
     const DmaRsrc rs = dma_rsrc(src, nvalid * pitch_bytes);
     const int w = wave_id();
 #pragma unroll

@@ -179,10 +179,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   constexpr int NL = DmaTile<C::BN, C::kFp8 ? D / 2 : D, C::NT>::N;  // loads per tile, wave
   constexpr int NDMA = C::kFp8 ? NL : 2 * NL;  // K and (bf16) V tile loads per stage
   DmaRsrc rk{}, rvv{};
-  char* st_next = smem;
+  const uint32_t smem_u = lds_addr_u(smem);
+  uint32_t st_next = smem_u;  // LDS address of the stage being filled
   auto dma_part = [&](int j) {
     if constexpr (C::kDma) {
-      const int w = threadIdx.x >> 6;
+      const int w = wave_id();  // wave-uniform: the LDS address stays scalar
       if (j < NL)
         dma_load16(rk, dt.voff[j], st_next + (j * (C::NT / 64) + w) * 1024);
       else
@@ -196,8 +197,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
     if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | mask words
       static_assert(C::BN == 64, "one end[] value per lane");
-      char* st = smem + (n & 1) * C::STAGE_BYTES;
-      st_next = st;
+      st_next = smem_u + (n & 1) * C::STAGE_BYTES;
       rk = dma_rsrc(K + kv0 * ldk + koff, nvalid * pitch);
       if constexpr (C::kFp8) {  // V into registers (rows past the end read 0)
         const auto rs = buf_rsrc(V + kv0 * ldk + koff, nvalid * pitch);
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       } else {
         rvv = dma_rsrc(V + kv0 * ldk + koff, nvalid * pitch);
       }
-      char* mw = st + C::KT_BYTES + C::VT_BYTES;
+      const uint32_t mw = st_next + C::KT_BYTES + C::VT_BYTES;
       if (wave == 0)  // keys past the end read end = 0 (or w = 0): never visible
         dma_load4(dma_rsrc(ev + kv0, nvalid * 4), lane * 4, mw);
       if constexpr (NODES)
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       }
       issue(n + 1, int(entry(n + 1) & 0x3fffffffu));
     } else if constexpr (C::kDma) {
-      st_next = smem + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
+      st_next = smem_u + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
       rk = dma_rsrc(K, 0);
       rvv = rk;
     }
