@@ -35,7 +35,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3, "fp8": 5033.2}  # MI355X dense MFM
 PEAK_FP8_FWD = 4.0 / (2.0 / PEAK_TFLOPS["fp8"] + 2.0 / PEAK_TFLOPS["bf16"])
 HBM_PEAK_GBS = 8000.0
 TILE = 128
-KERNEL_SOURCES = ["attn_common.h", "attn_fwd.hip", "attn_bwd.hip"]
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd.hip", "attn_bwd.h", "attn_bwd.hip", "attn_bwd_dkdv.hip"]
 
 
 def kernel_source_hash() -> str:

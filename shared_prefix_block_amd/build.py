@@ -21,7 +21,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsa.so")
 
-SOURCES = ["api.cpp", "tilemap.hip", "attn_fwd.hip", "attn_bwd.hip", "fold.hip"]
+SOURCES = ["api.cpp", "tilemap.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip",
+           "fold.hip"]
+# per-source flags on top of _flags(): the dK/dV unit takes MFMA results in VGPRs (its
+# kernel keeps K and V in AGPRs, so the S and dP products land where the VALU reads
+# them); the other units keep the compiler's default
+EXTRA_FLAGS = {"attn_bwd_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -40,7 +45,8 @@ def _flags():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA_FLAGS.get(src, [])
+    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(x for x in r.stderr.splitlines() if noise not in x)
