@@ -23,10 +23,13 @@ LIB = os.path.join(PKG, "libpsa.so")
 
 SOURCES = ["api.cpp", "tilemap.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip",
            "fold.hip"]
-# per-source flags on top of _flags(): the dK/dV unit takes MFMA results in VGPRs (its
-# kernel keeps K and V in AGPRs, so the S and dP products land where the VALU reads
-# them); the other units keep the compiler's default
-EXTRA_FLAGS = {"attn_bwd_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source flags on top of _flags(): the attention units take MFMA results in VGPRs
+# (their kernels keep constant operands, Q, dO or K and V, in AGPRs where registers are
+# short, so S and dP land where the VALU reads them instead of being copied out of
+# AGPRs); the map builder, fold and host code keep the default
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA_FLAGS = {"attn_fwd.hip": _VGPR_FORM, "attn_bwd.hip": _VGPR_FORM,
+               "attn_bwd_dkdv.hip": _VGPR_FORM}
 ARCH = "gfx950"
 
 

@@ -250,8 +250,12 @@ void dq_kernel(BwdParams p) {
     if constexpr (NODES) qkey = qvalid ? p.nkey[qrow] : 0;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      mark_ready(qf[s]);
-      mark_ready(gf[s]);
+      if constexpr (C::kBf16 && D == 256) {  // in AGPRs, where the MFMAs read them
+        asm volatile("" : "+a"(qf[s].v), "+a"(gf[s].v));
+      } else {
+        mark_ready(qf[s]);
+        mark_ready(gf[s]);
+      }
     }
     mark_ready(l2);
     mark_ready(dl);

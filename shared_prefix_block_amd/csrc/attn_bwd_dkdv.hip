@@ -1,12 +1,12 @@
 // dK and dV of the backward: one work-group per (kv-tile of 128 keys, kv head), see
 // attn_bwd.hip for the whole backward.
 //
-// This unit is compiled with MFMA results in VGPRs (-mllvm -amdgpu-mfma-vgpr-form,
-// set by the build for this file only) and the kernel pins its K and V fragments in
-// AGPRs: the per-step S and dP products then land where the softmax gradient reads
-// them, instead of being copied out of AGPRs one register at a time (64 copies per
-// 64-row sub-step at d = 128), and bf16 at d = 64 fits two waves per SIMD.  dQ, in the
-// other unit, keeps the default form: it ran no faster under this one.
+// Like the other attention units, this one is compiled with MFMA results in VGPRs
+// (-mllvm -amdgpu-mfma-vgpr-form, set by the build), and the kernel pins its K and V
+// fragments in AGPRs: the per-step S and dP products then land where the softmax
+// gradient reads them, instead of being copied out of AGPRs one register at a time
+// (64 copies per 64-row sub-step at d = 128), and bf16 at d = 64 fits two waves per
+// SIMD.
 //
 // Source of the gradient formulas: the analytic softmax-attention backward
 // (FlashAttention-2); the mask, layout and GQA conventions are the forward's

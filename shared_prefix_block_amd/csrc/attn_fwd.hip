@@ -120,6 +120,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   using PT = typename C::PT;
   constexpr int NQF = C::kFp8 ? D / 64 : D / 16;  // Q fragments (reduction steps of S)
   Frag<T> qf[NQF];  // loaded below, once the first tile's loads are in flight
+  // d = 256 (bf16, e4m3): Q is pinned in AGPRs, where the MFMAs read it, and this unit
+  // is compiled with MFMA results in VGPRs: S lands where the softmax reads it, instead
+  // of the compiler keeping S and O in AGPRs and moving them (456 register moves per
+  // sub-step at d = 256 before)
+  constexpr bool kQInAgpr = (C::kBf16 || C::kFp8) && D == 256;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -287,7 +292,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
     }
     if constexpr (NODES) qkey = qvalid ? p.nkey[qrow] : 0;
 #pragma unroll
-    for (int s = 0; s < NQF; ++s) mark_ready(qf[s]);
+    for (int s = 0; s < NQF; ++s) {
+      if constexpr (kQInAgpr)  // see kQInAgpr
+        asm volatile("" : "+a"(qf[s].v));
+      else
+        mark_ready(qf[s]);
+    }
     if constexpr (NODES) mark_ready(qkey);
   }
   if constexpr (!C::kDma) __syncthreads();
