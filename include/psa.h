@@ -295,7 +295,7 @@ psa_status psa_bwd_noalloc(const psa_tile_map* map, psa_dtype dtype, psa_dtype g
 /*
  * The backward in stages, for callers that time or overlap them (psa_bwd runs all
  * three), with options.  flags is the OR of a nonzero set of stages:
- *   PSA_STAGE_PREPARE  D = rowsum(dO * O) and LSE in log2 units, into the workspace
+ *   PSA_STAGE_PREPARE  -D = -rowsum(dO * O) and LSE in log2 units, into the workspace
  *                      (reads o, lse, dout);
  *   PSA_STAGE_DKDV     dK, dV (reads q, k, v, dout and the prepared workspace);
  *   PSA_STAGE_DQ       dQ (reads q, k, v, dout and the prepared workspace).

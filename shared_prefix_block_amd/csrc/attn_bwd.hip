@@ -1,13 +1,13 @@
 // Backward kernels (FlashAttention-2 style gradients of the block-sparse forward).
 //
-//   bwd_pre : Dl[h, q] = sum_d dO[q, h, d] * O[q, h, d];  L2[h, q] = LSE * log2(e)
+//   bwd_pre : nD[h, q] = -sum_d dO[q, h, d] * O[q, h, d];  L2[h, q] = LSE * log2(e)
 //             (+inf on rows that saw no key, so their probabilities come out 0).
 //   dkdv    : (attn_bwd_dkdv.hip) one work-group per (kv-tile of 128 keys, kv head).  K and V stay in
 //             registers; the CSC list of the kv-tile's non-empty q-tiles is walked for
 //             every q head of the GQA group, so dK and dV are summed over the group
 //             inside the work-group (no atomics, no repeated K/V).  Per q sub-step:
 //             S = Q K^T and dP = dO V^T (Q, dO from LDS), P = exp2(S c - L2), masked on
-//             partial tiles, dS = P (dP - Dl), dV^T += dO^T P, dK^T += Q^T dS.
+//             partial tiles, dS = P (dP + nD), dV^T += dO^T P, dK^T += Q^T dS.
 //   dq      : one work-group per (q-tile, q head), walking the CSR list like the
 //             forward: S^T = K Q^T and dP^T = V dO^T (Q, dO in registers), the same
 //             P and dS, dQ^T += K^T dS^T.  Recomputing P here costs two extra
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   if (valid && sub == 0) {
     const int64_t q = rid / p.hq;
     const int h = int(rid % p.hq);
-    p.Dl[int64_t(h) * p.T + q] = acc;
+    p.nD[int64_t(h) * p.T + q] = -acc;
     const float lse = p.lse[int64_t(h) * p.T + q];
     p.L2[int64_t(h) * p.T + q] = lse == -INFINITY ? INFINITY : lse * kLog2e;
   }
@@ -240,12 +240,12 @@ void dq_kernel(BwdParams p) {
       dl = part + __shfl_xor(part, 32);
       l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
       if (qvalid && half == 0) {
-        p.Dl[int64_t(h) * ntok + qrow] = dl;
+        p.nD[int64_t(h) * ntok + qrow] = -dl;
         p.L2[int64_t(h) * ntok + qrow] = l2;
       }
     } else if (qvalid) {
       l2 = p.L2[int64_t(h) * ntok + qrow];
-      dl = p.Dl[int64_t(h) * ntok + qrow];
+      dl = -p.nD[int64_t(h) * ntok + qrow];
     }
     if constexpr (NODES) qkey = qvalid ? p.nkey[qrow] : 0;
 #pragma unroll
@@ -481,7 +481,7 @@ hipError_t launch_bwd_t(const psa_tile_map& map, const AttnShape& s, const void*
   p.dk = dk;
   p.dv = dv;
   const size_t plane = ws_align(size_t(s.T) * s.hq * sizeof(float));
-  p.Dl = static_cast<float*>(workspace);
+  p.nD = static_cast<float*>(workspace);
   p.L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + plane);
   p.end = map.end;
   p.nkey = map.nkey;

@@ -54,7 +54,7 @@ struct DkdvCfg {
   static constexpr int OFF_QT = OFF_G + (kDK ? N_ELEMS : 0);
   static constexpr int OFF_GT = OFF_QT + (kDK ? T_ELEMS : 0);
   static constexpr int BUF_ELEMS = OFF_GT + (kDV ? T_ELEMS : 0);
-  // bf16: Q | dO | L2 | D (| node numbers) stages filled by direct-to-LDS loads into
+  // bf16: Q | dO | L2 | -D (| node numbers) stages filled by direct-to-LDS loads into
   // swizzled, unpadded tiles (as the forward's K and V); fp32: through registers.
   static constexpr bool kDma = kBf16;
   static constexpr int LW = NODES ? 3 : 2;  // per-row words: L2, D (, key)
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const T* qp = Qg + q0 * ldq + int64_t(h) * D;
     const T* gp = Gg + q0 * ldq + int64_t(h) * D;
     const int64_t at = int64_t(h) * ntok + q0;
-    if constexpr (C::kDma) {  // into LDS stage n & 1: Q | dO | L2 | D
+    if constexpr (C::kDma) {  // into LDS stage n & 1: Q | dO | L2 | -D
       const uint32_t st = smem_u + (n & 1) * C::STAGE_BYTES;
       st_next = st;
       rq = dma_rsrc(qp, nvalid * pitch);
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       if (wave == 0 && lane < C::BMS)
         dma_load4(dma_rsrc(p.L2 + at, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
       if (wave == 1 && lane < C::BMS)
-        dma_load4(dma_rsrc(p.Dl + at, nvalid * 4), lane * 4,
+        dma_load4(dma_rsrc(p.nD + at, nvalid * 4), lane * 4,
                   st + 2 * C::TILE_BYTES + C::BMS * 4);
       if constexpr (NODES)  // rows past T read node 0: never visible
         if (wave == 2 && lane < C::BMS)
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
       {  // the per-row values first, loaded by every lane; rows past the end read 0
         const int rr = int(threadIdx.x) & (C::BMS - 1);
         l2_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.L2 + at, nvalid * 4), rr * 4));
-        dl_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.Dl + at, nvalid * 4), rr * 4));
+        dl_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.nD + at, nvalid * 4), rr * 4));
         if constexpr (NODES) qk_reg = int32_t(buf_load4(buf_rsrc(p.nkey + q0, nvalid * 4), rr * 4));
         l2_valid = rr < nvalid;
       }
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         f32x16 sacc = zero16(), pacc = zero16();
         const T* qr = Qs + (32 * qb + l32) * C::NS + 8 * half;
         const T* gr = Gs + (32 * qb + l32) * C::NS + 8 * half;
-        // the rows' LSE (log2 units) and D, read before the products so that their
+        // the rows' LSE (log2 units) and -D, read before the products so that their
         // latency passes under them
         f32x4 l2v[4], dlv[4];
 #pragma unroll
@@ -327,6 +327,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
           const int ql = 32 * qb + g * 8 + half * 4;
           l2v[g] = *reinterpret_cast<const f32x4*>(Ls + ql);
           if constexpr (kDK) dlv[g] = *reinterpret_cast<const f32x4*>(Dsh + ql);
+        }
+        // bf16: the dP sums start at the rows' -D, so dP - D comes out of the MFMAs
+        // (16 subtractions fewer per block); fp32 subtracts after its own products
+        if constexpr (C::kDma && kDK) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pacc[4 * g + u] = dlv[g][u];
         }
         if constexpr (C::kDma) {
           // Q and dO fragments read PF reduction steps ahead of their MFMAs
@@ -400,7 +408,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) ds[4 * g + u] = pv[4 * g + u] * (pacc[4 * g + u] - dlv[g][u]);
+            for (int u = 0; u < 4; ++u)
+              ds[4 * g + u] = C::kDma ? pv[4 * g + u] * pacc[4 * g + u]
+                                      : pv[4 * g + u] * (pacc[4 * g + u] + dlv[g][u]);
         }
         if constexpr (C::kDma) {
           // dV += dO^T P and dK += Q^T dS over these 32 queries (two 16-query
