@@ -262,6 +262,11 @@ void dq_kernel(BwdParams p) {
     if constexpr (NODES) mark_ready(qkey);
   }
   if constexpr (!C::kDma) __syncthreads();
+  // bf16: the dP sums start at -D (all 16 elements of a lane are its row's), so dP - D
+  // comes out of the MFMAs
+  f32x16 nd16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) nd16[i] = -dl;
 
   for (int n = 0; n < n_steps; ++n) {
     const int b = kSingle ? 0 : n & 1;
@@ -297,7 +302,7 @@ void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb) {
         if (C::kDma && partial && p.causal && kv0i + 32 * kb > wave_last) continue;
-        f32x16 sacc = zero16(), pacc = zero16();
+        f32x16 sacc = zero16(), pacc = C::kDma ? nd16 : zero16();
         if constexpr (C::kDma) {
           // K and V fragments read PF reduction steps ahead of their MFMAs
           constexpr int NS = D / 16, PF = 3;
@@ -380,7 +385,7 @@ void dq_kernel(BwdParams p) {
         }
         float* const dsk = ds[C::kDma ? 0 : kb];
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) dsk[ii] = pv[ii] * (pacc[ii] - dl);
+        for (int ii = 0; ii < 16; ++ii) dsk[ii] = C::kDma ? pv[ii] * pacc[ii] : pv[ii] * (pacc[ii] - dl);
         if constexpr (C::kDma) {
           // dQ^T += K^T dS^T over this block's 32 keys (16-key fragments t): dS rounded,
           // the (t, db) transposed K reads PF products ahead of their MFMAs; then, where
