@@ -57,9 +57,12 @@ struct DkdvCfg {
   // bf16: Q | dO | L2 | -D (| node numbers) stages filled by direct-to-LDS loads into
   // swizzled, unpadded tiles (as the forward's K and V); fp32: through registers.
   static constexpr bool kDma = kBf16;
-  static constexpr int LW = NODES ? 3 : 2;  // per-row words: L2, D (, key)
+  static constexpr int LW = NODES ? 3 : 2;  // per-row words: L2, -D (, key)
   static constexpr int TILE_BYTES = BMS * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + LW * BMS * 4;
+  // DMA path: one 64-word slot per per-row array (a wave's dword load fills 64 lanes)
+  // and a spare slot for the waves that load none of them; register path: BMS words
+  static constexpr int RS = kDma ? 64 : BMS;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + (LW + 1) * 64 * 4;
   static constexpr int NBUF = 2 * BUF_ELEMS * EB + 2 * LW * BMS * 4 <= kLdsMax ? 2 : 1;
   static constexpr int LDS_BYTES = kDma ? 2 * STAGE_BYTES : NBUF * BUF_ELEMS * EB + 2 * LW * BMS * 4;
   static_assert(CS == 1 || !kDma, "column slices exist on the register path only");
@@ -187,29 +190,38 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
                    st_next + C::TILE_BYTES + ((j - NT_LOADS) * (C::NT / 64) + w) * 1024);
     }
   };
-  auto issue = [&](int n, const Cursor& u, int q_tile) {
+  // more = false: no next step; the loads then cover 0 bytes and write zeros into the
+  // idle stage
+  auto issue = [&](int n, const Cursor& u, int q_tile, bool more) {
     const int h = u.h, sub = u.sub;
-    const int64_t q0 = int64_t(q_tile) * kTileM + sub * C::BMS;
-    const int nvalid = ntok - q0 < C::BMS ? int(ntok - q0) : C::BMS;
-    const T* qp = Qg + q0 * ldq + int64_t(h) * D;
-    const T* gp = Gg + q0 * ldq + int64_t(h) * D;
-    const int64_t at = int64_t(h) * ntok + q0;
     if constexpr (C::kDma) {  // into LDS stage n & 1: Q | dO | L2 | -D
+      // Branch-free, so that its scalar work shares a block with the MFMAs that follow
+      // and runs under them; 32-bit rows (T < 2^31) and 32 x 32 -> 64-bit products (a
+      // 64-bit multiply is five scalar instructions, and the one wave of a SIMD issues
+      // every one of them)
+      const int q0 = q_tile * kTileM + sub * C::BMS;
+      const int nvalid = more ? min(int(ntok) - q0, C::BMS) : 0;
+      const uint64_t off = uint64_t(uint32_t(q0)) * uint32_t(pitch) + uint32_t(h * (2 * D));
+      const uint64_t at = (uint64_t(uint32_t(h)) * uint32_t(ntok) + uint32_t(q0)) * 4u;
       const uint32_t st = smem_u + (n & 1) * C::STAGE_BYTES;
       st_next = st;
-      rq = dma_rsrc(qp, nvalid * pitch);
-      rg = dma_rsrc(gp, nvalid * pitch);
-      // rows past T read L2 = D = 0; they sit in a partial tile and are masked
-      if (wave == 0 && lane < C::BMS)
-        dma_load4(dma_rsrc(p.L2 + at, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
-      if (wave == 1 && lane < C::BMS)
-        dma_load4(dma_rsrc(p.nD + at, nvalid * 4), lane * 4,
-                  st + 2 * C::TILE_BYTES + C::BMS * 4);
-      if constexpr (NODES)  // rows past T read node 0: never visible
-        if (wave == 2 && lane < C::BMS)
-          dma_load4(dma_rsrc(p.nkey + q0, nvalid * 4), lane * 4,
-                    st + 2 * C::TILE_BYTES + 2 * C::BMS * 4);
+      rq = dma_rsrc(reinterpret_cast<const char*>(Qg) + off, nvalid * pitch);
+      rg = dma_rsrc(reinterpret_cast<const char*>(Gg) + off, nvalid * pitch);
+      // the rows' L2, -D (node form: and node numbers): wave w < LW loads array w into
+      // slot w, the other waves load L2 again into the spare slot.  Rows past T (and
+      // lanes past BMS) read 0: they sit in a partial tile and are masked (node 0 is
+      // never visible).
+      const char* ws = reinterpret_cast<const char*>(wave == 1 ? p.nD : p.L2) + at;
+      if constexpr (NODES)
+        if (wave == 2) ws = reinterpret_cast<const char*>(p.nkey) + uint64_t(uint32_t(q0)) * 4u;
+      const int slot = wave < C::LW ? wave : C::LW;
+      dma_load4(dma_rsrc(ws, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES + slot * 256);
     } else {
+      const int64_t q0 = int64_t(q_tile) * kTileM + sub * C::BMS;
+      const int nvalid = ntok - q0 < C::BMS ? int(ntok - q0) : C::BMS;
+      const T* qp = Qg + q0 * ldq + int64_t(h) * D;
+      const T* gp = Gg + q0 * ldq + int64_t(h) * D;
+      const int64_t at = int64_t(h) * ntok + q0;
       {  // the per-row values first, loaded by every lane; rows past the end read 0
         const int rr = int(threadIdx.x) & (C::BMS - 1);
         l2_reg = __builtin_bit_cast(float, buf_load4(buf_rsrc(p.L2 + at, nvalid * 4), rr * 4));
@@ -243,7 +255,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
 
   Cursor cur{e0, hk * rep, 0};
   if (n_steps > 0) {
-    issue(0, cur, int(entry(e0) & 0x3fffffffu));
+    issue(0, cur, int(entry(e0) & 0x3fffffffu), true);
     if constexpr (C::kDma) {
 #pragma unroll
       for (int j = 0; j < 2 * NT_LOADS; ++j) dma_part(j);
@@ -289,17 +301,16 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const bool partial = (ent >> 30) == 1;
     const int q0i = int(ent & 0x3fffffffu) * kTileM + cur.sub * C::BMS;
     const Cursor nxt = advance(cur);
-    if (n + 1 < n_steps) {
-      if (nxt.e - e0 - wbase >= 64) {  // next window (a vector load; rare)
-        window_load(nxt.e - e0);
-        mark_ready(*reinterpret_cast<int32_t*>(&wreg));
-      }
+    const bool more = n + 1 < n_steps;
+    if (more && nxt.e - e0 - wbase >= 64) {  // next window (a vector load; rare)
+      window_load(nxt.e - e0);
+      mark_ready(*reinterpret_cast<int32_t*>(&wreg));
+    }
+    if constexpr (C::kDma) {
+      issue(n + 1, nxt, int(entry(more ? nxt.e : cur.e) & 0x3fffffffu), more);
+    } else if (more) {
       // one buffer: the next sub-step is staged after this one's math
-      if constexpr (!kSingle) issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu));
-    } else if constexpr (C::kDma) {
-      st_next = smem_u + ((n + 1) & 1) * C::STAGE_BYTES;  // idle buffer, zero-byte loads
-      rq = dma_rsrc(Qg, 0);
-      rg = rq;
+      if constexpr (!kSingle) issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu), true);
     }
 
     const char* st = smem + b * C::STAGE_BYTES;  // DMA stage
@@ -309,8 +320,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     const T* Gt = Qs + C::OFF_GT;
     const float* Ls = C::kDma ? reinterpret_cast<const float*>(st + 2 * C::TILE_BYTES)
                               : ld0 + (b * C::LW + 0) * C::BMS;
-    const float* Dsh = Ls + C::BMS;
-    const int32_t* Qk = reinterpret_cast<const int32_t*>(Ls + 2 * C::BMS);  // node form
+    const float* Dsh = Ls + C::RS;
+    const int32_t* Qk = reinterpret_cast<const int32_t*>(Ls + 2 * C::RS);  // node form
 
     {
       const int qd0 = q0i - kvrow_i;  // q - kv at the sub-step's first row
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
     if constexpr (kSingle) {  // every wave is done with the buffer: stage the next step
       if (n + 1 < n_steps) {
         __syncthreads();
-        issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu));
+        issue(n + 1, nxt, int(entry(nxt.e) & 0x3fffffffu), true);
         commit(0);
       }
       __syncthreads();
