@@ -177,12 +177,15 @@ void dq_kernel(BwdParams p) {
   const int32_t* const ev = NODES ? p.nlo : p.end;
 
   auto issue = [&](int n, int col_n) {
-    const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
-    const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
     if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | mask words
+      // 32-bit rows (T < 2^31) and one 32 x 32 -> 64-bit product for the tile's byte
+      // offset (a 64-bit multiply is five scalar instructions)
+      const int kv0 = col_n * kTileN + (n % C::NSUB) * C::BN;
+      const int nvalid = min(int(ntok) - kv0, C::BN);
+      const uint64_t off = uint64_t(uint32_t(kv0)) * uint32_t(pitch) + uint32_t(hk * (2 * D));
       const uint32_t st = lds_addr_u(smem) + (n & 1) * C::STAGE_BYTES;
-      dt.load(Kg + kv0 * ldk + koff, nvalid, pitch, st);
-      dt.load(Vg + kv0 * ldk + koff, nvalid, pitch, st + C::TILE_BYTES);
+      dt.load(reinterpret_cast<const char*>(Kg) + off, nvalid, pitch, st);
+      dt.load(reinterpret_cast<const char*>(Vg) + off, nvalid, pitch, st + C::TILE_BYTES);
       if (wave == 0 && lane < C::BN)  // keys past the end read end = 0 (or w = 0): never visible
         dma_load4(dma_rsrc(ev + kv0, nvalid * 4), lane * 4, st + 2 * C::TILE_BYTES);
       if constexpr (NODES)
@@ -190,6 +193,8 @@ void dq_kernel(BwdParams p) {
           dma_load4(dma_rsrc(p.nw + kv0, nvalid * 4), lane * 4,
                     st + 2 * C::TILE_BYTES + C::BN * 4);
     } else {
+      const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
+      const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
       {  // every lane loads; a key past the end reads end = 0 and gets reach 0
         const int r = int(threadIdx.x) & (C::BN - 1);
         e_reg = int32_t(buf_load4(buf_rsrc(ev + kv0, nvalid * 4), r * 4));

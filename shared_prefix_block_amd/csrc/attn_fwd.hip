@@ -198,21 +198,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
   };
 
   auto issue = [&](int n, int col_n) {  // global reads of sub-step n
-    const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
-    const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
     if constexpr (C::kDma) {  // straight into LDS stage n & 1: K | V | mask words
       static_assert(C::BN == 64, "one end[] value per lane");
+      // 32-bit rows (T < 2^31) and one 32 x 32 -> 64-bit product for the tile's byte
+      // offset (a 64-bit multiply is five scalar instructions)
+      const int kv0 = col_n * kTileN + (n % C::NSUB) * C::BN;
+      const int nvalid = min(int(ntok) - kv0, C::BN);
+      const uint64_t off = uint64_t(uint32_t(kv0)) * uint32_t(pitch) + uint32_t(hk * D * C::EB);
       st_next = smem_u + (n & 1) * C::STAGE_BYTES;
-      rk = dma_rsrc(K + kv0 * ldk + koff, nvalid * pitch);
+      rk = dma_rsrc(reinterpret_cast<const char*>(K) + off, nvalid * pitch);
       if constexpr (C::kFp8) {  // V into registers (rows past the end read 0)
-        const auto rs = buf_rsrc(V + kv0 * ldk + koff, nvalid * pitch);
+        const auto rs = buf_rsrc(reinterpret_cast<const char*>(V) + off, nvalid * pitch);
 #pragma unroll
         for (int it = 0; it < NVC; ++it) {
           const int cidx = it * C::NT + int(threadIdx.x);
           vreg[it] = buf_load16(rs, (cidx / (D / 16)) * pitch + (cidx % (D / 16)) * 16);
         }
       } else {
-        rvv = dma_rsrc(V + kv0 * ldk + koff, nvalid * pitch);
+        rvv = dma_rsrc(reinterpret_cast<const char*>(V) + off, nvalid * pitch);
       }
       const uint32_t mw = st_next + C::KT_BYTES + C::VT_BYTES;
       if (wave == 0)  // keys past the end read end = 0 (or w = 0): never visible
@@ -220,6 +223,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<T, D
       if constexpr (NODES)
         if (wave == 1) dma_load4(dma_rsrc(p.nw + kv0, nvalid * 4), lane * 4, mw + C::BN * 4);
     } else {  // into registers; commit() stores them
+      const int64_t kv0 = int64_t(col_n) * kTileN + (n % C::NSUB) * C::BN;
+      const int nvalid = ntok - kv0 < C::BN ? int(ntok - kv0) : C::BN;
       // mask words first: the loads retire in order, so waiting for them at commit
       // does not wait for the K/V reads issued after them
       const int r = int(threadIdx.x) & (C::BN - 1);
