@@ -348,8 +348,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
             for (int u = 0; u < 4; ++u) pacc[4 * g + u] = dlv[g][u];
         }
         if constexpr (C::kDma) {
-          // Q and dO fragments read PF reduction steps ahead of their MFMAs
-          constexpr int NS = D / 16, PF = 3;
+          // Q and dO fragments read PF - 1 reduction steps ahead of their MFMAs (one:
+          // two and three measured 0-3 % slower, the LDS pipe being shared by the
+          // four waves)
+          constexpr int NS = D / 16, PF = 2;
           Frag<T> qq[PF], gq[PF];
           constexpr int RD = kDK ? 2 : 1;  // fragment reads per reduction step
 #pragma unroll
@@ -426,9 +428,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
         if constexpr (C::kDma) {
           // dV += dO^T P and dK += Q^T dS over these 32 queries (two 16-query
           // fragments t): P and dS rounded to bf16, the (t, db) transposed reads
-          // PF products ahead of their MFMAs; then, where split_wanted, the
+          // PF - 1 products ahead of their MFMAs; then, where split_wanted, the
           // residuals in a second pass
-          constexpr int ND = D / 32, NI = 2 * ND, PF = 3;
+          constexpr int ND = D / 32, NI = 2 * ND, PF = 2;
           constexpr int TR = 2 * ((kDV ? 1 : 0) + (kDK ? 1 : 0));  // reads per product
           constexpr int MF = (kDV ? 1 : 0) + (kDK ? 1 : 0);        // MFMAs per product
           Frag<T> pf[2], sf[2];
