@@ -23,7 +23,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* nD;  // [hq, T]: -D = -sum_d dO * O (negated: the bf16 kernels start their dP sums there)
+  float* nD;  // [hq, T]: -D = -sum_d dO * O (negated: dK/dV starts its dP sums from it)
   float* L2;  // [hq, T]
   const int32_t* end;   // interval form
   const int32_t* nkey;  // node form
